@@ -1,0 +1,256 @@
+/*
+ * csa.h — C ABI of the MI355X (gfx950) hybrid compressed attention library
+ * (libcsa.so): DeepSeek-V4's CSA and HCA attention layers.
+ *
+ * Sources (page title, section):
+ *  [DD] "DeepSeek-V4 内部机制" (LLM-101-CN deep dive): §1.2 Step 1 (token-level
+ *       compressor), Step 2 (Lightning Indexer, top-k, shared-KV MQA), §1.3
+ *       (HCA: m' = 128, dense, no indexer), §1.4 table (Q/KV RMSNorm, partial
+ *       RoPE with the output rotated at -i, 128-token sliding window,
+ *       attention sink and its softmax equation), §1.5 (RoPE channels BF16,
+ *       the rest FP8), §6.2 (FP4 indexer QK, BF16 index scores), §7 (state
+ *       cache + paged cache whose block holds lcm(m, m') raw tokens).
+ *  [YP] yunpan.plus explainer, "CSA / HCA" section, eqs. (6)-(11).
+ *  [AD] m.admirer.cn article, CSA/HCA section (k = 512 / 1024, 128-token
+ *       window, 64 RoPE channels, block of 128 raw tokens = 32 CSA + 1 HCA
+ *       entries, state cache holding the window and the uncompressed tail).
+ *
+ * Conventions shared by every call
+ *  - Pointers are DEVICE memory unless marked [host].  The caller owns all
+ *    memory; the library allocates nothing and never synchronises.
+ *  - Every compute call enqueues its kernels on `stream` (a hipStream_t passed
+ *    as void*, NULL = the default stream) and returns without waiting.
+ *  - All arguments are validated on the host before anything is launched.
+ *    Return value: CSA_OK (0) or a negative csa_status; csa_last_error()
+ *    then holds a message (thread-local).  A launch failure reported by the
+ *    HIP runtime returns CSA_EHIP.  No exception crosses the ABI.
+ *  - Results are deterministic: every reduction runs in a fixed order that
+ *    does not depend on the launch configuration or on timing.
+ *  - Calls that share buffers must be ordered by the caller (same stream).
+ *
+ * The batch: a call processes the new tokens of n_req requests.  Request r
+ * owns new tokens cu_new[r] .. cu_new[r+1]-1 (global rows of H, q, ...) at
+ * positions start_pos[r], start_pos[r]+1, ...  Its state slot is r (slot r of
+ * the state buffer) and its logical block j is physical block
+ * block_table[r*max_blocks + j] of each layer's cache pools.
+ *
+ * Positions and visibility: compressed entry i of a request covers raw
+ * tokens m*i .. m*i+m-1; it becomes visible to the query at position t iff
+ * m*i+m-1 <= t, so a query sees V_t = floor((t+1)/m) entries.  Its RoPE
+ * position is m*i.  Queries are rotated at t and outputs back at -t.
+ *
+ * Storage layouts (all little-endian, no padding beyond what is stated):
+ *  KV block (one pool per layer, block stride csa_sizes.kv_block_bytes):
+ *    CSA_KV_F32   epb records of c fp32
+ *    CSA_KV_BF16  epb records of c bf16
+ *    CSA_KV_FP8   64-byte header (fp32 scale s at byte 0, rest 0), then epb
+ *                 records of (c - r) E4M3FN codes followed by r bf16 values
+ *                 (the RoPE channels).  FP8 channels decode to code * s.
+ *    epb = block_tokens / m entries per block (32 for CSA, 1 for HCA).
+ *  Indexer-key block (CSA only, stride csa_sizes.idx_block_bytes):
+ *    CSA_IDX_F32 / CSA_IDX_BF16  epb keys of c_idx values
+ *    CSA_IDX_MXFP4  epb*c_idx/2 bytes of E2M1 codes (key j at j*c_idx/2, two
+ *                   codes per byte, even element in the low nibble), then
+ *                   epb*c_idx/32 E8M0 scale bytes (key j at j*c_idx/32), one
+ *                   per 32 consecutive elements (OCP MX).
+ *  State slot (stride csa_sizes.state_bytes): window ring of win_cap rows x c
+ *    in act_fmt (row of position p at slot p mod win_cap), then the
+ *    compressor tail ring of R rows x ncols fp32 (R = 2m with overlap, m
+ *    without; row of position p at slot p mod R).  The tail holds the
+ *    projected rows of the tokens whose entries are not complete yet, plus
+ *    (CSA) the previous block that the next entry's b-half reads.
+ *  Projection columns (ncols): CSA [C^a | C^b | Z^a | Z^b] (4c) followed by
+ *    the indexer's [C^a | C^b | Z^a | Z^b] (4c_idx); HCA [C | Z] (2c).
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA_ABI_VERSION 1
+
+typedef enum {
+    CSA_OK = 0,
+    CSA_EINVAL = -1,        /* bad argument (null pointer, size, range) */
+    CSA_EUNSUPPORTED = -2,  /* valid but unsupported combination */
+    CSA_EWORKSPACE = -3,    /* workspace or output capacity too small */
+    CSA_EHIP = -4,          /* HIP runtime reported an error */
+    CSA_EINTERNAL = -5
+} csa_status;
+
+enum { CSA_KIND_CSA = 0, CSA_KIND_HCA = 1 };
+enum { CSA_KV_F32 = 0, CSA_KV_BF16 = 1, CSA_KV_FP8 = 2 };
+enum { CSA_IDX_F32 = 0, CSA_IDX_BF16 = 1, CSA_IDX_MXFP4 = 2 };
+enum { CSA_FMT_F32 = 0, CSA_FMT_BF16 = 1 };   /* activations, scores, outputs */
+
+/* One attention layer.  [host] */
+typedef struct {
+    int32_t kind;          /* CSA_KIND_CSA (overlapping 2m window, indexer, top-k) or CSA_KIND_HCA */
+    int32_t m;             /* compression ratio: 4 (CSA) or 128 (HCA); block_tokens % m == 0 */
+    int32_t c;             /* entry / head width (multiple of 32, <= 512) */
+    int32_t rope_dim;      /* r: RoPE on the last r channels (even, 0 < r <= c) */
+    int32_t n_heads;       /* query heads sharing the one KV head (multiple of 8, <= 128) */
+    int32_t n_idx_heads;   /* CSA: indexer heads (multiple of 4, <= 64) */
+    int32_t c_idx;         /* CSA: indexer key width (multiple of 32, <= 128) */
+    int32_t top_k;         /* CSA: entries kept per query (1..2048) */
+    int32_t n_win;         /* sliding-window rows (the query's own token and the n_win-1 before) */
+    int32_t win_cap;       /* window ring rows per state slot: cache_append takes <= win_cap new tokens per request,
+                              the attention calls <= win_cap - n_win + 1 */
+    int32_t block_tokens;  /* raw tokens per paged block (128 = lcm(4, 128)) */
+    int32_t kv_fmt;        /* CSA_KV_* */
+    int32_t idx_fmt;       /* CSA_IDX_* */
+    int32_t score_fmt;     /* CSA_FMT_*: index scores */
+    int32_t act_fmt;       /* CSA_FMT_*: H, W, q, q_idx and the window ring */
+    int32_t out_fmt;       /* CSA_FMT_*: attention output */
+    float rope_theta;      /* RoPE base (10000) */
+    float norm_eps;        /* RMSNorm epsilon (1e-6) */
+} csa_layer_desc;
+
+/* The requests of one call.  The struct itself is [host]. */
+typedef struct {
+    int32_t n_req;
+    int32_t max_new;               /* [host] >= every request's new-token count */
+    int32_t max_ctx;               /* [host] >= every request's start_pos + new-token count */
+    int32_t max_blocks;            /* columns of block_table */
+    const int32_t* cu_new;         /* [n_req+1] prefix sums of new tokens, cu_new[0] = 0 */
+    const int32_t* start_pos;      /* [n_req] position of each request's first new token */
+    const int32_t* block_table;    /* [n_req*max_blocks] physical block ids (-1 = unused) */
+} csa_batch;
+
+/* Sizes the caller allocates.  [host] */
+typedef struct {
+    size_t kv_block_bytes;         /* one KV block */
+    size_t idx_block_bytes;        /* one indexer-key block (0 for HCA) */
+    size_t state_bytes;            /* one state slot (window ring + tail ring) */
+    int32_t entries_per_block;     /* epb */
+    int32_t proj_cols;             /* ncols of the projection */
+} csa_sizes;
+
+int csa_abi_version(void);
+const char* csa_last_error(void);
+
+/* Fill *out for a layer (validates the descriptor). */
+int csa_layer_sizes(const csa_layer_desc* layer, csa_sizes* out);
+
+/* Workspace bytes an op needs for n_rows rows (tokens or queries):
+ *   CSA_OP_COMPRESS  projection rows [n_rows x ncols] fp32
+ *   CSA_OP_TOPK      candidate lists for n_rows score rows of up to max_cols
+ *   CSA_OP_ATTENTION split-KV partial results for n_rows queries, max_cols =
+ *                    the largest number of rows (entries + window) a query reads */
+enum { CSA_OP_COMPRESS = 0, CSA_OP_TOPK = 1, CSA_OP_ATTENTION = 2 };
+int csa_workspace_size(const csa_layer_desc* layer, int op, int n_rows, int max_cols, int top_k,
+                       size_t* bytes);
+
+/*
+ * a1: token-level compressor ([DD] §1.2 Step 1 and §1.3; [YP] eqs. (6),(7),
+ * (10),(11)).  Projects the call's new rows, H . W^T, into the workspace;
+ * for every token t with (t+1) % m == 0 emits entry i = (t+1)/m - 1:
+ *   per channel, softmax over the m logits Z^a + B^a of block i and (CSA,
+ *   i >= 1) the m logits Z^b + B^b of block i-1, then the weighted sum of the
+ *   matching C rows; entry 0 soft-maxes over its own block only.
+ * The main entry is then RMS-normalised (gamma, norm_eps) and its last r
+ * channels rotated at m*i ([DD] §1.4).  CSA also emits the indexer key, the
+ * same merge over the indexer's own projection, without norm or RoPE.  Every
+ * new token also yields its window row: C^a (HCA: C) normalised with gamma
+ * and rotated at its position.  Rows of earlier calls come from the tail
+ * ring, which is updated at the end of the call.
+ *   H         [n_tokens x d] act_fmt           W      [4c x d] (HCA [2c x d]) act_fmt
+ *   W_idx     [4c_idx x d] act_fmt (CSA)       B_a, B_b [m x c] fp32 (HCA: B_a only)
+ *   B_a_idx, B_b_idx [m x c_idx] fp32 (CSA)    gamma  [c] fp32
+ *   state     [n_req slots] read/write (tail ring)
+ *   out_entries [max_entries x c] fp32, out_keys [max_entries x c_idx] fp32 (CSA),
+ *   out_meta  [max_entries x 2] int32 (request, entry index), out_count [1] int32:
+ *             entries in (request, index) order; max_entries must be
+ *             >= sum over requests of floor((start+n)/m) - floor(start/m)
+ *             (checked on the device: excess entries are dropped and
+ *             out_count reports the true total).
+ *   out_win   [n_tokens x c] fp32 window rows
+ *   ws        >= csa_workspace_size(CSA_OP_COMPRESS, n_tokens)
+ */
+int csa_compress_kv(void* stream, const csa_layer_desc* layer, const csa_batch* batch,
+                    int n_tokens, int d, const void* H, const void* W, const void* W_idx,
+                    const float* B_a, const float* B_b, const float* B_a_idx, const float* B_b_idx,
+                    const float* gamma, void* state,
+                    float* out_entries, float* out_keys, int32_t* out_meta, int32_t* out_count,
+                    int max_entries, float* out_win, void* ws, size_t ws_bytes);
+
+/*
+ * a2: cache append ([DD] §1.5, §7; [AD] cache section).  Stores the entries,
+ * keys and window rows that csa_compress_kv produced:
+ *   entry (r, i)  -> slot i % epb of physical block block_table[r][i / epb]
+ *                    in kv_cache (format kv_fmt), key likewise in idx_cache;
+ *   window row of the token at position p -> ring slot p % win_cap of state r.
+ * FP8 block scale, per call and block, all decisions in fp32:
+ *   s_old = 0 if the call's first new slot in the block is 0, else the header;
+ *   s = max(s_old, amax / 448) with amax over the new entries' FP8 channels;
+ *   if s > s_old, earlier slots are re-encoded E4M3(decode(code)*s_old / s);
+ *   new entries are encoded E4M3(x / s) (round to nearest even, saturating).
+ * bf16 stores round to nearest even; MXFP4 keys use OCP MX rules (E8M0
+ * X = floor(log2 amax) - 2, E2M1 nearest-even, saturating at 6).
+ *   entries/keys/meta/count as written by csa_compress_kv; win [n_tokens x c] fp32.
+ */
+int csa_cache_append(void* stream, const csa_layer_desc* layer, const csa_batch* batch,
+                     int n_tokens, const float* entries, const float* keys, const int32_t* meta,
+                     const int32_t* count, int max_entries, const float* win,
+                     void* kv_cache, void* idx_cache, void* state);
+
+/*
+ * a3: Lightning Indexer scores ([DD] §1.2 Step 2; [YP] eq. (8); [DD] §6.2).
+ * For every new token t of the batch (query row g = its global row) and every
+ * visible entry s < V_t:
+ *   scores[g*ld + s] = round_score_fmt( sum_h w[g][h] * ReLU(q[g][h] . K[s]) )
+ * with fp32 accumulation; -0 is stored as +0.  For CSA_IDX_MXFP4 the query
+ * heads are first quantised to MXFP4 (same rules as the keys) and the
+ * product runs on the dequantised values.  Also writes n_valid[g] = V_t.
+ *   q_idx [n_tokens x n_idx_heads x c_idx] act_fmt, w [n_tokens x n_idx_heads] fp32
+ *   scores [n_tokens x ld] score_fmt (ld >= the largest V_t; columns >= V_t untouched)
+ */
+int csa_index_scores(void* stream, const csa_layer_desc* layer, const csa_batch* batch,
+                     int n_tokens, const void* q_idx, const float* w, const void* idx_cache,
+                     void* scores, int ld, int32_t* n_valid);
+
+/*
+ * a4: top-k selector ([DD] §1.2 Step 2; [AD]: k = 512 / 1024).  For each row
+ * g: the k largest of scores[g*ld + 0 .. n_valid[g]-1] (ties: the lower index
+ * wins), written to out_idx[g*k ..] in ascending index order, padded with -1
+ * when n_valid[g] < k.  Exact (integer radix selection on order-preserving
+ * keys).  ws >= csa_workspace_size(CSA_OP_TOPK, n_rows, ld, k).
+ */
+int csa_topk_select(void* stream, int score_fmt, int n_rows, const void* scores, int ld,
+                    const int32_t* n_valid, int k, int32_t* out_idx, void* ws, size_t ws_bytes);
+
+/*
+ * a5: sparse shared-KV MQA with window and sink ([DD] §1.2 Step 2, §1.4
+ * table and sink equation; [YP] eq. (9)).  For each new token t (row g) and
+ * head h: q = RoPE_t(RMSNorm_gamma_q(q_raw[g][h])); rows X = the entries
+ * sel[g][0..top_k) (skipping -1) and the window rows of positions
+ * max(0, t-n_win+1) .. t (from the ring, which csa_cache_append has already
+ * filled for this call's tokens); z_j = q . X_j / sqrt(c);
+ *   o = sum_j exp(z_j) X_j / (sum_j exp(z_j) + exp(sinks[h])), then RoPE_-t.
+ *   q [n_tokens x n_heads x c] act_fmt, q_gamma [c] fp32, sinks [n_heads] fp32,
+ *   sel [n_tokens x top_k] int32, out [n_tokens x n_heads x c] out_fmt
+ *   ws >= csa_workspace_size(CSA_OP_ATTENTION, n_tokens, top_k + n_win)
+ */
+int csa_sparse_mqa(void* stream, const csa_layer_desc* layer, const csa_batch* batch,
+                   int n_tokens, const void* q, const float* q_gamma, const int32_t* sel,
+                   const void* kv_cache, const void* state, const float* sinks, void* out,
+                   void* ws, size_t ws_bytes);
+
+/*
+ * a6: HCA dense MQA ([DD] §1.3; [YP] HCA attention).  As csa_sparse_mqa, with
+ * the rows being every visible entry s < V_t followed by the window.
+ *   ws >= csa_workspace_size(CSA_OP_ATTENTION, n_tokens, max_ctx/m + n_win)
+ */
+int csa_hca_attention(void* stream, const csa_layer_desc* layer, const csa_batch* batch,
+                      int n_tokens, const void* q, const float* q_gamma, const void* kv_cache,
+                      const void* state, const float* sinks, void* out, void* ws, size_t ws_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_H */

@@ -1,0 +1,193 @@
+// Device helpers shared by the gfx950 kernels: number formats, MFMA fragment
+// steps, RoPE tables, batch bookkeeping and wave/block reductions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define CSA_DEV __device__ __forceinline__
+
+namespace csa {
+
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
+
+// ---------------------------------------------------------------------------
+// number formats
+// ---------------------------------------------------------------------------
+
+CSA_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// Round to nearest even on the dropped 16 bits (inputs are finite).
+CSA_DEV uint16_t f32_to_bf16(float x)
+{
+    uint32_t u = __float_as_uint(x);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+CSA_DEV uint32_t pack_bf16x2(float a, float b)
+{
+    return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+// OCP E4M3FN -> fp32 (exact).  0x7F/0xFF (NaN) never occur in stored data.
+CSA_DEV float e4m3_to_f32(uint32_t q)
+{
+    uint32_t s = (q & 0x80u) << 24;
+    uint32_t E = (q >> 3) & 15u, M = q & 7u;
+    float v = (E == 0) ? (float)M * 0.001953125f                                 // M * 2^-9
+                       : __uint_as_float(((E + 120u) << 23) | (M << 20));       // 2^(E-7) * (1 + M/8)
+    return __uint_as_float(__float_as_uint(v) | s);
+}
+
+// E4M3FN code of an fp32 value: round to nearest even, saturate to +-448,
+// a zero result is stored as +0.
+CSA_DEV uint32_t f32_to_e4m3(float v)
+{
+    uint32_t s = (__float_as_uint(v) >> 24) & 0x80u;
+    float a = fabsf(v);
+    if (a >= 448.0f) return s | 0x7Eu;
+    if (a < 0.015625f) {                       // below 2^-6: spacing 2^-9
+        float m = rintf(a * 512.0f);           // exact scaling, then RNE
+        if (m == 0.0f) return 0u;
+        return s | (uint32_t)m;                // m == 8 is the smallest normal 0x08
+    }
+    int e = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;   // a in [2^e, 2^(e+1))
+    float m = rintf(ldexpf(a, 3 - e));         // in [8, 16]
+    if (m == 16.0f) { m = 8.0f; e += 1; }
+    if (e > 8 || (e == 8 && m > 14.0f)) return s | 0x7Eu;
+    return s | ((uint32_t)(e + 7) << 3) | ((uint32_t)m - 8u);
+}
+
+// OCP E2M1 magnitude table and encoder (round to nearest even, saturate at 6).
+CSA_DEV float e2m1_to_f32(uint32_t q)
+{
+    uint32_t mag = q & 7u;
+    float v = (mag < 4u) ? 0.5f * (float)mag : (mag == 4u ? 2.0f : mag == 5u ? 3.0f : mag == 6u ? 4.0f : 6.0f);
+    return (q & 8u) ? -v : v;
+}
+
+CSA_DEV uint32_t f32_to_e2m1(float v)
+{
+    float a = fabsf(v);
+    uint32_t code;
+    if (a >= 6.0f) code = 7u;
+    else if (a < 2.0f) code = (uint32_t)rintf(a * 2.0f);                 // 0..4 (4 == 2.0)
+    else if (a < 4.0f) { float m = rintf(a); code = m == 2.0f ? 4u : (m == 3.0f ? 5u : 6u); }
+    else { float m = rintf(a * 0.5f); code = m == 2.0f ? 6u : 7u; }
+    if (code == 0u) return 0u;
+    return code | ((v < 0.0f) ? 8u : 0u);
+}
+
+// E8M0 code of an MX block whose largest magnitude is amax: the exponent
+// floor(log2 amax) - 2 (E2M1's largest binade), biased by 127.
+CSA_DEV int mx_scale_code(float amax)
+{
+    if (!(amax > 0.0f)) return 127;
+    int e;
+    frexpf(amax, &e);                          // amax in [2^(e-1), 2^e)
+    int code = (e - 1) - 2 + 127;
+    return code < 0 ? 0 : (code > 254 ? 254 : code);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA steps.  A "fragment" is 16 bytes per lane: 8 bf16 or 4 fp32 values of
+// one row (A) / one column (B).  In a 16x16 tile, lane l holds row (col) l%16
+// and lane group g = l/16 holds its own slice of the contraction index; the
+// same (g, element) -> k mapping is used for A and B, so the sum covers every
+// k once.  The accumulator layout is the hardware's: lane l holds
+// D[4*g + i][l % 16], i = 0..3.
+// ---------------------------------------------------------------------------
+
+struct MmaBF16 {
+    static constexpr int K = 32;               // contraction length of one step (8 per lane group)
+    static CSA_DEV f32x4_t step(uint4 a, uint4 b, f32x4_t c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    }
+};
+
+struct MmaF32 {
+    static constexpr int K = 16;               // 4 per lane group, one MFMA per element
+    static CSA_DEV f32x4_t step(uint4 a, uint4 b, f32x4_t c)
+    {
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+        return c;
+    }
+};
+
+CSA_DEV f32x4_t zero4() { f32x4_t z = {0.f, 0.f, 0.f, 0.f}; return z; }
+
+// ---------------------------------------------------------------------------
+// batch bookkeeping
+// ---------------------------------------------------------------------------
+
+// Request owning global token row g: the largest r with cu_new[r] <= g.
+CSA_DEV int find_request(const int32_t* cu_new, int n_req, int g)
+{
+    int lo = 0, hi = n_req - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (cu_new[mid] <= g) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// ---------------------------------------------------------------------------
+// reductions (fixed order: butterfly over the wave, then waves in index order)
+// ---------------------------------------------------------------------------
+
+CSA_DEV float wave_sum(float v)
+{
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+CSA_DEV float wave_max(float v)
+{
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// Sum over the block (blockDim.x a multiple of 64, <= 1024); every thread gets
+// the total.  `red` is LDS scratch of >= 16 floats.
+CSA_DEV float block_sum(float v, float* red)
+{
+    int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    v = wave_sum(v);
+    __syncthreads();
+    if (lane == 0) red[w] = v;
+    __syncthreads();
+    float t = 0.f;
+    for (int i = 0; i < nw; ++i) t += red[i];
+    return t;
+}
+
+CSA_DEV float block_max(float v, float* red)
+{
+    int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    v = wave_max(v);
+    __syncthreads();
+    if (lane == 0) red[w] = v;
+    __syncthreads();
+    float t = red[0];
+    for (int i = 1; i < nw; ++i) t = fmaxf(t, red[i]);
+    return t;
+}
+
+// RoPE angle for pair j of r rotary channels at position pos, in double so
+// that positions up to millions keep full fp32 accuracy after reduction.
+CSA_DEV void rope_cs(double pos, int j, int r, float theta, float* cs, float* sn)
+{
+    double ang = pos * pow((double)theta, -2.0 * (double)j / (double)r);
+    double s, c;
+    sincos(ang, &s, &c);
+    *cs = (float)c;
+    *sn = (float)s;
+}
+
+}  // namespace csa

@@ -1,0 +1,289 @@
+// a1: token-level compressor on gfx950.
+//
+// Follows "DeepSeek-V4 内部机制" §1.2 Step 1 (CSA: per-channel softmax over
+// the overlapping 2m window of Z + B, weighted sum of the C rows) and §1.3
+// (HCA: m' rows, no overlap); yunpan.plus explainer eqs. (6)-(7), (10)-(11).
+// Entry normalisation and partial RoPE: "DeepSeek-V4 内部机制" §1.4 table.
+//
+// Kernels, in launch order:
+//   proj_*      H . W^T into the workspace (fp32 out), MFMA with fragments
+//               loaded straight from global memory (rows are k-contiguous).
+//   merge       one workgroup per completed entry: softmax-merge per channel,
+//               then RMSNorm + RoPE of the main entry; indexer keys raw.
+//   window_rows one workgroup per new token: RMSNorm + RoPE of its C^a row.
+//   tail_update copies the newest projected rows into the state's tail ring
+//               (after merge has read the old ring contents).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace csa {
+
+// ---------------------------------------------------------------------------
+// projection: P[M x N] = X[M x K] . Wt[N x K]^T, Wt rows n < n_main from W,
+// the rest from Wi.  T is float or uint16_t (bf16).
+// ---------------------------------------------------------------------------
+
+template <class T, class MMA>
+__global__ __launch_bounds__(256) void proj_large(const T* __restrict__ X, const T* __restrict__ W,
+                                                  const T* __restrict__ Wi, int n_main, int N, int M, int K,
+                                                  float* __restrict__ P)
+{
+    constexpr int EPF = 16 / sizeof(T);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
+    const int m0 = blockIdx.y * 128 + (wave >> 1) * 64;
+    const int n0 = blockIdx.x * 128 + (wave & 1) * 64;
+    const T* ap[4];
+    const T* bp[4];
+    bool av[4], bv[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        int m = m0 + 16 * t + li;
+        av[t] = m < M;
+        ap[t] = X + (size_t)(av[t] ? m : 0) * K + g * EPF;
+        int n = n0 + 16 * t + li;
+        bv[t] = n < N;
+        int nn = bv[t] ? n : 0;
+        bp[t] = (nn < n_main ? W + (size_t)nn * K : Wi + (size_t)(nn - n_main) * K) + g * EPF;
+    }
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    for (int k0 = 0; k0 < K; k0 += MMA::K) {
+        uint4 a[4], b[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            a[t] = av[t] ? *(const uint4*)(ap[t] + k0) : z;
+            b[t] = bv[t] ? *(const uint4*)(bp[t] + k0) : z;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = MMA::step(a[i], b[j], acc[i][j]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int n = n0 + 16 * j + li;
+            if (n >= N) continue;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                int m = m0 + 16 * i + 4 * g + q;
+                if (m < M) P[(size_t)m * N + n] = acc[i][j][q];
+            }
+        }
+}
+
+// Few rows (decode): a 16 x 16 output tile per workgroup, the four waves
+// split K into contiguous quarters and are summed in wave order.
+template <class T, class MMA>
+__global__ __launch_bounds__(256) void proj_small(const T* __restrict__ X, const T* __restrict__ W,
+                                                  const T* __restrict__ Wi, int n_main, int N, int M, int K,
+                                                  float* __restrict__ P)
+{
+    constexpr int EPF = 16 / sizeof(T);
+    __shared__ float red[4][64][4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
+    const int m = blockIdx.y * 16 + li, n = blockIdx.x * 16 + li;
+    const bool av = m < M, bv = n < N;
+    const int kq = K / 4, kb = wave * kq;
+    const T* ap = X + (size_t)(av ? m : 0) * K + kb + g * EPF;
+    int nn = bv ? n : 0;
+    const T* bp = (nn < n_main ? W + (size_t)nn * K : Wi + (size_t)(nn - n_main) * K) + kb + g * EPF;
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    f32x4_t acc0 = zero4(), acc1 = zero4();
+    int k0 = 0;
+    for (; k0 + 2 * MMA::K <= kq; k0 += 2 * MMA::K) {
+        uint4 a0 = av ? *(const uint4*)(ap + k0) : z;
+        uint4 b0 = bv ? *(const uint4*)(bp + k0) : z;
+        uint4 a1 = av ? *(const uint4*)(ap + k0 + MMA::K) : z;
+        uint4 b1 = bv ? *(const uint4*)(bp + k0 + MMA::K) : z;
+        acc0 = MMA::step(a0, b0, acc0);
+        acc1 = MMA::step(a1, b1, acc1);
+    }
+    for (; k0 < kq; k0 += MMA::K) {
+        uint4 a0 = av ? *(const uint4*)(ap + k0) : z;
+        uint4 b0 = bv ? *(const uint4*)(bp + k0) : z;
+        acc0 = MMA::step(a0, b0, acc0);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) red[wave][lane][q] = acc0[q] + acc1[q];
+    __syncthreads();
+    if (wave == 0) {
+        const int col = blockIdx.x * 16 + li;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float v = red[0][lane][q] + red[1][lane][q] + red[2][lane][q] + red[3][lane][q];
+            int row = blockIdx.y * 16 + 4 * g + q;
+            if (row < M && col < N) P[(size_t)row * N + col] = v;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm + RoPE of one row held in LDS (xs[0..c)), written to out.
+// ---------------------------------------------------------------------------
+
+CSA_DEV void norm_rope_store(float* xs, float* red, int c, int r, const float* gamma, float eps, double pos,
+                             float theta, float* out)
+{
+    float ss = 0.f;
+    for (int ch = threadIdx.x; ch < c; ch += blockDim.x) ss += xs[ch] * xs[ch];
+    ss = block_sum(ss, red);
+    const float inv = 1.0f / sqrtf(ss / (float)c + eps);
+    __syncthreads();
+    for (int ch = threadIdx.x; ch < c; ch += blockDim.x) xs[ch] = gamma[ch] * (xs[ch] * inv);
+    __syncthreads();
+    for (int j = threadIdx.x; j < r / 2; j += blockDim.x) {
+        float cs, sn;
+        rope_cs(pos, j, r, theta, &cs, &sn);
+        int d = c - r + 2 * j;
+        float a = xs[d], b = xs[d + 1];
+        xs[d] = a * cs - b * sn;
+        xs[d + 1] = a * sn + b * cs;
+    }
+    __syncthreads();
+    for (int ch = threadIdx.x; ch < c; ch += blockDim.x) out[ch] = xs[ch];
+}
+
+// ---------------------------------------------------------------------------
+// merge: one workgroup per entry completed in this call
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void merge_kernel(CompressArgs a)
+{
+    __shared__ float xs[512];
+    __shared__ float red[16];
+    const int e = blockIdx.x;
+    // locate the entry: requests in order, entries of a request in index order
+    int total = 0, req = -1, ent = 0;
+    for (int rr = 0; rr < a.n_req; ++rr) {
+        int s = a.start_pos[rr], n = a.cu_new[rr + 1] - a.cu_new[rr];
+        int cnt = (s + n) / a.m - s / a.m;
+        if (req < 0 && e < total + cnt) { req = rr; ent = s / a.m + (e - total); }
+        total += cnt;
+    }
+    if (e == 0 && threadIdx.x == 0) *a.out_count = total;
+    if (req < 0 || e >= a.max_entries) return;
+
+    const int s0 = a.start_pos[req], cu = a.cu_new[req];
+    const float* tail = (const float*)((const char*)a.state + (size_t)req * a.state_stride + a.tail_off);
+    const int m = a.m, c = a.c, cI = a.c_idx;
+    const bool has_b = a.overlap && ent >= 1;
+    const int nch = c + (a.overlap ? cI : 0);
+    for (int ch = threadIdx.x; ch < nch; ch += blockDim.x) {
+        const bool ix = ch >= c;
+        const int cc = ix ? ch - c : ch;
+        const int w = ix ? cI : c;
+        const int base = ix ? 4 * c : 0;
+        const float* Ba = ix ? a.B_a_idx : a.B_a;
+        const float* Bb = ix ? a.B_b_idx : a.B_b;
+        const int colCa = base + cc;
+        const int colCb = base + w + cc;
+        const int colZa = base + (a.overlap ? 2 * w : w) + cc;
+        const int colZb = base + 3 * w + cc;
+        float mx = -INFINITY;
+        for (int r = 0; r < m; ++r) {
+            int p = m * ent + r;
+            const float* row = (p >= s0) ? a.P + (size_t)(cu + p - s0) * a.ncols : tail + (size_t)(p % a.R) * a.ncols;
+            mx = fmaxf(mx, row[colZa] + Ba[r * w + cc]);
+        }
+        if (has_b)
+            for (int r = 0; r < m; ++r) {
+                int p = m * (ent - 1) + r;
+                const float* row = (p >= s0) ? a.P + (size_t)(cu + p - s0) * a.ncols : tail + (size_t)(p % a.R) * a.ncols;
+                mx = fmaxf(mx, row[colZb] + Bb[r * w + cc]);
+            }
+        float den = 0.f, acc = 0.f;
+        for (int r = 0; r < m; ++r) {
+            int p = m * ent + r;
+            const float* row = (p >= s0) ? a.P + (size_t)(cu + p - s0) * a.ncols : tail + (size_t)(p % a.R) * a.ncols;
+            float wgt = expf(row[colZa] + Ba[r * w + cc] - mx);
+            den += wgt;
+            acc += wgt * row[colCa];
+        }
+        if (has_b)
+            for (int r = 0; r < m; ++r) {
+                int p = m * (ent - 1) + r;
+                const float* row = (p >= s0) ? a.P + (size_t)(cu + p - s0) * a.ncols : tail + (size_t)(p % a.R) * a.ncols;
+                float wgt = expf(row[colZb] + Bb[r * w + cc] - mx);
+                den += wgt;
+                acc += wgt * row[colCb];
+            }
+        float v = acc / den;
+        if (ix) a.out_keys[(size_t)e * cI + cc] = v;
+        else xs[cc] = v;
+    }
+    __syncthreads();
+    norm_rope_store(xs, red, c, a.r, a.gamma, a.eps, (double)m * (double)ent, a.theta, a.out_entries + (size_t)e * c);
+    if (threadIdx.x == 0) {
+        a.out_meta[2 * e] = req;
+        a.out_meta[2 * e + 1] = ent;
+    }
+}
+
+__global__ __launch_bounds__(256) void window_rows_kernel(CompressArgs a)
+{
+    __shared__ float xs[512];
+    __shared__ float red[16];
+    const int gtok = blockIdx.x;
+    const int req = find_request(a.cu_new, a.n_req, gtok);
+    const int pos = a.start_pos[req] + (gtok - a.cu_new[req]);
+    const float* row = a.P + (size_t)gtok * a.ncols;       // C^a (CSA) or C (HCA) at column 0
+    for (int ch = threadIdx.x; ch < a.c; ch += blockDim.x) xs[ch] = row[ch];
+    __syncthreads();
+    norm_rope_store(xs, red, a.c, a.r, a.gamma, a.eps, (double)pos, a.theta, a.out_win + (size_t)gtok * a.c);
+}
+
+__global__ __launch_bounds__(256) void tail_update_kernel(CompressArgs a)
+{
+    const int j = blockIdx.x, req = blockIdx.y;
+    const int cu = a.cu_new[req], n = a.cu_new[req + 1] - cu, s0 = a.start_pos[req];
+    const int keep = n < a.R ? n : a.R;
+    if (j >= keep) return;
+    const int p = s0 + n - keep + j;
+    float* tail = (float*)((char*)a.state + (size_t)req * a.state_stride + a.tail_off);
+    const float* src = a.P + (size_t)(cu + n - keep + j) * a.ncols;
+    float* dst = tail + (size_t)(p % a.R) * a.ncols;
+    for (int ch = threadIdx.x; ch < a.ncols; ch += blockDim.x) dst[ch] = src[ch];
+}
+
+// ---------------------------------------------------------------------------
+// host launcher
+// ---------------------------------------------------------------------------
+
+hipError_t launch_compress(hipStream_t st, const CompressArgs& a, const void* H, const void* W, const void* Wi,
+                           int n_main, int d, bool bf16, int n_tokens)
+{
+    const int N = a.ncols, M = n_tokens;
+    if (M > 0) {
+        if (M <= 64) {
+            dim3 grid((N + 15) / 16, (M + 15) / 16);
+            if (bf16)
+                proj_small<uint16_t, MmaBF16><<<grid, 256, 0, st>>>((const uint16_t*)H, (const uint16_t*)W,
+                                                                    (const uint16_t*)Wi, n_main, N, M, d, a.P);
+            else
+                proj_small<float, MmaF32><<<grid, 256, 0, st>>>((const float*)H, (const float*)W, (const float*)Wi,
+                                                                n_main, N, M, d, a.P);
+        } else {
+            dim3 grid((N + 127) / 128, (M + 127) / 128);
+            if (bf16)
+                proj_large<uint16_t, MmaBF16><<<grid, 256, 0, st>>>((const uint16_t*)H, (const uint16_t*)W,
+                                                                    (const uint16_t*)Wi, n_main, N, M, d, a.P);
+            else
+                proj_large<float, MmaF32><<<grid, 256, 0, st>>>((const float*)H, (const float*)W, (const float*)Wi,
+                                                                n_main, N, M, d, a.P);
+        }
+    }
+    merge_kernel<<<a.max_entries > 0 ? a.max_entries : 1, 256, 0, st>>>(a);
+    if (M > 0) {
+        window_rows_kernel<<<M, 256, 0, st>>>(a);
+        tail_update_kernel<<<dim3(a.R, a.n_req), 256, 0, st>>>(a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace csa

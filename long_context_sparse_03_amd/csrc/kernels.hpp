@@ -1,0 +1,112 @@
+// Argument blocks and host-side launchers of the gfx950 kernels.  Everything
+// here is internal to libcsa.so; the public interface is include/csa.h.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa {
+
+struct CompressArgs {
+    float* P;                  // projection workspace [n_tokens x ncols]
+    int ncols;
+    void* state;               // state slots
+    size_t state_stride;       // bytes per slot
+    size_t tail_off;           // byte offset of the tail ring inside a slot
+    int R;                     // tail ring rows
+    const int32_t* cu_new;
+    const int32_t* start_pos;
+    int n_req;
+    int m, overlap, c, c_idx, r;
+    const float *B_a, *B_b, *B_a_idx, *B_b_idx, *gamma;
+    float eps, theta;
+    float* out_entries;
+    float* out_keys;
+    int32_t* out_meta;
+    int32_t* out_count;
+    int max_entries;
+    float* out_win;
+};
+
+hipError_t launch_compress(hipStream_t st, const CompressArgs& a, const void* H, const void* W, const void* Wi,
+                           int n_main, int d, bool bf16, int n_tokens);
+
+struct AppendArgs {
+    const float* entries;
+    const float* keys;
+    const int32_t* meta;
+    const int32_t* count;
+    int max_entries;
+    const float* win;
+    int n_tokens;
+    const int32_t* cu_new;
+    const int32_t* start_pos;
+    const int32_t* block_table;
+    int n_req, max_blocks;
+    int c, r, c_idx, epb;
+    int kv_fmt, idx_fmt, win_bf16;
+    void* kv;
+    size_t kv_block_bytes;
+    void* idx;
+    size_t idx_block_bytes;
+    void* state;
+    size_t state_stride;
+    int win_cap;
+};
+
+hipError_t launch_append(hipStream_t st, const AppendArgs& a);
+
+struct IndexArgs {
+    const void* q;             // [n_tokens x nh x cI] f32 or bf16
+    const float* w;            // [n_tokens x nh]
+    const void* keys;          // indexer-key pool
+    size_t key_block_bytes;
+    const int32_t* cu_new;
+    const int32_t* start_pos;
+    const int32_t* block_table;
+    int n_req, max_blocks;
+    int m, epb, nh, cI;
+    int q_bf16, idx_fmt, score_bf16;
+    void* scores;
+    int ld;
+    int32_t* n_valid;
+    int n_tokens;
+};
+
+hipError_t launch_index(hipStream_t st, const IndexArgs& a, int max_visible, int max_new);
+
+hipError_t launch_topk(hipStream_t st, int score_bf16, int n_rows, const void* scores, int ld,
+                       const int32_t* n_valid, int k, int32_t* out, void* ws, int max_cols);
+size_t topk_workspace(int n_rows, int max_cols, int k);
+
+struct AttnArgs {
+    const void* q;             // [n_tokens x nh x c] f32 or bf16
+    const float* q_gamma;
+    const int32_t* sel;        // [n_tokens x k] or null (dense)
+    int k;
+    const void* kv;
+    size_t kv_block_bytes;
+    const void* state;
+    size_t state_stride;
+    int win_cap, n_win;
+    const int32_t* cu_new;
+    const int32_t* start_pos;
+    const int32_t* block_table;
+    int n_req, max_blocks;
+    int m, epb, c, r, nh;
+    int kv_fmt, q_bf16, win_bf16, out_bf16;
+    float eps, theta, scale_log2;
+    const float* sinks;
+    void* out;
+    float* ws;                 // split partials
+    int n_tokens;
+    int rows_max;              // rows per query (slots): k + n_win, or max entries + n_win
+    int n_splits;
+    int tiles_per_split;
+};
+
+int attention_splits(int n_tokens, int n_heads, int rows_max);
+size_t attention_workspace(int n_tokens, int n_heads, int c, int rows_max);
+hipError_t launch_attention(hipStream_t st, AttnArgs a);
+
+}  // namespace csa
