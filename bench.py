@@ -1,0 +1,230 @@
+"""Decode throughput of the CSA / HCA hot path on one MI355X.
+
+A step is one decode token for every request through every layer of the
+workload: compress_kv, cache_append, index_scores, topk_select and
+sparse_mqa per CSA layer; compress_kv, cache_append and hca_attention per HCA
+layer.  Inputs (caches, window rings, compressor tails, weights, queries) are
+synthetic, resident in HBM before timing starts, and the cache is rotated
+over several replicas so that the 256 MB last-level cache cannot hold a
+step's working set.  Each replica's step is captured once in a HIP graph and
+replayed.  Prints one JSON line.
+
+Workloads:
+  csa_decode_128k  16 requests x 131072 cached tokens, one CSA layer
+                   (c=512: 448 fp8 + 64 bf16 channels, per-block scale; m=4;
+                   64 heads; indexer 64 x 128 bf16; top-512; window 128; d=4096)
+  hybrid_decode_1m 4 requests x 1048576 cached tokens, layers CSA, HCA, CSA,
+                   HCA (CSA: 128 heads, MXFP4 indexer, top-1024; HCA: m'=128;
+                   c=512 fp8/bf16 KV; window 128; d=7168)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA, published
+
+
+def workload_def(name: str):
+    from long_context_sparse_03_amd import abi, presets
+    if name == "csa_decode_128k":
+        return dict(descs=[presets.csa_flash_decode()], d=presets.D_FLASH, n_req=16, ctx=131072, replicas=3)
+    if name == "hybrid_decode_1m":
+        return dict(descs=[presets.csa_pro(idx_fmt=abi.IDX_MXFP4), presets.hca_pro(),
+                           presets.csa_pro(idx_fmt=abi.IDX_MXFP4), presets.hca_pro()],
+                    d=presets.D_PRO, n_req=4, ctx=1 << 20, replicas=2)
+    raise SystemExit(f"unknown workload {name}")
+
+
+def algorithmic_bytes(wd) -> dict:
+    """Bytes the method must move per decode step (no re-reads), by part."""
+    from long_context_sparse_03_amd import abi
+    n, ctx = wd["n_req"], wd["ctx"]
+    tot = {"index_keys": 0, "kv_rows": 0, "weights": 0, "q_out": 0, "other": 0}
+    idx_launch = 0
+    for desc in wd["descs"]:
+        c, r = desc.c, desc.rope_dim
+        rec = (c - r) + 2 * r if desc.kv_fmt == abi.KV_FP8 else c * (2 if desc.kv_fmt == abi.KV_BF16 else 4)
+        ncols = 4 * c + 4 * desc.c_idx if desc.kind == abi.KIND_CSA else 2 * c
+        tot["weights"] += ncols * wd["d"] * 2
+        tot["q_out"] += n * desc.n_heads * c * 2 * 2
+        if desc.kind == abi.KIND_CSA:
+            E = (ctx + 1) // desc.m
+            kb = desc.c_idx * 2 if desc.idx_fmt == abi.IDX_BF16 else desc.c_idx // 2 + desc.c_idx // 32
+            keys = n * E * kb
+            qw = n * desc.n_idx_heads * (desc.c_idx * 2 + 4)
+            sc = n * E * 2
+            tot["index_keys"] += keys
+            tot["kv_rows"] += n * (desc.top_k * (rec + 4) + desc.n_win * c * 2)
+            tot["other"] += qw + sc
+            idx_launch = keys + qw + sc
+        else:
+            E = (ctx + 1) // desc.m
+            tot["kv_rows"] += n * (E * (rec + 4) + desc.n_win * c * 2)
+    tot["total"] = sum(tot.values())
+    tot["index_launch"] = idx_launch
+    return tot
+
+
+def cpu_baseline(wd, n_tok: int, seed: int = 11) -> dict:
+    """The oracle (fp64, as it stands) on a bounded sample of the workload:
+    n_tok consecutive decode tokens of one request of the first CSA layer,
+    through the projection of the new tokens, index scores, top-k and
+    attention (the oracle runs a request's queries in parallel)."""
+    import oracle as O
+    from oracle import layer as OL
+    import synth
+    from long_context_sparse_03_amd import abi
+    desc = next(d for d in wd["descs"] if d.kind == abi.KIND_CSA)
+    spec = OL.Spec("csa", m=desc.m, c=desc.c, r=desc.rope_dim, n_h=desc.n_heads, n_hI=desc.n_idx_heads,
+                   c_I=desc.c_idx, top_k=desc.top_k, n_win=desc.n_win, kv_fmt="fp8",
+                   idx_fmt={abi.IDX_BF16: "bf16", abi.IDX_MXFP4: "mxfp4"}[desc.idx_fmt], score_fmt="bf16",
+                   win_fmt="bf16")
+    g = synth.rng(seed)
+    ctx, d = wd["ctx"], wd["d"]
+    E = (ctx + n_tok) // desc.m
+    W = synth.weights(g, d, 4 * desc.c + 4 * desc.c_idx)
+    ents = synth.normal(g, (E, desc.c))
+    keys = synth.normal(g, (E, desc.c_idx))
+    _, edeq = OL.store_entries(spec, ents, [(i, min(32, E - i)) for i in range(0, E, 32)])
+    _, kdeq = OL.store_keys(spec, keys)
+    win = np.zeros((ctx + n_tok, desc.c))
+    win[ctx - 127:] = OL.round_rows("bf16", synth.normal(g, (n_tok + 127, desc.c)))
+    qd = synth.queries(g, n_tok, desc.n_heads, desc.c, desc.n_idx_heads, desc.c_idx)
+    H = synth.normal(g, (n_tok, d))
+    sinks = synth.sinks(g, desc.n_heads)
+    pos = np.arange(ctx, ctx + n_tok)
+    t0 = time.perf_counter()
+    OL.project(H, W)
+    OL.csa_queries(spec, qd["q"], qd["qI"], qd["w"], pos, kdeq, edeq, win, sinks)
+    elapsed = time.perf_counter() - t0
+    return {"value": round(n_tok / elapsed, 3), "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"{n_tok} consecutive decode tokens of one request at {ctx} cached tokens, first CSA layer "
+                      f"({E} entries): new-token projection, index scores, top-{desc.top_k}, attention; fp64; "
+                      f"{elapsed:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="csa_decode_128k", choices=["csa_decode_128k", "hybrid_decode_1m"])
+    ap.add_argument("--replicas", type=int, default=0, help="cache replicas rotated between steps (0: workload default)")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=384, help="decode tokens in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--copy-probe", action="store_true", help="also run a 1 GiB device copy (HBM counter scale)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        raise SystemExit(2)
+
+    import torch
+    from long_context_sparse_03_amd.workloads import DecodeWorkload, torch_rows
+
+    wd = workload_def(args.workload)
+    reps = args.replicas or wd["replicas"]
+    total_steps = args.warmup + args.steps + 64
+    t_build = time.time()
+    wls = [DecodeWorkload(wd["descs"], wd["d"], wd["n_req"], wd["ctx"], max_steps=total_steps,
+                          rows=torch_rows(1000 + i), seed=i) for i in range(reps)]
+    torch.cuda.synchronize()
+    build_s = time.time() - t_build
+
+    if args.copy_probe:
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    stream = torch.cuda.Stream()
+    # per-kernel timing of the index scan, live, with events on the launch stream
+    n_eager = min(args.steps, 30)
+    idx_ms = []
+    with torch.cuda.stream(stream):
+        for i in range(4):
+            wls[i % reps].step()
+        stream.synchronize()
+        for i in range(n_eager):
+            wl = wls[i % reps]
+            evs = []
+            hooks = []
+            for st, _ in wl.layers:
+                if st.is_csa:
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    evs.append((e0, e1))
+                    hooks.append((lambda e=e0: e.record(stream), lambda e=e1: e.record(stream)))
+                else:
+                    hooks.append(None)
+            wl.step(hooks)
+            stream.synchronize()
+            idx_ms.extend(a.elapsed_time(b) for a, b in evs)
+
+    graphs = []
+    if not args.no_graph:
+        for wl in wls:
+            gph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gph, stream=stream):
+                wl.step()
+            graphs.append(gph)
+        torch.cuda.synchronize()
+
+    def run(i):
+        if graphs:
+            graphs[i % reps].replay()
+        else:
+            wls[i % reps].step()
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            run(i)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(args.steps):
+            run(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    tok_s = wd["n_req"] / (ms * 1e-3)
+
+    ab = algorithmic_bytes(wd)
+    idx_avg_ms = float(np.mean(idx_ms)) if idx_ms else None
+    roof = None
+    if idx_avg_ms:
+        achieved = ab["index_launch"] / (idx_avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "index_decode_kernel", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "launch_ms": round(idx_avg_ms, 5), "algorithmic_bytes_per_launch": ab["index_launch"]}
+    step_gbs = ab["total"] / (ms * 1e-3) / 1e9
+    cpu = cpu_baseline(wd, args.cpu_tokens) if args.cpu_tokens > 0 else None
+    line = {
+        "metric": "CSA decode tokens/s @128K & 1M ctx; achieved HBM GB/s and MFMA % of peak",
+        "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16/fp8 storage, fp32 accumulate", "data": "synthetic",
+        "config": {"workload": args.workload, "requests": wd["n_req"], "ctx": wd["ctx"],
+                   "layers": len(wd["descs"]), "d": wd["d"], "replicas": reps, "graph": not args.no_graph},
+        "step_hbm_gbs": round(step_gbs, 1), "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+        "step_algorithmic_bytes": ab,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "setup_s": round(build_s, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -168,7 +168,7 @@ int csa_workspace_size(const csa_layer_desc* layer, int op, int n_rows, int max_
     case CSA_OP_COMPRESS: *bytes = (size_t)n_rows * proj_cols(layer) * 4; return CSA_OK;
     case CSA_OP_TOPK:
         REQUIRE(top_k >= 1, CSA_EINVAL, "top_k=%d", top_k);
-        *bytes = csa::topk_workspace(n_rows, max_cols, top_k);
+        *bytes = csa::topk_workspace(n_rows, max_cols, top_k, layer->score_fmt == CSA_FMT_BF16);
         return CSA_OK;
     case CSA_OP_ATTENTION: *bytes = csa::attention_workspace(n_rows, layer->n_heads, layer->c, max_cols); return CSA_OK;
     default: return fail(CSA_EINVAL, "op=%d", op);
@@ -325,7 +325,9 @@ int csa_topk_select(void* stream, int score_fmt, int n_rows, const void* scores,
     REQUIRE(k >= 1 && k <= 2048, CSA_EUNSUPPORTED, "k=%d (1..2048)", k);
     REQUIRE(n_rows == 0 || (scores != nullptr && n_valid != nullptr && out_idx != nullptr), CSA_EINVAL,
             "NULL pointer argument");
-    const size_t need = csa::topk_workspace(n_rows, ld, k);
+    REQUIRE(csa::topk_supported(ld, k, score_fmt == CSA_FMT_BF16), CSA_EUNSUPPORTED,
+            "rows of %d scores with k=%d exceed the two-stage selector's capacity", ld, k);
+    const size_t need = csa::topk_workspace(n_rows, ld, k, score_fmt == CSA_FMT_BF16);
     REQUIRE(ws_bytes >= need && (need == 0 || ws != nullptr), CSA_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes,
             need);
     return hip_status(csa::launch_topk((hipStream_t)stream, score_fmt == CSA_FMT_BF16, n_rows, scores, ld, n_valid, k,

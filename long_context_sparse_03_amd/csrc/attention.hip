@@ -36,7 +36,7 @@ struct AttnCfg {
     using MMA = typename std::conditional<F32, MmaF32, MmaBF16>::type;
     using ET = typename std::conditional<F32, float, uint16_t>::type;   // LDS element type
     static constexpr int EPF = 16 / sizeof(ET);                          // elements per fragment
-    static constexpr int KP = C + 16 / sizeof(ET) * (F32 ? 1 : 1);      // Kt row stride (elements)
+    static constexpr int KP = C + (F32 ? 4 : 8);                         // Kt row stride (elements)
     static constexpr int VP = 32 + (F32 ? 4 : 8);                        // Vt row stride (elements)
     static constexpr int QSTEPS = C / MMA::K;                            // fragments of a query head
     static constexpr int DT = C / 16;                                    // 16-dim tiles of the output
@@ -49,19 +49,21 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
     using MMA = typename Cfg::MMA;
     using ET = typename Cfg::ET;
     constexpr int EPF = Cfg::EPF, KP = Cfg::KP, VP = Cfg::VP;
+    constexpr int DESC = 256;                                  // rows described at a time
 
     __shared__ __attribute__((aligned(16))) ET Kt[32 * KP];
     __shared__ __attribute__((aligned(16))) ET Vt[C * VP];
-    __shared__ float rscale[32];
-    __shared__ int rvalid[32];
+    __shared__ const char* rptr[DESC];                         // row start (null: masked row)
+    __shared__ float rscl[DESC];                               // fp8 block scale (1 otherwise)
     __shared__ float rcs[256], rsn[256];
-    __shared__ float inv_rms[4][16];
+    __shared__ float qg[C];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
     const int nthr = blockDim.x;
-    const int gq = blockIdx.x;
     const int NW = nthr >> 6;
+    const int gq = blockIdx.x;
     const int head = (blockIdx.y * NW + wave) * 16 + li;
+    const bool hv = head < a.nh;
     const int split = blockIdx.z;
     const int req = find_request(a.cu_new, a.n_req, gq);
     const int t = a.start_pos[req] + (gq - a.cu_new[req]);
@@ -76,41 +78,52 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
     const int tile0 = split * a.tiles_per_split;
     const int tile1 = min(n_tiles, tile0 + a.tiles_per_split);
 
-    // RoPE table at +t
+    // RoPE table at +t and the query norm gains
     for (int j = threadIdx.x; j < a.r / 2; j += nthr) rope_cs((double)t, j, a.r, a.theta, &rcs[j], &rsn[j]);
+    for (int j = threadIdx.x; j < C; j += nthr) qg[j] = a.q_gamma[j];
 
-    // per-head RMS of the raw query
-    const size_t qes = a.q_bf16 ? 2 : 4;
-    for (int hh = 0; hh < 16; ++hh) {
-        const int hd = (blockIdx.y * NW + wave) * 16 + hh;
-        float ss = 0.f;
-        if (hd < a.nh) {
-            const char* qp = (const char*)a.q + ((size_t)gq * a.nh + hd) * C * qes;
-            for (int d = lane; d < C; d += 64) {
-                float x = a.q_bf16 ? bf16_to_f32(((const uint16_t*)qp)[d]) : ((const float*)qp)[d];
-                ss += x * x;
-            }
-        }
-        ss = wave_sum(ss);
-        if (lane == 0) inv_rms[wave][hh] = 1.0f / sqrtf(ss / (float)C + a.eps);
-    }
-    __syncthreads();
-
-    // query fragments (B operand of S^T): head li, channels s*K + g*EPF + j
+    // query fragments (B operand of S^T): head li, channels s*K + g*EPF + j.
+    // One load per fragment; the RMS of the head is summed over the four lane
+    // groups that hold it.
     uint4 QB[Cfg::QSTEPS];
     {
-        const float inv = inv_rms[wave][li];
-        const bool hv = head < a.nh;
-        const char* qp = (const char*)a.q + ((size_t)gq * a.nh + (hv ? head : 0)) * C * qes;
+        const char* qp = (const char*)a.q + ((size_t)gq * a.nh + (hv ? head : 0)) * C * sizeof(ET);
+        float ss = 0.f;
+#pragma unroll
+        for (int s = 0; s < Cfg::QSTEPS; ++s) {
+            QB[s] = *(const uint4*)(qp + (size_t)(s * MMA::K + g * EPF) * sizeof(ET));
+            const uint32_t w4[4] = {QB[s].x, QB[s].y, QB[s].z, QB[s].w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                if constexpr (Cfg::F32) {
+                    float x = __uint_as_float(w4[h]);
+                    ss += x * x;
+                } else {
+                    float x0 = bf16_to_f32(w4[h] & 0xFFFF), x1 = bf16_to_f32(w4[h] >> 16);
+                    ss += x0 * x0 + x1 * x1;
+                }
+            }
+        }
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        const float inv = hv ? 1.0f / sqrtf(ss / (float)C + a.eps) : 0.f;
+        __syncthreads();                                       // RoPE table and gains ready
 #pragma unroll
         for (int s = 0; s < Cfg::QSTEPS; ++s) {
             const int d0 = s * MMA::K + g * EPF;
+            const uint32_t w4[4] = {QB[s].x, QB[s].y, QB[s].z, QB[s].w};
             float x[EPF];
 #pragma unroll
-            for (int j = 0; j < EPF; ++j) {
-                float v = a.q_bf16 ? bf16_to_f32(((const uint16_t*)qp)[d0 + j]) : ((const float*)qp)[d0 + j];
-                x[j] = hv ? a.q_gamma[d0 + j] * (v * inv) : 0.f;
+            for (int h = 0; h < 4; ++h) {
+                if constexpr (Cfg::F32) {
+                    x[h] = __uint_as_float(w4[h]);
+                } else {
+                    x[2 * h] = bf16_to_f32(w4[h] & 0xFFFF);
+                    x[2 * h + 1] = bf16_to_f32(w4[h] >> 16);
+                }
             }
+#pragma unroll
+            for (int j = 0; j < EPF; ++j) x[j] = qg[d0 + j] * (x[j] * inv);
             if (d0 >= nf) {
 #pragma unroll
                 for (int j = 0; j < EPF; j += 2) {
@@ -141,91 +154,122 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
     const size_t rec = KVF == 2 ? (size_t)(nf + 2 * a.r) : (size_t)C * (KVF == 0 ? 4 : 2);
     const size_t hdr = KVF == 2 ? 64 : 0;
     const char* ring = (const char*)a.state + (size_t)req * a.state_stride;
+    constexpr int CH = C / 8;                                  // 8-channel chunks per row
 
-    for (int tile = tile0; tile < tile1; ++tile) {
-        // ---- gather 32 rows into Kt (row-major), converting to the MMA type
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < 32 * (C / 8); idx += nthr) {
-            const int row = idx / (C / 8), ch = idx % (C / 8), d0 = ch * 8;
-            const int slot = tile * 32 + row;
-            float v[8];
-            bool valid = false;
+    // ---- row descriptors: source pointer and scale of DESC consecutive slots
+    auto describe = [&](int first_slot) {
+        for (int j = threadIdx.x; j < DESC; j += nthr) {
+            const int slot = first_slot + j;
+            const char* p = nullptr;
             float sc = 1.0f;
             if (slot < K0) {
                 const int e = dense ? slot : a.sel[(size_t)gq * a.k + slot];
-                valid = e >= 0 && e < V;
-                if (valid) {
+                if (e >= 0 && e < V) {
                     const int phys = a.block_table[(size_t)req * a.max_blocks + e / a.epb];
-                    const char* rp = (const char*)a.kv + (size_t)phys * a.kv_block_bytes + hdr + (size_t)(e % a.epb) * rec;
-                    if constexpr (KVF == 0) {
-                        const float4* p = (const float4*)((const float*)rp + d0);
-                        float4 x0 = p[0], x1 = p[1];
-                        v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
-                        v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
-                    } else if constexpr (KVF == 1) {
-                        uint4 u = *(const uint4*)((const uint16_t*)rp + d0);
-                        uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-                        for (int h = 0; h < 4; ++h) { v[2 * h] = bf16_to_f32(w4[h] & 0xFFFF); v[2 * h + 1] = bf16_to_f32(w4[h] >> 16); }
-                    } else {
-                        if (d0 < nf) {
-                            uint2 u = *(const uint2*)(rp + d0);
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) { v[j] = e4m3_to_f32((u.x >> (8 * j)) & 0xFF); v[4 + j] = e4m3_to_f32((u.y >> (8 * j)) & 0xFF); }
-                        } else {
-                            uint4 u = *(const uint4*)(rp + nf + 2 * (size_t)(d0 - nf));
-                            uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-                            for (int h = 0; h < 4; ++h) { v[2 * h] = bf16_to_f32(w4[h] & 0xFFFF); v[2 * h + 1] = bf16_to_f32(w4[h] >> 16); }
-                        }
-                        if (ch == 0) sc = *(const float*)((const char*)a.kv + (size_t)phys * a.kv_block_bytes);
-                    }
+                    const char* blk = (const char*)a.kv + (size_t)phys * a.kv_block_bytes;
+                    p = blk + hdr + (size_t)(e % a.epb) * rec;
+                    if (KVF == 2) sc = *(const float*)blk;
                 }
+            } else if (slot < n_slots && slot - K0 < nwr) {
+                p = ring + (size_t)((w0 + slot - K0) % a.win_cap) * C * win_es;
+            }
+            rptr[j] = p;
+            rscl[j] = sc;
+        }
+    };
+    // ---- gather: loads of one round (PF items per thread) of a tile, then
+    //      conversion into Kt (row-major) and Vt (transposed)
+    constexpr int PF = 4;                                      // items per thread per round
+    constexpr int NV = Cfg::F32 ? 2 : 1;                       // 16-byte loads per item
+    const int items = 32 * CH;
+    const int rounds = (items + PF * nthr - 1) / (PF * nthr);
+    // Loads are branch-free so that a round's loads stay in flight together:
+    // masked rows read a valid dummy address and are zeroed afterwards; an
+    // FP8 channel chunk is 8 bytes, every other chunk 16 (two 8-byte halves).
+    const char* dummy = (const char*)a.kv;
+    auto load_round = [&](int r, int tile, int drow0, uint4 (&raw)[PF][NV]) {
+        const int slot0 = tile * 32;
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+            const int idx = threadIdx.x + (r * PF + u) * nthr;
+            const int row = idx & 31, d0 = (idx >> 5) * 8;      // rows fastest: Vt writes spread over banks
+            const char* p = idx < items ? rptr[drow0 + row] : nullptr;
+            const bool ok = p != nullptr;
+            const char* base = ok ? p : dummy;
+            if constexpr (KVF == 2) {
+                const bool entry = slot0 + row < K0;
+                const char* a0 = entry ? (d0 < nf ? base + d0 : base + nf + 2 * (size_t)(d0 - nf)) : base + 2 * (size_t)d0;
+                const char* a1 = (entry && d0 < nf) ? a0 : a0 + 8;
+                const uint2 lo = *(const uint2*)a0, hi = *(const uint2*)a1;
+                raw[u][0] = sel16(ok, make_uint4(lo.x, lo.y, hi.x, hi.y));
+            } else if constexpr (KVF == 1) {
+                raw[u][0] = sel16(ok, ld16(base + 2 * (size_t)d0));
             } else {
-                const int j = slot - K0;
-                valid = j < nwr;
-                if (valid) {
-                    const int p = w0 + j;
-                    const char* rp = ring + (size_t)(p % a.win_cap) * C * win_es;
-                    if (a.win_bf16) {
-                        uint4 u = *(const uint4*)((const uint16_t*)rp + d0);
-                        uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-                        for (int h = 0; h < 4; ++h) { v[2 * h] = bf16_to_f32(w4[h] & 0xFFFF); v[2 * h + 1] = bf16_to_f32(w4[h] >> 16); }
-                    } else {
-                        const float4* p4 = (const float4*)((const float*)rp + d0);
-                        float4 x0 = p4[0], x1 = p4[1];
-                        v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
-                        v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
-                    }
-                }
+                raw[u][0] = sel16(ok, ld16(base + 4 * (size_t)d0));
+                raw[u][NV - 1] = sel16(ok, ld16(base + 4 * (size_t)d0 + 16));
             }
-            if (!valid) {
+        }
+    };
+    auto store_round = [&](int r, int tile, uint4 (&raw)[PF][NV]) {
+        const int slot0 = tile * 32;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) v[j] = 0.f;
-            }
+        for (int u = 0; u < PF; ++u) {
+            const int idx = threadIdx.x + (r * PF + u) * nthr;
+            if (idx >= items) break;
+            const int row = idx & 31, d0 = (idx >> 5) * 8;      // rows fastest: Vt writes spread over banks
+            const bool entry = slot0 + row < K0;
             ET* kr = Kt + row * KP + d0;
             if constexpr (Cfg::F32) {
-                *(float4*)kr = make_float4(v[0], v[1], v[2], v[3]);
-                *(float4*)(kr + 4) = make_float4(v[4], v[5], v[6], v[7]);
-            } else {
-                *(uint4*)kr = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                                         pack_bf16x2(v[6], v[7]));
-            }
-            if (ch == 0) {
-                rscale[row] = sc;
-                rvalid[row] = valid;
-            }
-        }
-        __syncthreads();
-        // ---- transpose into Vt (row index fastest so lanes write neighbouring rows)
-        for (int idx = threadIdx.x; idx < 32 * (C / 8); idx += nthr) {
-            const int row = idx & 31, d0 = (idx >> 5) * 8;
-            const ET* kr = Kt + row * KP + d0;
+                *(uint4*)kr = raw[u][0];
+                *(uint4*)(kr + 4) = raw[u][NV - 1];
+                const float* v = (const float*)&raw[u][0];
+                const float* v2 = (const float*)&raw[u][NV - 1];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) Vt[(d0 + j) * VP + row] = kr[j];
+                for (int j = 0; j < 4; ++j) {
+                    Vt[(d0 + j) * VP + row] = v[j];
+                    Vt[(d0 + 4 + j) * VP + row] = v2[j];
+                }
+            } else {
+                uint4 b;
+                if (KVF == 2 && entry && d0 < nf) {
+                    const uint32_t c0 = raw[u][0].x, c1 = raw[u][0].y;
+                    b = make_uint4(pack_bf16x2(e4m3_to_f32(c0 & 0xFF), e4m3_to_f32((c0 >> 8) & 0xFF)),
+                                   pack_bf16x2(e4m3_to_f32((c0 >> 16) & 0xFF), e4m3_to_f32(c0 >> 24)),
+                                   pack_bf16x2(e4m3_to_f32(c1 & 0xFF), e4m3_to_f32((c1 >> 8) & 0xFF)),
+                                   pack_bf16x2(e4m3_to_f32((c1 >> 16) & 0xFF), e4m3_to_f32(c1 >> 24)));
+                } else {
+                    b = raw[u][0];
+                }
+                *(uint4*)kr = b;
+                const uint32_t w4[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    Vt[(d0 + 2 * h) * VP + row] = (uint16_t)(w4[h] & 0xFFFF);
+                    Vt[(d0 + 2 * h + 1) * VP + row] = (uint16_t)(w4[h] >> 16);
+                }
+            }
+        }
+    };
+
+    uint4 raw[PF][NV];
+    if (tile0 < tile1) {
+        describe(tile0 * 32);
+        __syncthreads();
+        load_round(0, tile0, 0, raw);
+    }
+    for (int tile = tile0; tile < tile1; ++tile) {
+        const int drow0 = ((tile - tile0) * 32) % DESC;
+        const int slot0 = tile * 32;
+        store_round(0, tile, raw);
+        for (int r = 1; r < rounds; ++r) {
+            uint4 more[PF][NV];
+            load_round(r, tile, drow0, more);
+            store_round(r, tile, more);
         }
         __syncthreads();
+        // prefetch the next tile's first round while this one computes
+        const bool next_same_window = tile + 1 < tile1 && drow0 + 32 < DESC;
+        if (next_same_window) load_round(0, tile + 1, drow0 + 32, raw);
 
         // ---- S^T = K . Q^T for 32 rows x 16 heads (two 16-row tiles)
         // tile rt, MFMA row r' -> tile row 8*(r'/4) + 4*rt + r'%4
@@ -250,10 +294,12 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r0 = 8 * g + i, r1 = 8 * g + 4 + i;
-            rsc[i] = rscale[r0];
-            rsc[4 + i] = rscale[r1];
-            sv[i] = rvalid[r0] ? (KVF == 2 ? rsc[i] * sn0[i] + sr0[i] : sr0[i]) : -INFINITY;
-            sv[4 + i] = rvalid[r1] ? (KVF == 2 ? rsc[4 + i] * sn1[i] + sr1[i] : sr1[i]) : -INFINITY;
+            const bool v0 = rptr[drow0 + r0] != nullptr, v1 = rptr[drow0 + r1] != nullptr;
+            const bool e0 = slot0 + r0 < K0, e1 = slot0 + r1 < K0;
+            rsc[i] = rscl[drow0 + r0];
+            rsc[4 + i] = rscl[drow0 + r1];
+            sv[i] = v0 ? (KVF == 2 && e0 ? rsc[i] * sn0[i] + sr0[i] : sn0[i] + sr0[i]) : -INFINITY;
+            sv[4 + i] = v1 ? (KVF == 2 && e1 ? rsc[4 + i] * sn1[i] + sr1[i] : sn1[i] + sr1[i]) : -INFINITY;
         }
         float mx = sv[0];
 #pragma unroll
@@ -284,27 +330,35 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
                 O[dt] = MMA::step(*(const uint4*)(vr + 4), pb, O[dt]);
             }
         } else {
+            // FP8 value channels of entry rows carry the block scale; window rows do not
+            float ps8[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ps8[i] = (KVF == 2 && slot0 + 8 * g + i < K0) ? p[i] * rsc[i] : p[i];
             const uint4 pr = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                                         pack_bf16x2(p[6], p[7]));
-            uint4 pn = pr;
-            if (KVF == 2)
-                pn = make_uint4(pack_bf16x2(p[0] * rsc[0], p[1] * rsc[1]), pack_bf16x2(p[2] * rsc[2], p[3] * rsc[3]),
-                                pack_bf16x2(p[4] * rsc[4], p[5] * rsc[5]), pack_bf16x2(p[6] * rsc[6], p[7] * rsc[7]));
+            const uint4 pn = make_uint4(pack_bf16x2(ps8[0], ps8[1]), pack_bf16x2(ps8[2], ps8[3]),
+                                        pack_bf16x2(ps8[4], ps8[5]), pack_bf16x2(ps8[6], ps8[7]));
 #pragma unroll
             for (int dt = 0; dt < Cfg::DT; ++dt) {
                 const ET* vr = Vt + (dt * 16 + li) * VP + 8 * g;
                 O[dt] = MMA::step(*(const uint4*)vr, (KVF == 2 && dt * 16 < nf) ? pn : pr, O[dt]);
             }
         }
+        __syncthreads();                                       // Kt, Vt and rptr are rewritten next
+        if (tile + 1 < tile1 && !next_same_window) {
+            describe((tile + 1) * 32);
+            __syncthreads();
+            load_round(0, tile + 1, 0, raw);
+        }
     }
 
     // lane holds O^T[16*dt + 4g + i][head li]
     if (a.n_splits == 1) {
-        const float zs = (head < a.nh ? a.sinks[head] : 0.f) * LOG2E;
+        const float zs = (hv ? a.sinks[head] : 0.f) * LOG2E;
         const float M = fmaxf(m_run, zs);
         const float sc = exp2f(m_run - M);
         const float inv = sc / (l_run * sc + exp2f(zs - M));
-        if (head < a.nh) {
+        if (hv) {
 #pragma unroll
             for (int dt = 0; dt < Cfg::DT; ++dt) {
                 const int d = dt * 16 + 4 * g;
@@ -326,14 +380,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
                 }
             }
         }
-    } else if (head < a.nh) {
+    } else if (hv) {
         float* pp = a.ws + (((size_t)gq * a.nh + head) * a.n_splits + split) * (C + 2);
         if (g == 0) { pp[0] = m_run; pp[1] = l_run; }
 #pragma unroll
         for (int dt = 0; dt < Cfg::DT; ++dt) {
             const int d = dt * 16 + 4 * g;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pp[2 + d + i] = O[dt][i];
+            *(float4*)(pp + 2 + d) = make_float4(O[dt][0], O[dt][1], O[dt][2], O[dt][3]);
         }
     }
 }

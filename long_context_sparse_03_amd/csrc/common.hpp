@@ -122,6 +122,19 @@ struct MmaF32 {
 
 CSA_DEV f32x4_t zero4() { f32x4_t z = {0.f, 0.f, 0.f, 0.f}; return z; }
 
+// 16-byte load as one dwordx4 (the address must be 16-byte aligned).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+CSA_DEV uint4 ld16(const void* p)
+{
+    u32x4_t v = *(const u32x4_t*)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+CSA_DEV uint4 sel16(bool keep, uint4 v)
+{
+    return make_uint4(keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u);
+}
+
 // ---------------------------------------------------------------------------
 // batch bookkeeping
 // ---------------------------------------------------------------------------

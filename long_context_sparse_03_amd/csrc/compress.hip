@@ -50,13 +50,12 @@ __global__ __launch_bounds__(256) void proj_large(const T* __restrict__ X, const
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
-    const uint4 z = make_uint4(0, 0, 0, 0);
     for (int k0 = 0; k0 < K; k0 += MMA::K) {
         uint4 a[4], b[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            a[t] = av[t] ? *(const uint4*)(ap[t] + k0) : z;
-            b[t] = bv[t] ? *(const uint4*)(bp[t] + k0) : z;
+            a[t] = ld16(ap[t] + k0);        // rows past M / N are clamped, their outputs dropped
+            b[t] = ld16(bp[t] + k0);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -93,22 +92,25 @@ __global__ __launch_bounds__(256) void proj_small(const T* __restrict__ X, const
     const T* ap = X + (size_t)(av ? m : 0) * K + kb + g * EPF;
     int nn = bv ? n : 0;
     const T* bp = (nn < n_main ? W + (size_t)nn * K : Wi + (size_t)(nn - n_main) * K) + kb + g * EPF;
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    f32x4_t acc0 = zero4(), acc1 = zero4();
+    f32x4_t acc[4] = {zero4(), zero4(), zero4(), zero4()};
     int k0 = 0;
-    for (; k0 + 2 * MMA::K <= kq; k0 += 2 * MMA::K) {
-        uint4 a0 = av ? *(const uint4*)(ap + k0) : z;
-        uint4 b0 = bv ? *(const uint4*)(bp + k0) : z;
-        uint4 a1 = av ? *(const uint4*)(ap + k0 + MMA::K) : z;
-        uint4 b1 = bv ? *(const uint4*)(bp + k0 + MMA::K) : z;
-        acc0 = MMA::step(a0, b0, acc0);
-        acc1 = MMA::step(a1, b1, acc1);
+    for (; k0 + 8 * MMA::K <= kq; k0 += 8 * MMA::K) {      // eight fragment pairs in flight
+        uint4 a8[8], b8[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            a8[u] = ld16(ap + k0 + u * MMA::K);   // clamped rows: only dropped outputs see them
+            b8[u] = ld16(bp + k0 + u * MMA::K);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[u & 3] = MMA::step(a8[u], b8[u], acc[u & 3]);
     }
     for (; k0 < kq; k0 += MMA::K) {
-        uint4 a0 = av ? *(const uint4*)(ap + k0) : z;
-        uint4 b0 = bv ? *(const uint4*)(bp + k0) : z;
-        acc0 = MMA::step(a0, b0, acc0);
+        uint4 a0 = ld16(ap + k0);
+        uint4 b0 = ld16(bp + k0);
+        acc[0] = MMA::step(a0, b0, acc[0]);
     }
+    const f32x4_t acc0 = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    const f32x4_t acc1 = zero4();
 #pragma unroll
     for (int q = 0; q < 4; ++q) red[wave][lane][q] = acc0[q] + acc1[q];
     __syncthreads();

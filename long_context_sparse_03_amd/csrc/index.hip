@@ -84,24 +84,60 @@ CSA_DEV void mx_expand_frags(uint4 codes, uint32_t scale_code, uint4* out)
     }
 }
 
-// Decode-shaped launch: one workgroup per (query, 256 entries); each wave
-// scores 64 entries as four 16-key tiles.  HT = head tiles (<= 4),
-// S = fragments per lane group (key width / 4 / elements per fragment).
+// Decode-shaped launch: one workgroup per (query, EPW entries).  Each wave
+// scores 64 entries per iteration as four 16-key tiles and keeps the next
+// iteration's key loads in flight while it computes the current one.
+// HT = head tiles (<= 4), S = fragments per lane group.
+constexpr int IDX_EPW = 1024;                 // entries per workgroup
+constexpr int IDX_ITERS = IDX_EPW / 256;      // iterations of 256 entries (64 per wave)
+
+template <int IDXF, int S>
+CSA_DEV void load_keys(const IndexArgs& a, const int* bt, int blk0, int e0, int V, int g, int li, uint4 (&B)[4][S],
+                       uint32_t (&SC)[4])
+{
+    // Loads are unconditional (entries past V are clamped to V-1): an MFMA
+    // column only feeds the score of its own entry, and scores of entries
+    // >= V are not stored.  Branch-free loads stay in flight together.
+    const int cI = a.cI, quarter = cI / 4;
+    const size_t kbytes = IDXF == 0 ? (size_t)cI * 4 : (IDXF == 1 ? (size_t)cI * 2 : (size_t)cI / 2);
+#pragma unroll
+    for (int tile = 0; tile < 4; ++tile) {
+        const int e = min(e0 + 16 * tile + li, V - 1);
+        const int phys = bt[e / a.epb - blk0];
+        const int slot = e % a.epb;
+        const char* kb = (const char*)a.keys + (size_t)phys * a.key_block_bytes;
+        if constexpr (IDXF == 2) {
+            B[tile][0] = ld16(kb + (size_t)slot * (cI / 2) + (size_t)g * 16);
+            SC[tile] = (uint8_t)kb[(size_t)a.epb * (cI / 2) + (size_t)slot * (cI / 32) + g];
+        } else {
+            const char* kp = kb + (size_t)slot * kbytes + (size_t)g * quarter * (IDXF == 0 ? 4 : 2);
+#pragma unroll
+            for (int s = 0; s < S; ++s) B[tile][s] = ld16(kp + 16 * s);
+        }
+    }
+}
+
 template <int IDXF, int HT, int S>
 __global__ __launch_bounds__(256) void index_decode_kernel(IndexArgs a)
 {
     using MMA = typename std::conditional<IDXF == 0, MmaF32, MmaBF16>::type;
     constexpr bool MB = IDXF != 0;
+    __shared__ int bt[IDX_EPW / 1 + 1];          // physical blocks of this workgroup's entries
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
     const int gq = blockIdx.y;
     const int req = find_request(a.cu_new, a.n_req, gq);
     const int t = a.start_pos[req] + (gq - a.cu_new[req]);
     const int V = (t + 1) / a.m;
     if (blockIdx.x == 0 && threadIdx.x == 0) a.n_valid[gq] = V;
-    const int e_base = blockIdx.x * 256 + wave * 64;
-    if (e_base >= V) return;
+    const int wg0 = blockIdx.x * IDX_EPW;
+    if (wg0 >= V) return;
     const int cI = a.cI, nh = a.nh, quarter = cI / 4;
     const int esz = IDXF == 0 ? 4 : (a.q_bf16 ? 2 : 4);
+
+    // block-table slice of the workgroup's entries
+    const int blk0 = wg0 / a.epb;
+    const int nblk = (min(V, wg0 + IDX_EPW) - 1) / a.epb - blk0 + 1;
+    for (int j = threadIdx.x; j < nblk; j += blockDim.x) bt[j] = a.block_table[(size_t)req * a.max_blocks + blk0 + j];
 
     // query fragments (A operand): head 16*ht + li, elements [g*quarter, (g+1)*quarter)
     uint4 A[HT][S];
@@ -129,46 +165,44 @@ __global__ __launch_bounds__(256) void index_decode_kernel(IndexArgs a)
             wv[ht][i] = hh < nh ? a.w[(size_t)gq * nh + hh] : 0.f;
         }
     }
+    __syncthreads();
 
-    const size_t kbytes = IDXF == 0 ? (size_t)cI * 4 : (IDXF == 1 ? (size_t)cI * 2 : (size_t)cI / 2);
-#pragma unroll 1
-    for (int tile = 0; tile < 4; ++tile) {
-        if (e_base + 16 * tile >= V) break;     // wave-uniform: the whole tile is past V
-        const int e = e_base + 16 * tile + li;
-        const bool ev = e < V;
-        uint4 B[S];
-        if (ev) {
-            const int phys = a.block_table[(size_t)req * a.max_blocks + e / a.epb];
-            const int slot = e % a.epb;
-            const char* kb = (const char*)a.keys + (size_t)phys * a.key_block_bytes;
+    uint4 B[2][4][S];
+    uint32_t SC[2][4];
+    load_keys<IDXF, S>(a, bt, blk0, wg0 + wave * 64, V, g, li, B[0], SC[0]);
+#pragma unroll
+    for (int it = 0; it < IDX_ITERS; ++it) {
+        const int cur = it & 1;
+        const int e_base = wg0 + it * 256 + wave * 64;
+        if (it + 1 < IDX_ITERS) load_keys<IDXF, S>(a, bt, blk0, e_base + 256, V, g, li, B[cur ^ 1], SC[cur ^ 1]);
+        if (e_base >= V) break;                  // wave-uniform
+#pragma unroll
+        for (int tile = 0; tile < 4; ++tile) {
+            if (e_base + 16 * tile >= V) break;  // wave-uniform: the whole tile is past V
+            const int e = e_base + 16 * tile + li;
+            uint4 Bt[S];
             if constexpr (IDXF == 2) {
-                uint4 codes = *(const uint4*)(kb + (size_t)slot * (cI / 2) + (size_t)g * 16);
-                uint32_t sc = kb[(size_t)a.epb * (cI / 2) + (size_t)slot * (cI / 32) + g];
-                mx_expand_frags(codes, sc & 0xFFu, B);
+                mx_expand_frags(B[cur][tile][0], SC[cur][tile], Bt);
             } else {
-                const uint4* kp = (const uint4*)(kb + (size_t)slot * kbytes + (size_t)g * quarter * (IDXF == 0 ? 4 : 2));
 #pragma unroll
-                for (int s = 0; s < S; ++s) B[s] = kp[s];
+                for (int s = 0; s < S; ++s) Bt[s] = B[cur][tile][s];
             }
-        } else {
+            float v = 0.f;
 #pragma unroll
-            for (int s = 0; s < S; ++s) B[s] = make_uint4(0, 0, 0, 0);
-        }
-        float v = 0.f;
+            for (int ht = 0; ht < HT; ++ht) {
+                f32x4_t acc = zero4();
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-            f32x4_t acc = zero4();
+                for (int s = 0; s < S; ++s) acc = MMA::step(A[ht][s], Bt[s], acc);
 #pragma unroll
-            for (int s = 0; s < S; ++s) acc = MMA::step(A[ht][s], B[s], acc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v += wv[ht][i] * fmaxf(acc[i], 0.f);
-        }
-        v += __shfl_xor(v, 16, 64);
-        v += __shfl_xor(v, 32, 64);
-        if (g == 0 && ev) {
-            if (v == 0.0f) v = 0.0f;                // -0 is stored as +0
-            if (a.score_bf16) ((uint16_t*)a.scores)[(size_t)gq * a.ld + e] = f32_to_bf16(v);
-            else ((float*)a.scores)[(size_t)gq * a.ld + e] = v;
+                for (int i = 0; i < 4; ++i) v += wv[ht][i] * fmaxf(acc[i], 0.f);
+            }
+            v += __shfl_xor(v, 16, 64);
+            v += __shfl_xor(v, 32, 64);
+            if (g == 0 && e < V) {
+                if (v == 0.0f) v = 0.0f;                // -0 is stored as +0
+                if (a.score_bf16) ((uint16_t*)a.scores)[(size_t)gq * a.ld + e] = f32_to_bf16(v);
+                else ((float*)a.scores)[(size_t)gq * a.ld + e] = v;
+            }
         }
     }
 }
@@ -209,7 +243,7 @@ hipError_t launch_index(hipStream_t st, const IndexArgs& a, int max_visible, int
 {
     (void)max_new;
     if (a.n_tokens <= 0) return hipSuccess;
-    dim3 grid((max_visible + 255) / 256 > 0 ? (max_visible + 255) / 256 : 1, a.n_tokens);
+    dim3 grid(max_visible > 0 ? (max_visible + IDX_EPW - 1) / IDX_EPW : 1, a.n_tokens);
     if (a.idx_fmt == 0) launch_fmt<0>(st, a, grid);
     else if (a.idx_fmt == 1) launch_fmt<1>(st, a, grid);
     else launch_fmt<2>(st, a, grid);

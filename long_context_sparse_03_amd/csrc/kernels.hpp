@@ -77,7 +77,8 @@ hipError_t launch_index(hipStream_t st, const IndexArgs& a, int max_visible, int
 
 hipError_t launch_topk(hipStream_t st, int score_bf16, int n_rows, const void* scores, int ld,
                        const int32_t* n_valid, int k, int32_t* out, void* ws, int max_cols);
-size_t topk_workspace(int n_rows, int max_cols, int k);
+size_t topk_workspace(int n_rows, int max_cols, int k, bool bf16);
+bool topk_supported(int max_cols, int k, bool bf16);
 
 struct AttnArgs {
     const void* q;             // [n_tokens x nh x c] f32 or bf16

@@ -13,24 +13,26 @@
 // top-k (in index order) as candidates, and a second pass selects from the
 // concatenated candidates.  Every element of the global top-k is in its
 // chunk's top-k under the same total order, so the result is the same.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace csa {
 
 constexpr int TOPK_THREADS = 1024;
-constexpr int TOPK_CHUNK = 16384;        // elements per first-stage workgroup when rows are long
+constexpr int CAP16 = 40960;             // bf16 keys per workgroup (16-bit keys in LDS)
+constexpr int CAP32 = 20480;             // fp32 keys per workgroup
 
-CSA_DEV uint32_t score_key(const void* base, size_t i, bool bf16)
+// Order-preserving key of a score: sign-magnitude flip; -0 and +0 share the key.
+CSA_DEV uint32_t key16(uint32_t b)
 {
-    uint32_t u;
-    if (bf16) {
-        uint32_t b = ((const uint16_t*)base)[i];
-        if ((b & 0x7FFFu) == 0u) b = 0u;
-        b = (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
-        return b << 16;
-    }
-    u = ((const uint32_t*)base)[i];
+    if ((b & 0x7FFFu) == 0u) b = 0u;
+    return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+}
+
+CSA_DEV uint32_t key32(uint32_t u)
+{
     if ((u & 0x7FFFFFFFu) == 0u) u = 0u;
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
@@ -56,142 +58,209 @@ CSA_DEV int block_exscan(int v, int* sh, int* total)
     return off + inc - v;
 }
 
-// Select the top kk (kk <= n) of keys key(i), i < n, by (key desc, i asc) and
-// write the selected positions, ascending, through emit(rank, i).
-template <class KeyF, class EmitF>
-CSA_DEV void select_top(int n, int kk, int min_shift, KeyF key, EmitF emit)
+// Select the top kk of the n keys in LDS (order: key descending, position
+// ascending) and emit the selected positions in ascending order through
+// emit(rank, position).  BITS = key width (16 or 32).  The threshold is
+// found MSB first with an 11-bit first digit (sign, exponent and the top
+// mantissa bits, so that clustered scores spread over many bins) and
+// histograms kept in four interleaved copies to cut atomic contention.
+template <int BITS, class KT, class EmitF>
+CSA_DEV void select_top(const KT* keys, int n, int kk, EmitF emit)
 {
-    __shared__ uint32_t hist[256];
+    constexpr int COPIES = 4;
+    __shared__ uint32_t hist[2048 * COPIES];
     __shared__ uint32_t sh_prefix, sh_rem;
     __shared__ int scan_sh[32];
     const int tid = threadIdx.x, nt = blockDim.x;
-    const int per = (n + nt - 1) / nt;
-    const int i0 = tid * per, i1 = min(n, i0 + per);
     uint32_t prefix = 0, mask = 0, rem = (uint32_t)kk;
     const bool all = kk >= n;
     if (!all) {
-        for (int shift = 24; shift >= min_shift; shift -= 8) {
-            for (int b = tid; b < 256; b += nt) hist[b] = 0;
+        int hi = BITS;                                          // digits: 11, then 5 (16-bit) or 11, 10 (32-bit)
+        while (hi > 0) {
+            const int width = hi == BITS ? 11 : (hi > 11 ? 11 : hi);
+            const int shift = hi - width;
+            const int nb = 1 << width;
+            for (int b = tid; b < nb * COPIES; b += nt) hist[b] = 0;
             __syncthreads();
-            for (int i = i0; i < i1; ++i) {
-                uint32_t k = key(i);
-                if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+            for (int i = tid; i < n; i += nt) {                 // strided: conflict-free LDS reads
+                const uint32_t k = keys[i];
+                if ((k & mask) == prefix) atomicAdd(&hist[((k >> shift) & (uint32_t)(nb - 1)) * COPIES + (tid & 3)], 1u);
             }
             __syncthreads();
-            if (tid == 0) {
-                uint32_t cum = 0;
-                for (int b = 255; b >= 0; --b) {
-                    uint32_t h = hist[b];
-                    if (cum + h >= rem) {
-                        sh_prefix = prefix | ((uint32_t)b << shift);
-                        sh_rem = rem - cum;
-                        break;
-                    }
-                    cum += h;
-                }
+            // two bins per thread, from the top: bA = nb-1-2*tid, bB = bA-1
+            const int bA = nb - 1 - 2 * tid, bB = bA - 1;
+            uint32_t cA = 0, cB = 0;
+            if (bA >= 0)
+                for (int c = 0; c < COPIES; ++c) cA += hist[bA * COPIES + c];
+            if (bB >= 0)
+                for (int c = 0; c < COPIES; ++c) cB += hist[bB * COPIES + c];
+            int tot;
+            const uint32_t above = (uint32_t)block_exscan((int)(cA + cB), scan_sh, &tot);
+            if (bA >= 0 && above < rem && rem <= above + cA) {
+                sh_prefix = prefix | ((uint32_t)bA << shift);
+                sh_rem = rem - above;
+            } else if (bB >= 0 && above + cA < rem && rem <= above + cA + cB) {
+                sh_prefix = prefix | ((uint32_t)bB << shift);
+                sh_rem = rem - above - cA;
             }
             __syncthreads();
             prefix = sh_prefix;
             rem = sh_rem;
-            mask |= 255u << shift;
-            __syncthreads();
+            mask |= (uint32_t)(nb - 1) << shift;
+            hi = shift;
         }
     }
-    // prefix = threshold key T (keys above T are all taken), rem = how many
+    // prefix = threshold key T (keys above T are all taken); rem = how many
     // keys equal to T to take, lowest positions first.
+    const int per = (n + nt - 1) / nt;
+    const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
     int eq = 0;
     if (!all)
-        for (int i = i0; i < i1; ++i) eq += key(i) == prefix;
+        for (int i = i0; i < i1; ++i) eq += (uint32_t)keys[i] == prefix;
     int tot;
-    int eq_before = block_exscan(eq, scan_sh, &tot);
+    const int eq_before = block_exscan(eq, scan_sh, &tot);
     int sel = 0;
     {
         int er = eq_before;
         for (int i = i0; i < i1; ++i) {
-            uint32_t k = key(i);
-            bool s = all || k > prefix || (k == prefix && (uint32_t)(er++) < rem);
-            sel += s;
+            uint32_t k = keys[i];
+            sel += all || k > prefix || (k == prefix && (uint32_t)(er++) < rem);
         }
     }
-    int out_before = block_exscan(sel, scan_sh, &tot);
+    const int out_before = block_exscan(sel, scan_sh, &tot);
     {
         int er = eq_before, o = out_before;
         for (int i = i0; i < i1; ++i) {
-            uint32_t k = all ? 0u : key(i);
-            bool s = all || k > prefix || (k == prefix && (uint32_t)(er++) < rem);
-            if (s) emit(o++, i);
+            uint32_t k = keys[i];
+            if (all || k > prefix || (k == prefix && (uint32_t)(er++) < rem)) emit(o++, i);
         }
     }
 }
 
 // Stage 1 (or the only stage): chunk blockIdx.x of row blockIdx.y.
-__global__ __launch_bounds__(TOPK_THREADS) void topk_chunk_kernel(const void* scores, int ld, int bf16,
+template <bool BF16>
+__global__ __launch_bounds__(TOPK_THREADS) void topk_chunk_kernel(const void* scores, int ld,
                                                                   const int32_t* n_valid, int k, int chunk,
                                                                   int n_chunks, int32_t* out, uint32_t* cand_key,
                                                                   int32_t* cand_idx)
 {
+    using KT = typename std::conditional<BF16, uint16_t, uint32_t>::type;
+    __shared__ KT keys[BF16 ? CAP16 : CAP32];
     const int row = blockIdx.y, ch = blockIdx.x;
     const int V = n_valid[row];
     const int start = ch * chunk;
     const int n = max(0, min(V, start + chunk) - start);
     const int kk = min(k, n);
-    const char* base = (const char*)scores + ((size_t)row * ld + start) * (bf16 ? 2 : 4);
-    const bool isbf = bf16 != 0;
-    auto key = [&](int i) { return score_key(base, (size_t)i, isbf); };
-    if (n_chunks == 1) {
-        int32_t* o = out + (size_t)row * k;
-        select_top(n, kk, isbf ? 16 : 0, key, [&](int r, int i) { o[r] = start + i; });
-        for (int r = kk + threadIdx.x; r < k; r += blockDim.x) o[r] = -1;
-    } else {
-        uint32_t* ck = cand_key + ((size_t)row * n_chunks + ch) * k;
-        int32_t* ci = cand_idx + ((size_t)row * n_chunks + ch) * k;
-        select_top(n, kk, isbf ? 16 : 0, key, [&](int r, int i) { ck[r] = key(i); ci[r] = start + i; });
-        for (int r = kk + threadIdx.x; r < k; r += blockDim.x) { ck[r] = 0u; ci[r] = -1; }
+    // stage the chunk's keys in LDS; 16-byte loads, four in flight per thread
+    const size_t off = (size_t)row * ld + start;
+    constexpr int EPL = BF16 ? 8 : 4;                       // scores per 16-byte load
+    const int head = (int)min((size_t)n, (EPL - off % EPL) % EPL);   // scalar prologue up to alignment
+    const char* base = (const char*)scores + off * (BF16 ? 2 : 4);
+    for (int i = threadIdx.x; i < head; i += blockDim.x)
+        keys[i] = (KT)(BF16 ? key16(((const uint16_t*)base)[i]) : key32(((const uint32_t*)base)[i]));
+    const int nvec = (n - head) / EPL;
+    const char* vbase = base + (size_t)head * (BF16 ? 2 : 4);
+    for (int v0 = threadIdx.x; v0 < nvec; v0 += 4 * blockDim.x) {
+        uint4 q[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int v = min(v0 + u * (int)blockDim.x, nvec - 1);
+            q[u] = ld16(vbase + (size_t)v * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int v = v0 + u * (int)blockDim.x;
+            if (v >= nvec) break;
+            const uint32_t w4[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+            KT* dst = keys + head + v * EPL;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                if (BF16) {
+                    dst[2 * h] = (KT)key16(w4[h] & 0xFFFFu);
+                    dst[2 * h + 1] = (KT)key16(w4[h] >> 16);
+                } else {
+                    dst[h] = (KT)key32(w4[h]);
+                }
+            }
+        }
+    }
+    for (int i = head + nvec * EPL + threadIdx.x; i < n; i += blockDim.x)
+        keys[i] = (KT)(BF16 ? key16(((const uint16_t*)base)[i]) : key32(((const uint32_t*)base)[i]));
+    __syncthreads();
+    // one stage: final indices; first of two: candidates (key, index) per chunk
+    const bool single = n_chunks == 1;
+    int32_t* o = single ? out + (size_t)row * k : cand_idx + ((size_t)row * n_chunks + ch) * k;
+    uint32_t* ck = single ? nullptr : cand_key + ((size_t)row * n_chunks + ch) * k;
+    select_top<BF16 ? 16 : 32>(keys, n, kk, [&](int r, int i) {
+        o[r] = start + i;
+        if (!single) ck[r] = keys[i];
+    });
+    for (int r = kk + threadIdx.x; r < k; r += blockDim.x) {
+        o[r] = -1;
+        if (!single) ck[r] = 0u;
     }
 }
 
 // Stage 2: select from the n_chunks*k candidates of row blockIdx.x.  Invalid
-// candidates carry key 0, below every real key.
+// candidates carry key 0, below every real key; candidates are in ascending
+// index order, so position order is index order.
+template <bool BF16>
 __global__ __launch_bounds__(TOPK_THREADS) void topk_merge_kernel(const int32_t* n_valid, int k, int n_chunks,
                                                                   const uint32_t* cand_key, const int32_t* cand_idx,
-                                                                  int bf16, int32_t* out)
+                                                                  int32_t* out)
 {
+    using KT = typename std::conditional<BF16, uint16_t, uint32_t>::type;
+    __shared__ KT keys[BF16 ? CAP16 : CAP32];
     const int row = blockIdx.x;
     const int V = n_valid[row];
     const int kk = min(k, V);
     const int n = n_chunks * k;
     const uint32_t* ck = cand_key + (size_t)row * n;
     const int32_t* ci = cand_idx + (size_t)row * n;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) keys[i] = (KT)ck[i];
+    __syncthreads();
     int32_t* o = out + (size_t)row * k;
-    select_top(n, kk, bf16 ? 16 : 0, [&](int i) { return ck[i]; }, [&](int r, int i) { o[r] = ci[i]; });
+    select_top<BF16 ? 16 : 32>(keys, n, kk, [&](int r, int i) { o[r] = ci[i]; });
     for (int r = kk + threadIdx.x; r < k; r += blockDim.x) o[r] = -1;
 }
 
-static int chunk_for(int max_cols)
+static int chunk_for(int max_cols, bool bf16)
 {
-    return max_cols <= 2 * TOPK_CHUNK ? (max_cols > 0 ? max_cols : 1) : TOPK_CHUNK;
+    const int cap = bf16 ? CAP16 : CAP32;
+    return max_cols <= cap ? (max_cols > 0 ? max_cols : 1) : cap;
 }
 
-size_t topk_workspace(int n_rows, int max_cols, int k)
+size_t topk_workspace(int n_rows, int max_cols, int k, bool bf16)
 {
-    int chunk = chunk_for(max_cols);
-    int n_chunks = (max_cols + chunk - 1) / chunk;
+    const int chunk = chunk_for(max_cols, bf16);
+    const int n_chunks = (max_cols + chunk - 1) / chunk;
     if (n_chunks <= 1) return 0;
     return (size_t)n_rows * n_chunks * k * 8;
+}
+
+bool topk_supported(int max_cols, int k, bool bf16)
+{
+    const int chunk = chunk_for(max_cols, bf16);
+    const int n_chunks = (max_cols + chunk - 1) / chunk;
+    return n_chunks <= 1 || (long)n_chunks * k <= (bf16 ? CAP16 : CAP32);
 }
 
 hipError_t launch_topk(hipStream_t st, int score_bf16, int n_rows, const void* scores, int ld,
                        const int32_t* n_valid, int k, int32_t* out, void* ws, int max_cols)
 {
     if (n_rows <= 0) return hipSuccess;
-    const int chunk = chunk_for(max_cols);
+    const bool bf = score_bf16 != 0;
+    const int chunk = chunk_for(max_cols, bf);
     const int n_chunks = max(1, (max_cols + chunk - 1) / chunk);
     uint32_t* ck = (uint32_t*)ws;
     int32_t* ci = n_chunks > 1 ? (int32_t*)((char*)ws + (size_t)n_rows * n_chunks * k * 4) : nullptr;
-    topk_chunk_kernel<<<dim3(n_chunks, n_rows), TOPK_THREADS, 0, st>>>(scores, ld, score_bf16, n_valid, k, chunk,
-                                                                       n_chunks, out, ck, ci);
-    if (n_chunks > 1)
-        topk_merge_kernel<<<n_rows, TOPK_THREADS, 0, st>>>(n_valid, k, n_chunks, ck, ci, score_bf16, out);
+    dim3 g1(n_chunks, n_rows);
+    if (bf) topk_chunk_kernel<true><<<g1, TOPK_THREADS, 0, st>>>(scores, ld, n_valid, k, chunk, n_chunks, out, ck, ci);
+    else topk_chunk_kernel<false><<<g1, TOPK_THREADS, 0, st>>>(scores, ld, n_valid, k, chunk, n_chunks, out, ck, ci);
+    if (n_chunks > 1) {
+        if (bf) topk_merge_kernel<true><<<n_rows, TOPK_THREADS, 0, st>>>(n_valid, k, n_chunks, ck, ci, out);
+        else topk_merge_kernel<false><<<n_rows, TOPK_THREADS, 0, st>>>(n_valid, k, n_chunks, ck, ci, out);
+    }
     return hipGetLastError();
 }
 

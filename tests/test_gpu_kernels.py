@@ -100,7 +100,7 @@ def test_window_ring_rows():
     desc = presets.csa_flash_decode(win_cap=200)
     _flush("window ring")
     g = synth.rng(101)
-    bt = synth.block_table(g, 2, 4)
+    bt = synth.block_table(g, 2, 10)
     st = LayerState(desc, 2, bt.size)
     sp = [0, 1000]
     rows = [synth.normal(g, (150, 512)), synth.normal(g, (73, 512))]
@@ -138,7 +138,7 @@ def test_topk_exact(fmt, V, k):
     dt = torch.bfloat16 if fmt == "bf16" else torch.float32
     scores = to_dev(sc, dt)
     out = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
-    desc = presets.csa_flash_decode()
+    desc = presets.csa_flash_decode() if fmt == "bf16" else presets.tiny_csa_fp32()
     nbytes = abi.workspace_size(desc, abi.OP_TOPK, T, ld, k)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
     abi.topk_select(abi.ACT_BF16 if fmt == "bf16" else abi.ACT_F32, T, scores, ld, i32(nv), k, out, ws)
