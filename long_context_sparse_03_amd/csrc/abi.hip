@@ -90,6 +90,7 @@ int check_layer(const csa_layer_desc* L)
     REQUIRE(L->out_fmt == CSA_FMT_F32 || L->out_fmt == CSA_FMT_BF16, CSA_EINVAL, "out_fmt=%d", L->out_fmt);
     REQUIRE(L->kv_fmt != CSA_KV_F32 || L->act_fmt == CSA_FMT_F32, CSA_EUNSUPPORTED,
             "fp32 KV needs fp32 activations (window ring)");
+    REQUIRE(L->kv_fmt != CSA_KV_F32 || L->c <= 256, CSA_EUNSUPPORTED, "fp32 KV supports c <= 256");
     REQUIRE(L->kv_fmt == CSA_KV_F32 || L->act_fmt == CSA_FMT_BF16, CSA_EUNSUPPORTED,
             "bf16 / fp8 KV needs bf16 activations (window ring)");
     REQUIRE(L->kv_fmt != CSA_KV_FP8 || (L->c - L->rope_dim) % 32 == 0, CSA_EUNSUPPORTED,
@@ -103,8 +104,8 @@ int check_layer(const csa_layer_desc* L)
         REQUIRE(L->idx_fmt != CSA_IDX_MXFP4 || L->c_idx == 128, CSA_EUNSUPPORTED, "MXFP4 keys need c_idx=128");
         REQUIRE(L->idx_fmt != CSA_IDX_F32 || L->act_fmt == CSA_FMT_F32, CSA_EUNSUPPORTED,
                 "fp32 indexer keys need fp32 queries");
-        REQUIRE(L->idx_fmt != CSA_IDX_BF16 || L->act_fmt == CSA_FMT_BF16, CSA_EUNSUPPORTED,
-                "bf16 indexer keys need bf16 queries");
+        REQUIRE(L->idx_fmt == CSA_IDX_F32 || L->act_fmt == CSA_FMT_BF16, CSA_EUNSUPPORTED,
+                "bf16 / MXFP4 indexer keys need bf16 queries");
         REQUIRE(L->score_fmt == CSA_FMT_F32 || L->score_fmt == CSA_FMT_BF16, CSA_EINVAL, "score_fmt=%d",
                 L->score_fmt);
         REQUIRE(L->top_k >= 1 && L->top_k <= 2048, CSA_EUNSUPPORTED, "top_k=%d (1..2048)", L->top_k);

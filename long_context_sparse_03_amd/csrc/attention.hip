@@ -57,6 +57,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
     __shared__ float rscl[DESC];                               // fp8 block scale (1 otherwise)
     __shared__ float rcs[256], rsn[256];
     __shared__ float qg[C];
+    __shared__ uint4 qf[4][Cfg::QSTEPS][64];                   // query fragments per wave, fragment order
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
     const int nthr = blockDim.x;
@@ -65,8 +66,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
     const int head = (blockIdx.y * NW + wave) * 16 + li;
     const bool hv = head < a.nh;
     const int split = blockIdx.z;
-    const int req = find_request(a.cu_new, a.n_req, gq);
-    const int t = a.start_pos[req] + (gq - a.cu_new[req]);
+    __shared__ int cu_sh[1025];
+    const int req = find_request_block(a.cu_new, a.n_req, gq, cu_sh);
+    const int t = a.start_pos[req] + (gq - cu_sh[req]);
     const int nf = C - a.r;                                   // non-rotary channels
     const bool dense = a.sel == nullptr;
     const int V = (t + 1) / a.m;
@@ -85,8 +87,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
     // query fragments (B operand of S^T): head li, channels s*K + g*EPF + j.
     // One load per fragment; the RMS of the head is summed over the four lane
     // groups that hold it.
-    uint4 QB[Cfg::QSTEPS];
     {
+        uint4 QB[Cfg::QSTEPS];
         const char* qp = (const char*)a.q + ((size_t)gq * a.nh + (hv ? head : 0)) * C * sizeof(ET);
         float ss = 0.f;
 #pragma unroll
@@ -142,6 +144,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
                 for (int h = 0; h < 4; ++h) w[h] = pack_bf16x2(x[2 * h] * a.scale_log2, x[2 * h + 1] * a.scale_log2);
                 QB[s] = make_uint4(w[0], w[1], w[2], w[3]);
             }
+            qf[wave][s][lane] = QB[s];
         }
     }
 
@@ -281,12 +284,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
             const int d0 = s * MMA::K + g * EPF;
             uint4 ka = *(const uint4*)(Kt + ra * KP + d0);
             uint4 kb = *(const uint4*)(Kt + rb * KP + d0);
+            const uint4 qb = qf[wave][s][lane];
             if (KVF == 2 && s * MMA::K < nf) {
-                sn0 = MMA::step(ka, QB[s], sn0);
-                sn1 = MMA::step(kb, QB[s], sn1);
+                sn0 = MMA::step(ka, qb, sn0);
+                sn1 = MMA::step(kb, qb, sn1);
             } else {
-                sr0 = MMA::step(ka, QB[s], sr0);
-                sr1 = MMA::step(kb, QB[s], sr1);
+                sr0 = MMA::step(ka, qb, sr0);
+                sr1 = MMA::step(kb, qb, sr1);
             }
         }
         // lane holds rows 8g + i (i < 4 from tile 0, 4..7 from tile 1) of head li
@@ -452,7 +456,9 @@ static void launch_c(hipStream_t st, const AttnArgs& a, dim3 grid, int threads)
     switch (a.c) {
     case 128: attn_kernel<KVF, 128><<<grid, threads, 0, st>>>(a); break;
     case 256: attn_kernel<KVF, 256><<<grid, threads, 0, st>>>(a); break;
-    case 512: attn_kernel<KVF, 512><<<grid, threads, 0, st>>>(a); break;
+    case 512:
+        if constexpr (KVF != 0) attn_kernel<KVF, 512><<<grid, threads, 0, st>>>(a);   // fp32 KV: c <= 256
+        break;
     default: break;
     }
 }

@@ -192,15 +192,31 @@ CSA_DEV float block_max(float v, float* red)
     return t;
 }
 
-// RoPE angle for pair j of r rotary channels at position pos, in double so
-// that positions up to millions keep full fp32 accuracy after reduction.
+// RoPE angle for pair j of r rotary channels at position pos: the angle is
+// formed and reduced to [-pi, pi] in double (positions reach millions), then
+// its sine and cosine are taken in fp32.
 CSA_DEV void rope_cs(double pos, int j, int r, float theta, float* cs, float* sn)
 {
-    double ang = pos * pow((double)theta, -2.0 * (double)j / (double)r);
-    double s, c;
-    sincos(ang, &s, &c);
-    *cs = (float)c;
-    *sn = (float)s;
+    const double inv_freq = exp2(-2.0 * (double)j / (double)r * log2((double)theta));
+    double ang = pos * inv_freq;
+    ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
+    sincosf((float)ang, sn, cs);
+}
+
+// Request of global token row g, found by all threads of the block together:
+// cu_new is staged in LDS (sh, >= n_req + 1 ints when n_req < 1024), then
+// searched there.  Every thread of the block must call it.
+CSA_DEV int find_request_block(const int32_t* cu_new, int n_req, int g, int* sh)
+{
+    if (n_req >= 1024) return find_request(cu_new, n_req, g);
+    for (int i = threadIdx.x; i <= n_req; i += blockDim.x) sh[i] = cu_new[i];
+    __syncthreads();
+    int lo = 0, hi = n_req - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (sh[mid] <= g) lo = mid; else hi = mid - 1;
+    }
+    return lo;
 }
 
 }  // namespace csa

@@ -120,53 +120,72 @@ CSA_DEV void load_keys(const IndexArgs& a, const int* bt, int blk0, int e0, int 
 template <int IDXF, int HT, int S>
 __global__ __launch_bounds__(256) void index_decode_kernel(IndexArgs a)
 {
+    // IDXF 0: fp32 keys and queries; 1: bf16 keys and queries; 2: MXFP4 keys,
+    // bf16 queries quantised to MXFP4 here.
     using MMA = typename std::conditional<IDXF == 0, MmaF32, MmaBF16>::type;
-    constexpr bool MB = IDXF != 0;
-    __shared__ int bt[IDX_EPW / 1 + 1];          // physical blocks of this workgroup's entries
+    __shared__ int bt[IDX_EPW + 1];             // physical blocks of this workgroup's entries
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
     const int gq = blockIdx.y;
-    const int req = find_request(a.cu_new, a.n_req, gq);
-    const int t = a.start_pos[req] + (gq - a.cu_new[req]);
+    __shared__ int cu_sh[1025];
+    const int req = find_request_block(a.cu_new, a.n_req, gq, cu_sh);
+    const int t = a.start_pos[req] + (gq - cu_sh[req]);
     const int V = (t + 1) / a.m;
     if (blockIdx.x == 0 && threadIdx.x == 0) a.n_valid[gq] = V;
     const int wg0 = blockIdx.x * IDX_EPW;
     if (wg0 >= V) return;
     const int cI = a.cI, nh = a.nh, quarter = cI / 4;
-    const int esz = IDXF == 0 ? 4 : (a.q_bf16 ? 2 : 4);
+    constexpr int QES = IDXF == 0 ? 4 : 2;      // query element size
 
-    // block-table slice of the workgroup's entries
+    // ---- prologue: block-table slice, query fragments and head weights,
+    //      all loads issued together (clamped indices, masked afterwards)
     const int blk0 = wg0 / a.epb;
     const int nblk = (min(V, wg0 + IDX_EPW) - 1) / a.epb - blk0 + 1;
-    for (int j = threadIdx.x; j < nblk; j += blockDim.x) bt[j] = a.block_table[(size_t)req * a.max_blocks + blk0 + j];
-
-    // query fragments (A operand): head 16*ht + li, elements [g*quarter, (g+1)*quarter)
+    int btv[(IDX_EPW + 255) / 256];
+#pragma unroll
+    for (int i = 0; i < (IDX_EPW + 255) / 256; ++i) {
+        const int j = min((int)threadIdx.x + 256 * i, nblk - 1);
+        btv[i] = a.block_table[(size_t)req * a.max_blocks + blk0 + j];
+    }
     uint4 A[HT][S];
     float wv[HT][4];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-        const int head = 16 * ht + li;
-        if (head < nh) {
-            const char* qp = (const char*)a.q + ((size_t)gq * nh + head) * cI * esz + (size_t)g * quarter * esz;
-            if constexpr (IDXF == 2) {
-                float v[32];
-                for (int j = 0; j < 32; ++j)
-                    v[j] = a.q_bf16 ? bf16_to_f32(((const uint16_t*)qp)[j]) : ((const float*)qp)[j];
-                mx_quant_frags(v, A[ht]);
-            } else {
-                load_frags<MB>(qp, a.q_bf16 != 0, S, quarter, A[ht]);
+        const int head = min(16 * ht + li, nh - 1);
+        const char* qp = (const char*)a.q + ((size_t)gq * nh + head) * cI * QES + (size_t)g * quarter * QES;
+#pragma unroll
+        for (int s = 0; s < S; ++s) A[ht][s] = ld16(qp + 16 * s);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wv[ht][i] = a.w[(size_t)gq * nh + min(16 * ht + 4 * g + i, nh - 1)];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < (IDX_EPW + 255) / 256; ++i)
+        if ((int)threadIdx.x + 256 * i < nblk) bt[threadIdx.x + 256 * i] = btv[i];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        const bool hv = 16 * ht + li < nh;
+        if constexpr (IDXF == 2) {
+            float v[32];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const uint32_t w4[4] = {A[ht][s].x, A[ht][s].y, A[ht][s].z, A[ht][s].w};
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    v[8 * s + 2 * h] = bf16_to_f32(w4[h] & 0xFFFF);
+                    v[8 * s + 2 * h + 1] = bf16_to_f32(w4[h] >> 16);
+                }
             }
-        } else {
-#pragma unroll
-            for (int s = 0; s < S; ++s) A[ht][s] = make_uint4(0, 0, 0, 0);
+            mx_quant_frags(v, A[ht]);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int hh = 16 * ht + 4 * g + i;
-            wv[ht][i] = hh < nh ? a.w[(size_t)gq * nh + hh] : 0.f;
-        }
+        for (int s = 0; s < S; ++s) A[ht][s] = sel16(hv, A[ht][s]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wv[ht][i] = 16 * ht + 4 * g + i < nh ? wv[ht][i] : 0.f;
     }
     __syncthreads();
 
+    // ---- main loop: 256 entries per iteration (64 per wave); the next
+    //      iteration's key loads are issued before this one's arithmetic
     uint4 B[2][4][S];
     uint32_t SC[2][4];
     load_keys<IDXF, S>(a, bt, blk0, wg0 + wave * 64, V, g, li, B[0], SC[0]);
@@ -174,7 +193,9 @@ __global__ __launch_bounds__(256) void index_decode_kernel(IndexArgs a)
     for (int it = 0; it < IDX_ITERS; ++it) {
         const int cur = it & 1;
         const int e_base = wg0 + it * 256 + wave * 64;
-        if (it + 1 < IDX_ITERS) load_keys<IDXF, S>(a, bt, blk0, e_base + 256, V, g, li, B[cur ^ 1], SC[cur ^ 1]);
+        if (it + 1 < IDX_ITERS && e_base + 256 < V)
+            load_keys<IDXF, S>(a, bt, blk0, e_base + 256, V, g, li, B[cur ^ 1], SC[cur ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);
         if (e_base >= V) break;                  // wave-uniform
 #pragma unroll
         for (int tile = 0; tile < 4; ++tile) {
