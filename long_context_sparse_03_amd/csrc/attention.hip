@@ -40,6 +40,11 @@ struct AttnCfg {
     static constexpr int VP = 32 + (F32 ? 4 : 8);                        // Vt row stride (elements)
     static constexpr int QSTEPS = C / MMA::K;                            // fragments of a query head
     static constexpr int DT = C / 16;                                    // 16-dim tiles of the output
+    // bf16 KV with fp32 accumulation: the normalised query and the softmax
+    // weights enter the bf16 MFMAs as hi + lo bf16 pairs (about 16
+    // significant bits) instead of one rounded bf16 value
+    static constexpr bool SPLIT = KVF == 1 && C <= 256;
+    static constexpr int QPARTS = SPLIT ? 2 : 1;
 };
 
 template <int KVF, int C>
@@ -57,7 +62,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
     __shared__ float rscl[DESC];                               // fp8 block scale (1 otherwise)
     __shared__ float rcs[256], rsn[256];
     __shared__ float qg[C];
-    __shared__ uint4 qf[4][Cfg::QSTEPS][64];                   // query fragments per wave, fragment order
+    __shared__ uint4 qf[4][Cfg::QPARTS][Cfg::QSTEPS][64];      // query fragments per wave, fragment order
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
     const int nthr = blockDim.x;
@@ -139,12 +144,17 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
                 QB[s] = make_uint4(__float_as_uint(x[0] * a.scale_log2), __float_as_uint(x[1] * a.scale_log2),
                                    __float_as_uint(x[2] * a.scale_log2), __float_as_uint(x[3] * a.scale_log2));
             } else {
-                uint32_t w[4];
+                uint32_t w[4], wl[4];
 #pragma unroll
-                for (int h = 0; h < 4; ++h) w[h] = pack_bf16x2(x[2 * h] * a.scale_log2, x[2 * h + 1] * a.scale_log2);
+                for (int h = 0; h < 4; ++h) {
+                    const float v0 = x[2 * h] * a.scale_log2, v1 = x[2 * h + 1] * a.scale_log2;
+                    w[h] = pack_bf16x2(v0, v1);
+                    wl[h] = pack_bf16x2(v0 - bf16_to_f32(w[h] & 0xFFFF), v1 - bf16_to_f32(w[h] >> 16));
+                }
                 QB[s] = make_uint4(w[0], w[1], w[2], w[3]);
+                if constexpr (Cfg::SPLIT) qf[wave][Cfg::QPARTS - 1][s][lane] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
             }
-            qf[wave][s][lane] = QB[s];
+            qf[wave][0][s][lane] = QB[s];
         }
     }
 
@@ -284,13 +294,16 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
             const int d0 = s * MMA::K + g * EPF;
             uint4 ka = *(const uint4*)(Kt + ra * KP + d0);
             uint4 kb = *(const uint4*)(Kt + rb * KP + d0);
-            const uint4 qb = qf[wave][s][lane];
-            if (KVF == 2 && s * MMA::K < nf) {
-                sn0 = MMA::step(ka, qb, sn0);
-                sn1 = MMA::step(kb, qb, sn1);
-            } else {
-                sr0 = MMA::step(ka, qb, sr0);
-                sr1 = MMA::step(kb, qb, sr1);
+#pragma unroll
+            for (int part = 0; part < Cfg::QPARTS; ++part) {
+                const uint4 qb = qf[wave][part][s][lane];
+                if (KVF == 2 && s * MMA::K < nf) {
+                    sn0 = MMA::step(ka, qb, sn0);
+                    sn1 = MMA::step(kb, qb, sn1);
+                } else {
+                    sr0 = MMA::step(ka, qb, sr0);
+                    sr1 = MMA::step(kb, qb, sr1);
+                }
             }
         }
         // lane holds rows 8g + i (i < 4 from tile 0, 4..7 from tile 1) of head li
@@ -342,10 +355,21 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
                                         pack_bf16x2(p[6], p[7]));
             const uint4 pn = make_uint4(pack_bf16x2(ps8[0], ps8[1]), pack_bf16x2(ps8[2], ps8[3]),
                                         pack_bf16x2(ps8[4], ps8[5]), pack_bf16x2(ps8[6], ps8[7]));
+            uint4 pl = pr;
+            if constexpr (Cfg::SPLIT) {
+                const uint32_t h4[4] = {pr.x, pr.y, pr.z, pr.w};
+                uint32_t l4[4];
+#pragma unroll
+                for (int h = 0; h < 4; ++h)
+                    l4[h] = pack_bf16x2(p[2 * h] - bf16_to_f32(h4[h] & 0xFFFF), p[2 * h + 1] - bf16_to_f32(h4[h] >> 16));
+                pl = make_uint4(l4[0], l4[1], l4[2], l4[3]);
+            }
 #pragma unroll
             for (int dt = 0; dt < Cfg::DT; ++dt) {
                 const ET* vr = Vt + (dt * 16 + li) * VP + 8 * g;
-                O[dt] = MMA::step(*(const uint4*)vr, (KVF == 2 && dt * 16 < nf) ? pn : pr, O[dt]);
+                const uint4 va = *(const uint4*)vr;
+                O[dt] = MMA::step(va, (KVF == 2 && dt * 16 < nf) ? pn : pr, O[dt]);
+                if constexpr (Cfg::SPLIT) O[dt] = MMA::step(va, pl, O[dt]);
             }
         }
         __syncthreads();                                       // Kt, Vt and rptr are rewritten next

@@ -78,8 +78,11 @@ def project(H, W):
     return np.asarray(H, np.float64) @ np.asarray(W, np.float64)
 
 
-def compress_layer(spec: Spec, H, W, Ba, Bb=None, gamma=None, W_I=None, BaI=None, BbI=None):
-    """Entries, indexer keys and window rows of one request's tokens 0..n-1.
+def compress_layer(spec: Spec, H, W, Ba, Bb=None, gamma=None, W_I=None, BaI=None, BbI=None, pos0: int = 0):
+    """Entries, indexer keys and window rows of one request's tokens 0..n-1
+    (the sequence may start at position pos0, a multiple of m: entry i is then
+    rotated at pos0 + m*i and window row j at pos0 + j; its first entry has no
+    previous block).
 
     CSA: W = [W^aKV | W^bKV | W^aZ | W^bZ] (d x 4c), W_I likewise (d x 4c_I).
     HCA: W = [W^KV | W^Z] (d x 2c).
@@ -97,8 +100,9 @@ def compress_layer(spec: Spec, H, W, Ba, Bb=None, gamma=None, W_I=None, BaI=None
         E = O.compress(Ca, None, Za, None, Ba, None, m, False)
     ne = E.shape[0]
     g = np.ones(c) if gamma is None else np.asarray(gamma, np.float64)
-    Ehat = O.rope(O.rmsnorm(E, g, spec.eps), m * np.arange(ne, dtype=np.float64), spec.r, spec.theta)
-    R = O.rope(O.rmsnorm(Ca, g, spec.eps), np.arange(n, dtype=np.float64), spec.r, spec.theta)
+    assert pos0 % m == 0
+    Ehat = O.rope(O.rmsnorm(E, g, spec.eps), pos0 + m * np.arange(ne, dtype=np.float64), spec.r, spec.theta)
+    R = O.rope(O.rmsnorm(Ca, g, spec.eps), pos0 + np.arange(n, dtype=np.float64), spec.r, spec.theta)
     K = None
     if spec.kind == "csa" and W_I is not None:
         cI = spec.c_I
