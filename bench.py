@@ -113,44 +113,23 @@ def cpu_baseline(wd, n_tok: int, seed: int = 11) -> dict:
                       f"{elapsed:.1f} s"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="csa_decode_128k", choices=["csa_decode_128k", "hybrid_decode_1m"])
-    ap.add_argument("--replicas", type=int, default=0, help="cache replicas rotated between steps (0: workload default)")
-    ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=384, help="decode tokens in the CPU-oracle sample (0: skip)")
-    ap.add_argument("--copy-probe", action="store_true", help="also run a 1 GiB device copy (HBM counter scale)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
-        raise SystemExit(2)
-
+def time_decode(name, steps, warmup, replicas=0, graph=True):
+    """Decode throughput of one workload; returns a dict of measurements."""
     import torch
     from long_context_sparse_03_amd.workloads import DecodeWorkload, torch_rows
 
-    wd = workload_def(args.workload)
-    reps = args.replicas or wd["replicas"]
-    total_steps = args.warmup + args.steps + 64
+    wd = workload_def(name)
+    reps = replicas or wd["replicas"]
+    total_steps = warmup + steps + 64
     t_build = time.time()
     wls = [DecodeWorkload(wd["descs"], wd["d"], wd["n_req"], wd["ctx"], max_steps=total_steps,
                           rows=torch_rows(1000 + i), seed=i) for i in range(reps)]
     torch.cuda.synchronize()
     build_s = time.time() - t_build
 
-    if args.copy_probe:
-        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
-
     stream = torch.cuda.Stream()
     # per-kernel timing of the index scan, live, with events on the launch stream
-    n_eager = min(args.steps, 30)
+    n_eager = min(steps, 30)
     idx_ms = []
     with torch.cuda.stream(stream):
         for i in range(4):
@@ -172,7 +151,7 @@ def main():
             idx_ms.extend(a.elapsed_time(b) for a, b in evs)
 
     graphs = []
-    if not args.no_graph:
+    if graph:
         for wl in wls:
             gph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gph, stream=stream):
@@ -187,19 +166,17 @@ def main():
             wls[i % reps].step()
 
     with torch.cuda.stream(stream):
-        for i in range(args.warmup):
+        for i in range(warmup):
             run(i)
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         t0.record(stream)
-        for i in range(args.steps):
+        for i in range(steps):
             run(i)
         t1.record(stream)
         torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
-    tok_s = wd["n_req"] / (ms * 1e-3)
-
+    ms = t0.elapsed_time(t1) / steps
     ab = algorithmic_bytes(wd)
     idx_avg_ms = float(np.mean(idx_ms)) if idx_ms else None
     roof = None
@@ -209,19 +186,143 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                 "launch_ms": round(idx_avg_ms, 5), "algorithmic_bytes_per_launch": ab["index_launch"]}
     step_gbs = ab["total"] / (ms * 1e-3) / 1e9
+    del wls, graphs
+    torch.cuda.empty_cache()
+    return {"workload": name, "tokens_per_s": round(wd["n_req"] / (ms * 1e-3), 1), "ms_per_step": round(ms, 5),
+            "requests": wd["n_req"], "ctx": wd["ctx"], "layers": len(wd["descs"]), "d": wd["d"],
+            "replicas": reps, "graph": graph, "step_hbm_gbs": round(step_gbs, 1),
+            "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4), "step_algorithmic_bytes": ab, "roofline": roof,
+            "setup_s": round(build_s, 1)}
+
+
+def time_prefill(steps, warmup):
+    """One 4096-token chunk on top of 1,048,576 cached tokens (Pro shape):
+    compress_kv, cache_append, index_scores, topk_select, sparse_mqa."""
+    import torch
+    from long_context_sparse_03_amd import abi, presets
+    from long_context_sparse_03_amd.workloads import DecodeWorkload, torch_rows
+    from long_context_sparse_03_amd.layer import make_batch
+
+    desc = presets.csa_pro(win_cap=4352)
+    T, ctx, d = 4096, 1 << 20, presets.D_PRO
+    wl = DecodeWorkload([desc], d, 1, ctx, max_steps=T + 256, rows=torch_rows(77), seed=5)
+    st, P = wl.layers[0]
+    dev = "cuda"
+    cu = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    sp = torch.tensor([ctx], dtype=torch.int32, device=dev)
+    bi = make_batch(cu, sp, wl.block_table, T, ctx + T, T)
+    H = torch.randn((T, d), device=dev).to(torch.bfloat16)
+    q = torch.randn((T, desc.n_heads, desc.c), device=dev).to(torch.bfloat16)
+    qI = torch.randn((T, desc.n_idx_heads, desc.c_idx), device=dev).to(torch.bfloat16)
+    w = torch.randn((T, desc.n_idx_heads), device=dev) / 8.0
+    n_e = T // desc.m
+    ent = torch.empty((n_e, desc.c), device=dev)
+    keys = torch.empty((n_e, desc.c_idx), device=dev)
+    meta = torch.empty((n_e, 2), dtype=torch.int32, device=dev)
+    cnt = torch.zeros(1, dtype=torch.int32, device=dev)
+    win = torch.empty((T, desc.c), device=dev)
+    ws_c = torch.empty(abi.workspace_size(desc, abi.OP_COMPRESS, T), dtype=torch.uint8, device=dev)
+    ld = ((ctx + T) // desc.m + 63) // 64 * 64
+    scores = torch.empty((T, ld), dtype=torch.bfloat16, device=dev)
+    nv = torch.empty(T, dtype=torch.int32, device=dev)
+    sel = torch.empty((T, desc.top_k), dtype=torch.int32, device=dev)
+    ws_t = torch.empty(max(1, abi.workspace_size(desc, abi.OP_TOPK, T, ld, desc.top_k)), dtype=torch.uint8, device=dev)
+    out = torch.empty((T, desc.n_heads, desc.c), dtype=torch.bfloat16, device=dev)
+    ws_a = torch.empty(max(1, abi.workspace_size(desc, abi.OP_ATTENTION, T, desc.top_k + desc.n_win)),
+                       dtype=torch.uint8, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+
+    def step():
+        ev[0].record()
+        abi.compress_kv(desc, bi.batch, T, d, H, P["W"], P["W_idx"], P["B_a"], P["B_b"], P["B_a_idx"], P["B_b_idx"],
+                        P["gamma"], st.state, ent, keys, meta, cnt, n_e, win, ws_c)
+        abi.cache_append(desc, bi.batch, T, ent, keys, meta, cnt, n_e, win, st.kv, st.idx, st.state)
+        ev[1].record()
+        abi.index_scores(desc, bi.batch, T, qI, w, st.idx, scores, ld, nv)
+        ev[2].record()
+        abi.topk_select(desc.score_fmt, T, scores, ld, nv, desc.top_k, sel, ws_t)
+        ev[3].record()
+        abi.sparse_mqa(desc, bi.batch, T, q, P["q_gamma"], sel, st.kv, st.state, P["sinks"], out, ws_a)
+        ev[4].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    parts = np.zeros(4)
+    tot = 0.0
+    for _ in range(steps):
+        step()
+        torch.cuda.synchronize()
+        e = [ev[i].elapsed_time(ev[i + 1]) for i in range(4)]
+        parts += e
+        tot += ev[0].elapsed_time(ev[4])
+    parts /= steps
+    ms = tot / steps
+    E = ctx // desc.m
+    sumV = sum((ctx + t + 1) // desc.m for t in range(T))
+    idx_flop = 2.0 * desc.n_idx_heads * desc.c_idx * sumV
+    attn_flop = 4.0 * desc.n_heads * desc.c * T * (desc.top_k + desc.n_win)
+    proj_flop = 2.0 * T * d * (4 * desc.c + 4 * desc.c_idx)
+    idx_tfs = idx_flop / (parts[1] * 1e-3) / 1e12
+    del wl
+    torch.cuda.empty_cache()
+    return {"workload": "csa_prefill_1m", "tokens_per_s": round(T / (ms * 1e-3), 1), "ms_per_chunk": round(ms, 3),
+            "chunk": T, "ctx": ctx, "d": d,
+            "ms_compress_append": round(parts[0], 3), "ms_index": round(parts[1], 3), "ms_topk": round(parts[2], 3),
+            "ms_attention": round(parts[3], 3),
+            "tflops_total": round((idx_flop + attn_flop + proj_flop) / (ms * 1e-3) / 1e12, 1),
+            "roofline": {"bound": "mfma", "kernel": "index_prefill_kernel", "achieved": round(idx_tfs, 1),
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(idx_tfs / BF16_PEAK_TFLOPS, 4),
+                         "traffic": None, "algorithmic_flop_per_launch": idx_flop},
+            "attention_tflops": round(attn_flop / (parts[3] * 1e-3) / 1e12, 1)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="csa_decode_128k", choices=["csa_decode_128k", "hybrid_decode_1m"])
+    ap.add_argument("--replicas", type=int, default=0, help="cache replicas rotated between steps (0: workload default)")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the 1M decode and 1M prefill sub-results")
+    ap.add_argument("--cpu-tokens", type=int, default=384, help="decode tokens in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--copy-probe", action="store_true", help="also run a 1 GiB device copy (HBM counter scale)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        raise SystemExit(2)
+
+    import torch
+    if args.copy_probe:
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    prim = time_decode(args.workload, args.steps, args.warmup, args.replicas, not args.no_graph)
+    extras = {}
+    if not args.no_extras:
+        other = "hybrid_decode_1m" if args.workload == "csa_decode_128k" else "csa_decode_128k"
+        extras[other] = time_decode(other, max(20, args.steps // 2), args.warmup, 0, not args.no_graph)
+        extras["csa_prefill_1m"] = time_prefill(max(2, min(5, args.steps // 40)), 1)
+    wd = workload_def(args.workload)
     cpu = cpu_baseline(wd, args.cpu_tokens) if args.cpu_tokens > 0 else None
     line = {
         "metric": "CSA decode tokens/s @128K & 1M ctx; achieved HBM GB/s and MFMA % of peak",
-        "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "value": prim["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": prim["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16/fp8 storage, fp32 accumulate", "data": "synthetic",
-        "config": {"workload": args.workload, "requests": wd["n_req"], "ctx": wd["ctx"],
-                   "layers": len(wd["descs"]), "d": wd["d"], "replicas": reps, "graph": not args.no_graph},
-        "step_hbm_gbs": round(step_gbs, 1), "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
-        "step_algorithmic_bytes": ab,
-        "roofline": roof,
+        "config": {"workload": args.workload, "requests": prim["requests"], "ctx": prim["ctx"],
+                   "layers": prim["layers"], "d": prim["d"], "replicas": prim["replicas"], "graph": prim["graph"]},
+        "step_hbm_gbs": prim["step_hbm_gbs"], "step_hbm_frac": prim["step_hbm_frac"],
+        "step_algorithmic_bytes": prim["step_algorithmic_bytes"],
+        "roofline": prim["roofline"],
         "cpu_baseline": cpu,
-        "setup_s": round(build_s, 1),
+        "extra": extras,
+        "setup_s": prim["setup_s"],
     }
     print(json.dumps(line), flush=True)
 

@@ -76,6 +76,8 @@ int check_layer(const csa_layer_desc* L)
     REQUIRE(L->kind == CSA_KIND_CSA || L->kind == CSA_KIND_HCA, CSA_EINVAL, "kind %d", L->kind);
     REQUIRE(L->m >= 1 && L->block_tokens >= L->m && L->block_tokens % L->m == 0, CSA_EINVAL,
             "m=%d must divide block_tokens=%d", L->m, L->block_tokens);
+    REQUIRE(((L->block_tokens / L->m) & (L->block_tokens / L->m - 1)) == 0, CSA_EUNSUPPORTED,
+            "entries per block (block_tokens / m = %d) must be a power of two", L->block_tokens / L->m);
     REQUIRE(L->c == 128 || L->c == 256 || L->c == 512, CSA_EUNSUPPORTED, "c=%d (supported: 128, 256, 512)", L->c);
     REQUIRE(L->rope_dim > 0 && L->rope_dim <= L->c && L->rope_dim % 2 == 0 && L->rope_dim <= 512, CSA_EINVAL,
             "rope_dim=%d", L->rope_dim);
@@ -306,6 +308,7 @@ int csa_index_scores(void* stream, const csa_layer_desc* layer, const csa_batch*
     a.max_blocks = batch->max_blocks;
     a.m = layer->m;
     a.epb = layer->block_tokens / layer->m;
+    a.epb_log2 = __builtin_ctz((unsigned)a.epb);
     a.nh = layer->n_idx_heads;
     a.cI = layer->c_idx;
     a.q_bf16 = layer->act_fmt == CSA_FMT_BF16;
@@ -368,6 +371,7 @@ static int attention_common(void* stream, const csa_layer_desc* layer, const csa
     a.max_blocks = batch->max_blocks;
     a.m = layer->m;
     a.epb = layer->block_tokens / layer->m;
+    a.epb_log2 = __builtin_ctz((unsigned)a.epb);
     a.c = layer->c;
     a.r = layer->rope_dim;
     a.nh = layer->n_heads;

@@ -178,9 +178,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
             if (slot < K0) {
                 const int e = dense ? slot : a.sel[(size_t)gq * a.k + slot];
                 if (e >= 0 && e < V) {
-                    const int phys = a.block_table[(size_t)req * a.max_blocks + e / a.epb];
+                    const int phys = a.block_table[(size_t)req * a.max_blocks + (e >> a.epb_log2)];
                     const char* blk = (const char*)a.kv + (size_t)phys * a.kv_block_bytes;
-                    p = blk + hdr + (size_t)(e % a.epb) * rec;
+                    p = blk + hdr + (size_t)(e & (a.epb - 1)) * rec;
                     if (KVF == 2) sc = *(const float*)blk;
                 }
             } else if (slot < n_slots && slot - K0 < nwr) {
@@ -245,11 +245,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
             } else {
                 uint4 b;
                 if (KVF == 2 && entry && d0 < nf) {
-                    const uint32_t c0 = raw[u][0].x, c1 = raw[u][0].y;
-                    b = make_uint4(pack_bf16x2(e4m3_to_f32(c0 & 0xFF), e4m3_to_f32((c0 >> 8) & 0xFF)),
-                                   pack_bf16x2(e4m3_to_f32((c0 >> 16) & 0xFF), e4m3_to_f32(c0 >> 24)),
-                                   pack_bf16x2(e4m3_to_f32(c1 & 0xFF), e4m3_to_f32((c1 >> 8) & 0xFF)),
-                                   pack_bf16x2(e4m3_to_f32((c1 >> 16) & 0xFF), e4m3_to_f32(c1 >> 24)));
+                    const uint2 b0 = e4m3x4_to_bf16x4(raw[u][0].x), b1 = e4m3x4_to_bf16x4(raw[u][0].y);
+                    b = make_uint4(b0.x, b0.y, b1.x, b1.y);
                 } else {
                     b = raw[u][0];
                 }
@@ -323,9 +320,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
         for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx);
+        // The reference max only moves when a logit exceeds it by more than
+        // 2^8 (base-2 units), so weights stay <= 256 and the accumulators are
+        // rescaled rarely; the final normalisation uses the same reference.
+        const bool raise = mx > m_run + 8.0f;
+        const float m_new = raise ? mx : m_run;
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = exp2f(m_run - m_use);
+        const float alpha = raise ? exp2f(m_run - m_use) : 1.0f;
         float p[8], ps = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) { p[i] = exp2f(sv[i] - m_use); ps += p[i]; }
@@ -333,8 +334,10 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
         ps += __shfl_xor(ps, 32, 64);
         l_run = l_run * alpha + ps;
         m_run = m_new;
+        if (__any(raise)) {
 #pragma unroll
-        for (int i = 0; i < Cfg::DT; ++i) O[i] *= alpha;
+            for (int i = 0; i < Cfg::DT; ++i) O[i] *= alpha;
+        }
 
         // ---- O^T += V^T . P^T
         if constexpr (Cfg::F32) {

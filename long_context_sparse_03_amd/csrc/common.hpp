@@ -40,6 +40,17 @@ CSA_DEV float e4m3_to_f32(uint32_t q)
     return __uint_as_float(__float_as_uint(v) | s);
 }
 
+// Four E4M3FN codes (one dword) to four bf16 values (two dwords), exactly,
+// with gfx950's conversion instruction (OCP E4M3; checked against
+// e4m3_to_f32 for every finite code).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+CSA_DEV uint2 e4m3x4_to_bf16x4(uint32_t codes)
+{
+    const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)codes, 1.0f, false);
+    const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)codes, 1.0f, true);
+    return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+}
+
 // E4M3FN code of an fp32 value: round to nearest even, saturate to +-448,
 // a zero result is stored as +0.
 CSA_DEV uint32_t f32_to_e4m3(float v)

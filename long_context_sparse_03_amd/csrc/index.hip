@@ -11,9 +11,10 @@
 // are applied to the accumulators in registers; the sum over the four lane
 // groups is a fixed butterfly, so the result is deterministic.
 //
-// MXFP4 keys (and the MXFP4-quantised query) are expanded to bf16 in
-// registers; every E2M1 value times its power-of-two scale is exact in bf16,
-// so the bf16 MFMA computes exactly the dequantised product.
+// MXFP4 keys and the MXFP4-quantised query go straight into gfx950's scaled
+// FP4 MFMA (16x16x128 with E8M0 block scales): one instruction covers a
+// 128-wide key, and the products of E2M1 values and power-of-two scales are
+// exact, so only the fp32 accumulation order differs from the definition.
 #include <type_traits>
 
 #include "common.hpp"
@@ -45,43 +46,41 @@ CSA_DEV void load_frags(const void* base, bool src_bf16, int n_frag, int q_elems
     }
 }
 
-// Quantise 32 values (one MX block) to MXFP4 and return them dequantised as
-// four bf16 fragments.
-CSA_DEV void mx_quant_frags(const float* v, uint4* out)
+// Quantise the 32 bf16 values of four fragments (one MX block) to E2M1 codes
+// (element 2i in the low nibble of byte i) and return the E8M0 scale code.
+CSA_DEV int mx_quant_codes(const uint4 (&f)[4], uint4& codes)
 {
+    float v[32];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const uint32_t w4[4] = {f[s].x, f[s].y, f[s].z, f[s].w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            v[8 * s + 2 * h] = bf16_to_f32(w4[h] & 0xFFFF);
+            v[8 * s + 2 * h + 1] = bf16_to_f32(w4[h] >> 16);
+        }
+    }
     float amax = 0.f;
 #pragma unroll
     for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
     const int sc = mx_scale_code(amax);
-    const float up = ldexpf(1.0f, sc - 127);
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-        uint32_t w[4];
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            float a = e2m1_to_f32(f32_to_e2m1(ldexpf(v[8 * f + 2 * h], 127 - sc))) * up;
-            float b = e2m1_to_f32(f32_to_e2m1(ldexpf(v[8 * f + 2 * h + 1], 127 - sc))) * up;
-            w[h] = pack_bf16x2(a, b);
-        }
-        out[f] = make_uint4(w[0], w[1], w[2], w[3]);
-    }
+    for (int j = 0; j < 32; ++j) w[j / 8] |= f32_to_e2m1(ldexpf(v[j], 127 - sc)) << (4 * (j % 8));
+    codes = make_uint4(w[0], w[1], w[2], w[3]);
+    return sc;
 }
 
-// Expand 32 stored E2M1 codes (16 bytes) with their E8M0 scale to four bf16 fragments.
-CSA_DEV void mx_expand_frags(uint4 codes, uint32_t scale_code, uint4* out)
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// One scaled FP4 MFMA (16x16x128, E2M1 operands with E8M0 block scales): the
+// lane's 16 bytes hold its row's (column's) 32-element block l/16, and its
+// scale applies to those 32 elements.
+CSA_DEV f32x4_t mfma_fp4(uint4 a, int sa, uint4 b, int sb)
 {
-    const float up = ldexpf(1.0f, (int)scale_code - 127);
-    uint32_t c4[4] = {codes.x, codes.y, codes.z, codes.w};
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-        uint32_t w[4];
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            uint32_t byte = (c4[f] >> (8 * h)) & 0xFFu;
-            w[h] = pack_bf16x2(e2m1_to_f32(byte & 15u) * up, e2m1_to_f32(byte >> 4) * up);
-        }
-        out[f] = make_uint4(w[0], w[1], w[2], w[3]);
-    }
+    const i32x8_t av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+    const i32x8_t bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, zero4(), 4, 4, 0, sa, 0, sb);
 }
 
 // Decode-shaped launch: one workgroup per (query, EPW entries).  Each wave
@@ -92,36 +91,29 @@ constexpr int IDX_EPW = 1024;                 // entries per workgroup
 constexpr int IDX_ITERS = IDX_EPW / 256;      // iterations of 256 entries (64 per wave)
 
 template <int IDXF, int S>
-CSA_DEV void load_keys(const IndexArgs& a, const int* bt, int blk0, int e0, int V, int g, int li, uint4 (&B)[4][S],
-                       uint32_t (&SC)[4])
+CSA_DEV void load_keys(const IndexArgs& a, const int* bt, int blk0, int e0, int V, int g, int li, uint4 (&B)[4][S])
 {
     // Loads are unconditional (entries past V are clamped to V-1): an MFMA
     // column only feeds the score of its own entry, and scores of entries
     // >= V are not stored.  Branch-free loads stay in flight together.
     const int cI = a.cI, quarter = cI / 4;
-    const size_t kbytes = IDXF == 0 ? (size_t)cI * 4 : (IDXF == 1 ? (size_t)cI * 2 : (size_t)cI / 2);
+    const size_t kbytes = IDXF == 0 ? (size_t)cI * 4 : (size_t)cI * 2;
 #pragma unroll
     for (int tile = 0; tile < 4; ++tile) {
         const int e = min(e0 + 16 * tile + li, V - 1);
-        const int phys = bt[e / a.epb - blk0];
-        const int slot = e % a.epb;
+        const int phys = bt[(e >> a.epb_log2) - blk0];
+        const int slot = (e & (a.epb - 1));
         const char* kb = (const char*)a.keys + (size_t)phys * a.key_block_bytes;
-        if constexpr (IDXF == 2) {
-            B[tile][0] = ld16(kb + (size_t)slot * (cI / 2) + (size_t)g * 16);
-            SC[tile] = (uint8_t)kb[(size_t)a.epb * (cI / 2) + (size_t)slot * (cI / 32) + g];
-        } else {
-            const char* kp = kb + (size_t)slot * kbytes + (size_t)g * quarter * (IDXF == 0 ? 4 : 2);
+        const char* kp = kb + (size_t)slot * kbytes + (size_t)g * quarter * (IDXF == 0 ? 4 : 2);
 #pragma unroll
-            for (int s = 0; s < S; ++s) B[tile][s] = ld16(kp + 16 * s);
-        }
+        for (int s = 0; s < S; ++s) B[tile][s] = ld16(kp + 16 * s);
     }
 }
 
 template <int IDXF, int HT, int S>
 __global__ __launch_bounds__(256) void index_decode_kernel(IndexArgs a)
 {
-    // IDXF 0: fp32 keys and queries; 1: bf16 keys and queries; 2: MXFP4 keys,
-    // bf16 queries quantised to MXFP4 here.
+    // IDXF 0: fp32 keys and queries; 1: bf16 keys and queries.
     using MMA = typename std::conditional<IDXF == 0, MmaF32, MmaBF16>::type;
     __shared__ int bt[IDX_EPW + 1];             // physical blocks of this workgroup's entries
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
@@ -138,8 +130,8 @@ __global__ __launch_bounds__(256) void index_decode_kernel(IndexArgs a)
 
     // ---- prologue: block-table slice, query fragments and head weights,
     //      all loads issued together (clamped indices, masked afterwards)
-    const int blk0 = wg0 / a.epb;
-    const int nblk = (min(V, wg0 + IDX_EPW) - 1) / a.epb - blk0 + 1;
+    const int blk0 = wg0 >> a.epb_log2;
+    const int nblk = ((min(V, wg0 + IDX_EPW) - 1) >> a.epb_log2) - blk0 + 1;
     int btv[(IDX_EPW + 255) / 256];
 #pragma unroll
     for (int i = 0; i < (IDX_EPW + 255) / 256; ++i) {
@@ -164,19 +156,6 @@ __global__ __launch_bounds__(256) void index_decode_kernel(IndexArgs a)
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
         const bool hv = 16 * ht + li < nh;
-        if constexpr (IDXF == 2) {
-            float v[32];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const uint32_t w4[4] = {A[ht][s].x, A[ht][s].y, A[ht][s].z, A[ht][s].w};
-#pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    v[8 * s + 2 * h] = bf16_to_f32(w4[h] & 0xFFFF);
-                    v[8 * s + 2 * h + 1] = bf16_to_f32(w4[h] >> 16);
-                }
-            }
-            mx_quant_frags(v, A[ht]);
-        }
 #pragma unroll
         for (int s = 0; s < S; ++s) A[ht][s] = sel16(hv, A[ht][s]);
 #pragma unroll
@@ -187,33 +166,25 @@ __global__ __launch_bounds__(256) void index_decode_kernel(IndexArgs a)
     // ---- main loop: 256 entries per iteration (64 per wave); the next
     //      iteration's key loads are issued before this one's arithmetic
     uint4 B[2][4][S];
-    uint32_t SC[2][4];
-    load_keys<IDXF, S>(a, bt, blk0, wg0 + wave * 64, V, g, li, B[0], SC[0]);
+    load_keys<IDXF, S>(a, bt, blk0, wg0 + wave * 64, V, g, li, B[0]);
 #pragma unroll
     for (int it = 0; it < IDX_ITERS; ++it) {
         const int cur = it & 1;
         const int e_base = wg0 + it * 256 + wave * 64;
         if (it + 1 < IDX_ITERS && e_base + 256 < V)
-            load_keys<IDXF, S>(a, bt, blk0, e_base + 256, V, g, li, B[cur ^ 1], SC[cur ^ 1]);
+            load_keys<IDXF, S>(a, bt, blk0, e_base + 256, V, g, li, B[cur ^ 1]);
         __builtin_amdgcn_sched_barrier(0);
         if (e_base >= V) break;                  // wave-uniform
 #pragma unroll
         for (int tile = 0; tile < 4; ++tile) {
             if (e_base + 16 * tile >= V) break;  // wave-uniform: the whole tile is past V
             const int e = e_base + 16 * tile + li;
-            uint4 Bt[S];
-            if constexpr (IDXF == 2) {
-                mx_expand_frags(B[cur][tile][0], SC[cur][tile], Bt);
-            } else {
-#pragma unroll
-                for (int s = 0; s < S; ++s) Bt[s] = B[cur][tile][s];
-            }
             float v = 0.f;
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) {
                 f32x4_t acc = zero4();
 #pragma unroll
-                for (int s = 0; s < S; ++s) acc = MMA::step(A[ht][s], Bt[s], acc);
+                for (int s = 0; s < S; ++s) acc = MMA::step(A[ht][s], B[cur][tile][s], acc);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) v += wv[ht][i] * fmaxf(acc[i], 0.f);
             }
@@ -228,6 +199,226 @@ __global__ __launch_bounds__(256) void index_decode_kernel(IndexArgs a)
     }
 }
 
+// Prefill-shaped launch (bf16 keys): eight queries of one request per
+// workgroup, one per wave, share every 128-key tile staged in LDS, so a key
+// is read from memory once per eight queries.  Tiles are double-buffered:
+// the next tile's loads are in flight while the current one is multiplied.
+constexpr int PF_QPW = 8;                     // queries (waves) per workgroup
+constexpr int PF_TILE = 128;                  // keys per LDS tile
+constexpr int PF_ECH = 8192;                  // keys per workgroup
+
+template <int HT, int S>
+__global__ __launch_bounds__(512) void index_prefill_kernel(IndexArgs a, int groups_per_req)
+{
+    constexpr int KSTR = 136;                 // LDS key stride in bf16 (272 bytes: spreads banks)
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][PF_TILE * KSTR];
+    __shared__ int bt[PF_ECH / 32 + 2];
+    __shared__ int cu_sh[1025];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
+    const int req = blockIdx.y / groups_per_req, grp = blockIdx.y % groups_per_req;
+    if (a.n_req >= 1024) return;                                    // host dispatch keeps n_req small here
+    for (int i = threadIdx.x; i <= a.n_req; i += blockDim.x) cu_sh[i] = a.cu_new[i];
+    __syncthreads();
+    const int cu = cu_sh[req], n_tok = cu_sh[req + 1] - cu;
+    if (PF_QPW * grp >= n_tok) return;                             // whole workgroup
+    const int s0 = a.start_pos[req];
+    const int qi = min(PF_QPW * grp + wave, n_tok - 1);              // clamped: extra waves help with loads only
+    const bool qvalid = PF_QPW * grp + wave < n_tok;
+    const int gq = cu + qi;
+    const int V = (s0 + qi + 1) / a.m;
+    const int Vmax = (s0 + min(PF_QPW * grp + PF_QPW, n_tok)) / a.m;  // of the workgroup's last query
+    if (blockIdx.x == 0 && lane == 0 && qvalid) a.n_valid[gq] = V;
+    const int e0 = blockIdx.x * PF_ECH;
+    if (e0 >= Vmax) return;                                         // whole workgroup
+    const int e1 = min(Vmax, e0 + PF_ECH);
+    const int cI = a.cI, nh = a.nh, quarter = cI / 4;
+    const size_t kbytes = (size_t)cI * 2;
+
+    const int blk0 = e0 >> a.epb_log2;
+    const int nblk = ((e1 - 1) >> a.epb_log2) - blk0 + 1;
+    for (int j = threadIdx.x; j < nblk; j += blockDim.x) bt[j] = a.block_table[(size_t)req * a.max_blocks + blk0 + j];
+
+    // query fragments and head weights of this wave's query
+    uint4 A[HT][S];
+    float wv[HT][4];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        const int head = min(16 * ht + li, nh - 1);
+        const char* qp = (const char*)a.q + ((size_t)gq * nh + head) * cI * 2 + (size_t)g * quarter * 2;
+#pragma unroll
+        for (int s = 0; s < S; ++s) A[ht][s] = ld16(qp + 16 * s);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wv[ht][i] = a.w[(size_t)gq * nh + min(16 * ht + 4 * g + i, nh - 1)];
+    }
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        const bool hv = 16 * ht + li < nh;
+#pragma unroll
+        for (int s = 0; s < S; ++s) A[ht][s] = sel16(hv, A[ht][s]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wv[ht][i] = 16 * ht + 4 * g + i < nh ? wv[ht][i] : 0.f;
+    }
+    __syncthreads();                                                // bt ready
+
+    // tile staging: 16-byte chunks, chunk c of key e at idx = e * CPK + c
+    const int CPK = cI / 8;                                         // chunks per key
+    const int chunks = PF_TILE * CPK;
+    constexpr int LPT = 4;                                          // chunk loads per thread (PF_TILE*16/512)
+    auto load_tile = [&](int t0, uint4 (&r)[LPT]) {
+#pragma unroll
+        for (int u = 0; u < LPT; ++u) {
+            const int idx = threadIdx.x + u * 512;
+            const int e = min(t0 + idx / CPK, e1 - 1);
+            const int c = idx % CPK;
+            const char* kb = (const char*)a.keys + (size_t)bt[(e >> a.epb_log2) - blk0] * a.key_block_bytes;
+            r[u] = idx < chunks ? ld16(kb + (size_t)((e & (a.epb - 1))) * kbytes + 16 * c) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto store_tile = [&](int buf, const uint4 (&r)[LPT]) {
+#pragma unroll
+        for (int u = 0; u < LPT; ++u) {
+            const int idx = threadIdx.x + u * 512;
+            if (idx < chunks) *(uint4*)&Ks[buf][(idx / CPK) * KSTR + (idx % CPK) * 8] = r[u];
+        }
+    };
+
+    uint4 R[LPT];
+    load_tile(e0, R);
+    store_tile(0, R);
+    __syncthreads();
+    const int n_tiles = (e1 - e0 + PF_TILE - 1) / PF_TILE;
+    for (int it = 0; it < n_tiles; ++it) {
+        const int t0 = e0 + it * PF_TILE;
+        const bool more = it + 1 < n_tiles;
+        if (more) load_tile(t0 + PF_TILE, R);
+        const uint16_t* K = Ks[it & 1];
+        if (qvalid && t0 < V) {
+#pragma unroll 2
+            for (int et = 0; et < PF_TILE / 16; ++et) {
+                const int e = t0 + et * 16 + li;
+                uint4 B[S];
+#pragma unroll
+                for (int s = 0; s < S; ++s) B[s] = *(const uint4*)&K[(et * 16 + li) * KSTR + g * quarter + s * 8];
+                float v = 0.f;
+#pragma unroll
+                for (int ht = 0; ht < HT; ++ht) {
+                    f32x4_t acc = zero4();
+#pragma unroll
+                    for (int s = 0; s < S; ++s) acc = MmaBF16::step(A[ht][s], B[s], acc);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v += wv[ht][i] * fmaxf(acc[i], 0.f);
+                }
+                v += __shfl_xor(v, 16, 64);
+                v += __shfl_xor(v, 32, 64);
+                if (g == 0 && e < V) {
+                    if (v == 0.0f) v = 0.0f;            // -0 is stored as +0
+                    if (a.score_bf16) ((uint16_t*)a.scores)[(size_t)gq * a.ld + e] = f32_to_bf16(v);
+                    else ((float*)a.scores)[(size_t)gq * a.ld + e] = v;
+                }
+            }
+        }
+        if (more) store_tile((it + 1) & 1, R);
+        __syncthreads();
+    }
+}
+
+// MXFP4 decode launch: as the bf16 decode kernel, with the stored key bytes
+// fed straight into the scaled FP4 MFMA (one instruction per 16 keys and 16
+// heads covers the whole 128-wide key).
+template <int HT>
+__global__ __launch_bounds__(256) void index_decode_fp4_kernel(IndexArgs a)
+{
+    __shared__ int bt[IDX_EPW + 1];
+    __shared__ int cu_sh[1025];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
+    const int gq = blockIdx.y;
+    const int req = find_request_block(a.cu_new, a.n_req, gq, cu_sh);
+    const int t = a.start_pos[req] + (gq - cu_sh[req]);
+    const int V = (t + 1) / a.m;
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.n_valid[gq] = V;
+    const int wg0 = blockIdx.x * IDX_EPW;
+    if (wg0 >= V) return;
+    const int cI = a.cI, nh = a.nh;                // cI == 128: lane group g holds MX block g
+    const int blk0 = wg0 >> a.epb_log2;
+    const int nblk = ((min(V, wg0 + IDX_EPW) - 1) >> a.epb_log2) - blk0 + 1;
+    int btv[(IDX_EPW + 255) / 256];
+#pragma unroll
+    for (int i = 0; i < (IDX_EPW + 255) / 256; ++i) {
+        const int j = min((int)threadIdx.x + 256 * i, nblk - 1);
+        btv[i] = a.block_table[(size_t)req * a.max_blocks + blk0 + j];
+    }
+    uint4 Aq[HT];
+    int sa[HT];
+    float wv[HT][4];
+#pragma unroll 1
+    for (int ht = 0; ht < HT; ++ht) {
+        const int head = min(16 * ht + li, nh - 1);
+        const char* qp = (const char*)a.q + ((size_t)gq * nh + head) * cI * 2 + (size_t)g * 64;
+        uint4 f[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) f[s] = ld16(qp + 16 * s);
+        uint4 codes;
+        const int sc = mx_quant_codes(f, codes);
+        const bool hv = 16 * ht + li < nh;
+#pragma unroll
+        for (int h = 0; h < HT; ++h)
+            if (h == ht) { Aq[h] = sel16(hv, codes); sa[h] = sc; }
+    }
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int hh = 16 * ht + 4 * g + i;
+            wv[ht][i] = hh < nh ? a.w[(size_t)gq * nh + hh] : 0.f;
+        }
+#pragma unroll
+    for (int i = 0; i < (IDX_EPW + 255) / 256; ++i)
+        if ((int)threadIdx.x + 256 * i < nblk) bt[threadIdx.x + 256 * i] = btv[i];
+    __syncthreads();
+
+    const size_t codes_off = (size_t)a.epb * (cI / 2);
+    auto load = [&](int e0, uint4 (&B)[4], uint32_t (&SC)[4]) {
+#pragma unroll
+        for (int tile = 0; tile < 4; ++tile) {
+            const int e = min(e0 + 16 * tile + li, V - 1);
+            const char* kb = (const char*)a.keys + (size_t)bt[(e >> a.epb_log2) - blk0] * a.key_block_bytes;
+            const int slot = (e & (a.epb - 1));
+            B[tile] = ld16(kb + (size_t)slot * (cI / 2) + (size_t)g * 16);
+            SC[tile] = (uint8_t)kb[codes_off + (size_t)slot * (cI / 32) + g];
+        }
+    };
+    uint4 B[2][4];
+    uint32_t SC[2][4];
+    load(wg0 + wave * 64, B[0], SC[0]);
+#pragma unroll
+    for (int it = 0; it < IDX_ITERS; ++it) {
+        const int cur = it & 1;
+        const int e_base = wg0 + it * 256 + wave * 64;
+        if (it + 1 < IDX_ITERS && e_base + 256 < V) load(e_base + 256, B[cur ^ 1], SC[cur ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (e_base >= V) break;
+#pragma unroll
+        for (int tile = 0; tile < 4; ++tile) {
+            if (e_base + 16 * tile >= V) break;
+            const int e = e_base + 16 * tile + li;
+            float v = 0.f;
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+                const f32x4_t acc = mfma_fp4(Aq[ht], sa[ht], B[cur][tile], (int)SC[cur][tile]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v += wv[ht][i] * fmaxf(acc[i], 0.f);
+            }
+            v += __shfl_xor(v, 16, 64);
+            v += __shfl_xor(v, 32, 64);
+            if (g == 0 && e < V) {
+                if (v == 0.0f) v = 0.0f;
+                if (a.score_bf16) ((uint16_t*)a.scores)[(size_t)gq * a.ld + e] = f32_to_bf16(v);
+                else ((float*)a.scores)[(size_t)gq * a.ld + e] = v;
+            }
+        }
+    }
+}
+
 template <int IDXF, int HT>
 static void launch_ht(hipStream_t st, const IndexArgs& a, dim3 grid)
 {
@@ -235,9 +426,7 @@ static void launch_ht(hipStream_t st, const IndexArgs& a, dim3 grid)
     const int quarter = a.cI / 4;
     const int epf = IDXF == 0 ? 4 : 8;
     const int S = quarter / epf;
-    if constexpr (IDXF == 2) {             // MXFP4: one 32-element MX block per lane group (c_idx = 128)
-        index_decode_kernel<IDXF, HT, 4><<<grid, 256, 0, st>>>(a);
-    } else {
+    {
         switch (S) {
         case 1: index_decode_kernel<IDXF, HT, 1><<<grid, 256, 0, st>>>(a); break;
         case 2: index_decode_kernel<IDXF, HT, 2><<<grid, 256, 0, st>>>(a); break;
@@ -262,12 +451,27 @@ static void launch_fmt(hipStream_t st, const IndexArgs& a, dim3 grid)
 
 hipError_t launch_index(hipStream_t st, const IndexArgs& a, int max_visible, int max_new)
 {
-    (void)max_new;
     if (a.n_tokens <= 0) return hipSuccess;
+    if (a.idx_fmt == 1 && a.cI == 128 && a.nh <= 64 && max_new >= 2 * PF_QPW && a.n_req < 1024) {
+        const int groups = (max_new + PF_QPW - 1) / PF_QPW;
+        dim3 grid(max_visible > 0 ? (max_visible + PF_ECH - 1) / PF_ECH : 1, a.n_req * groups);
+        const int HT = (a.nh + 15) / 16;
+        if (HT == 4) index_prefill_kernel<4, 4><<<grid, 512, 0, st>>>(a, groups);
+        else if (HT == 3) index_prefill_kernel<3, 4><<<grid, 512, 0, st>>>(a, groups);
+        else if (HT == 2) index_prefill_kernel<2, 4><<<grid, 512, 0, st>>>(a, groups);
+        else index_prefill_kernel<1, 4><<<grid, 512, 0, st>>>(a, groups);
+        return hipGetLastError();
+    }
     dim3 grid(max_visible > 0 ? (max_visible + IDX_EPW - 1) / IDX_EPW : 1, a.n_tokens);
     if (a.idx_fmt == 0) launch_fmt<0>(st, a, grid);
     else if (a.idx_fmt == 1) launch_fmt<1>(st, a, grid);
-    else launch_fmt<2>(st, a, grid);
+    else {
+        const int HT = (a.nh + 15) / 16;
+        if (HT == 4) index_decode_fp4_kernel<4><<<grid, 256, 0, st>>>(a);
+        else if (HT == 3) index_decode_fp4_kernel<3><<<grid, 256, 0, st>>>(a);
+        else if (HT == 2) index_decode_fp4_kernel<2><<<grid, 256, 0, st>>>(a);
+        else index_decode_fp4_kernel<1><<<grid, 256, 0, st>>>(a);
+    }
     return hipGetLastError();
 }
 

@@ -65,7 +65,7 @@ struct IndexArgs {
     const int32_t* start_pos;
     const int32_t* block_table;
     int n_req, max_blocks;
-    int m, epb, nh, cI;
+    int m, epb, epb_log2, nh, cI;
     int q_bf16, idx_fmt, score_bf16;
     void* scores;
     int ld;
@@ -94,7 +94,7 @@ struct AttnArgs {
     const int32_t* start_pos;
     const int32_t* block_table;
     int n_req, max_blocks;
-    int m, epb, c, r, nh;
+    int m, epb, epb_log2, c, r, nh;
     int kv_fmt, q_bf16, win_bf16, out_bf16;
     float eps, theta, scale_log2;
     const float* sinks;
