@@ -113,9 +113,33 @@ def cpu_baseline(wd, n_tok: int, seed: int = 11) -> dict:
                       f"{elapsed:.1f} s"}
 
 
+def profiled_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of a kernel from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter on a copy of
+    known size), or None when there is none or the kernel sources changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for ln in open(path):
+        if ":" in ln and not ln.startswith(" "):
+            k, v = ln.split(":", 1)
+            vals[k.strip()] = v.strip().split()[0] if v.strip() else ""
+    h = hashlib.sha256()
+    for f in ("index.hip", "common.hpp", "kernels.hpp"):
+        with open(os.path.join(ROOT, "long_context_sparse_03_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if vals.get("sources_sha256") != h.hexdigest():
+        return None
+    return int(float(vals["traffic_bytes_per_launch"]))
+
+
 def time_decode(name, steps, warmup, replicas=0, graph=True):
     """Decode throughput of one workload; returns a dict of measurements."""
     import torch
+    from long_context_sparse_03_amd import abi
     from long_context_sparse_03_amd.workloads import DecodeWorkload, torch_rows
 
     wd = workload_def(name)
@@ -128,27 +152,10 @@ def time_decode(name, steps, warmup, replicas=0, graph=True):
     build_s = time.time() - t_build
 
     stream = torch.cuda.Stream()
-    # per-kernel timing of the index scan, live, with events on the launch stream
-    n_eager = min(steps, 30)
-    idx_ms = []
     with torch.cuda.stream(stream):
         for i in range(4):
             wls[i % reps].step()
         stream.synchronize()
-        for i in range(n_eager):
-            wl = wls[i % reps]
-            evs = []
-            hooks = []
-            for st, _ in wl.layers:
-                if st.is_csa:
-                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    evs.append((e0, e1))
-                    hooks.append((lambda e=e0: e.record(stream), lambda e=e1: e.record(stream)))
-                else:
-                    hooks.append(None)
-            wl.step(hooks)
-            stream.synchronize()
-            idx_ms.extend(a.elapsed_time(b) for a, b in evs)
 
     graphs = []
     if graph:
@@ -177,13 +184,33 @@ def time_decode(name, steps, warmup, replicas=0, graph=True):
         t1.record(stream)
         torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
+    # Per-launch time of the index scan of the first CSA layer, on the launch
+    # stream, right after the timed steps: HIP events cannot be recorded
+    # inside a captured graph here (torch on ROCm refuses external events),
+    # so the same launches run back to back over the rotated cache replicas
+    # (the rotation keeps the keys out of the last-level cache) between one
+    # pair of events.
+    li = next(i for i, (st, _) in enumerate(wls[0].layers) if st.is_csa)
+    n_idx = 12 * reps
+    with torch.cuda.stream(stream):
+        for j in range(reps):
+            wls[j].index_call(li)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for j in range(n_idx):
+            wls[j % reps].index_call(li)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    idx_avg_ms = e0.elapsed_time(e1) / n_idx
     ab = algorithmic_bytes(wd)
-    idx_avg_ms = float(np.mean(idx_ms)) if idx_ms else None
+    kname = "index_decode_fp4_kernel" if wls[0].layers[li][0].desc.idx_fmt == abi.IDX_MXFP4 else "index_decode_kernel"
     roof = None
     if idx_avg_ms:
         achieved = ab["index_launch"] / (idx_avg_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": "index_decode_kernel", "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+        roof = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": profiled_traffic(kname, name),
                 "launch_ms": round(idx_avg_ms, 5), "algorithmic_bytes_per_launch": ab["index_launch"]}
     step_gbs = ab["total"] / (ms * 1e-3) / 1e9
     del wls, graphs
@@ -200,6 +227,7 @@ def time_prefill(steps, warmup):
     compress_kv, cache_append, index_scores, topk_select, sparse_mqa."""
     import torch
     from long_context_sparse_03_amd import abi, presets
+    from long_context_sparse_03_amd import abi
     from long_context_sparse_03_amd.workloads import DecodeWorkload, torch_rows
     from long_context_sparse_03_amd.layer import make_batch
 
@@ -286,7 +314,7 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas rotated between steps (0: workload default)")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the 1M decode and 1M prefill sub-results")
-    ap.add_argument("--cpu-tokens", type=int, default=384, help="decode tokens in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--cpu-tokens", type=int, default=640, help="decode tokens in the CPU-oracle sample (0: skip)")
     ap.add_argument("--copy-probe", action="store_true", help="also run a 1 GiB device copy (HBM counter scale)")
     args = ap.parse_args()
     if args.gpus != 1:

@@ -81,7 +81,8 @@ int check_layer(const csa_layer_desc* L)
     REQUIRE(L->c == 128 || L->c == 256 || L->c == 512, CSA_EUNSUPPORTED, "c=%d (supported: 128, 256, 512)", L->c);
     REQUIRE(L->rope_dim > 0 && L->rope_dim <= L->c && L->rope_dim % 2 == 0 && L->rope_dim <= 512, CSA_EINVAL,
             "rope_dim=%d", L->rope_dim);
-    REQUIRE((L->c - L->rope_dim) % 16 == 0, CSA_EUNSUPPORTED, "c - rope_dim must be a multiple of 16");
+    REQUIRE((L->c == 128 && L->rope_dim == 32) || (L->c >= 256 && L->rope_dim == 64), CSA_EUNSUPPORTED,
+            "(c, rope_dim) = (%d, %d); supported: (128, 32), (256, 64), (512, 64)", L->c, L->rope_dim);
     REQUIRE(L->n_heads >= 1 && L->n_heads <= 128 && (L->n_heads <= 64 || L->n_heads % 64 == 0), CSA_EUNSUPPORTED,
             "n_heads=%d (1..64, or a multiple of 64 up to 128)", L->n_heads);
     REQUIRE(L->n_heads <= 16 || L->n_heads % 16 == 0, CSA_EUNSUPPORTED, "n_heads=%d must be a multiple of 16 above 16",

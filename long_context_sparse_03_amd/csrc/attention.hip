@@ -30,8 +30,9 @@ namespace csa {
 
 constexpr float LOG2E = 1.4426950408889634f;
 
-template <int KVF, int C>
+template <int KVF, int C, int R>
 struct AttnCfg {
+    static constexpr int NF = C - R;                                     // non-rotary channels
     static constexpr bool F32 = KVF == 0;
     using MMA = typename std::conditional<F32, MmaF32, MmaBF16>::type;
     using ET = typename std::conditional<F32, float, uint16_t>::type;   // LDS element type
@@ -47,10 +48,10 @@ struct AttnCfg {
     static constexpr int QPARTS = SPLIT ? 2 : 1;
 };
 
-template <int KVF, int C>
+template <int KVF, int C, int R>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
 {
-    using Cfg = AttnCfg<KVF, C>;
+    using Cfg = AttnCfg<KVF, C, R>;
     using MMA = typename Cfg::MMA;
     using ET = typename Cfg::ET;
     constexpr int EPF = Cfg::EPF, KP = Cfg::KP, VP = Cfg::VP;
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
     __shared__ int cu_sh[1025];
     const int req = find_request_block(a.cu_new, a.n_req, gq, cu_sh);
     const int t = a.start_pos[req] + (gq - cu_sh[req]);
-    const int nf = C - a.r;                                   // non-rotary channels
+    constexpr int nf = Cfg::NF;                               // non-rotary channels
     const bool dense = a.sel == nullptr;
     const int V = (t + 1) / a.m;
     const int K0 = dense ? V : a.k;                            // entry slots before the window
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
     const int tile1 = min(n_tiles, tile0 + a.tiles_per_split);
 
     // RoPE table at +t and the query norm gains
-    for (int j = threadIdx.x; j < a.r / 2; j += nthr) rope_cs((double)t, j, a.r, a.theta, &rcs[j], &rsn[j]);
+    for (int j = threadIdx.x; j < R / 2; j += nthr) rope_cs((double)t, j, R, a.theta, &rcs[j], &rsn[j]);
     for (int j = threadIdx.x; j < C; j += nthr) qg[j] = a.q_gamma[j];
 
     // query fragments (B operand of S^T): head li, channels s*K + g*EPF + j.
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
     float m_run = -INFINITY, l_run = 0.f;
 
     const size_t win_es = a.win_bf16 ? 2 : 4;
-    const size_t rec = KVF == 2 ? (size_t)(nf + 2 * a.r) : (size_t)C * (KVF == 0 ? 4 : 2);
+    const size_t rec = KVF == 2 ? (size_t)(nf + 2 * R) : (size_t)C * (KVF == 0 ? 4 : 2);
     const size_t hdr = KVF == 2 ? 64 : 0;
     const char* ring = (const char*)a.state + (size_t)req * a.state_stride;
     constexpr int CH = C / 8;                                  // 8-channel chunks per row
@@ -477,14 +478,15 @@ size_t attention_workspace(int n_tokens, int n_heads, int c, int rows_max)
     return (size_t)n_tokens * n_heads * s * (c + 2) * sizeof(float);
 }
 
+// (c, rope) shapes: (128, 32), (256, 64), (512, 64); fp32 KV up to c = 256
 template <int KVF>
 static void launch_c(hipStream_t st, const AttnArgs& a, dim3 grid, int threads)
 {
     switch (a.c) {
-    case 128: attn_kernel<KVF, 128><<<grid, threads, 0, st>>>(a); break;
-    case 256: attn_kernel<KVF, 256><<<grid, threads, 0, st>>>(a); break;
+    case 128: attn_kernel<KVF, 128, 32><<<grid, threads, 0, st>>>(a); break;
+    case 256: attn_kernel<KVF, 256, 64><<<grid, threads, 0, st>>>(a); break;
     case 512:
-        if constexpr (KVF != 0) attn_kernel<KVF, 512><<<grid, threads, 0, st>>>(a);   // fp32 KV: c <= 256
+        if constexpr (KVF != 0) attn_kernel<KVF, 512, 64><<<grid, threads, 0, st>>>(a);
         break;
     default: break;
     }

@@ -21,6 +21,7 @@
 namespace csa {
 
 constexpr int TOPK_THREADS = 1024;
+constexpr int MAX_K = 2048;                                  // largest k the entry points accept
 constexpr int CAP16 = 40960;             // bf16 keys per workgroup (16-bit keys in LDS)
 constexpr int CAP32 = 20480;             // fp32 keys per workgroup
 
@@ -64,8 +65,10 @@ CSA_DEV int block_exscan(int v, int* sh, int* total)
 // found MSB first with an 11-bit first digit (sign, exponent and the top
 // mantissa bits, so that clustered scores spread over many bins) and
 // histograms kept in four interleaved copies to cut atomic contention.
+// Keys below lo are known to lie under the threshold: the histograms skip
+// them (the caller guarantees at least kk keys >= lo).
 template <int BITS, class KT, class EmitF>
-CSA_DEV void select_top(const KT* keys, int n, int kk, EmitF emit)
+CSA_DEV void select_top(const KT* keys, int n, int kk, EmitF emit, uint32_t lo = 0u)
 {
     constexpr int COPIES = 4;
     __shared__ uint32_t hist[2048 * COPIES];
@@ -84,24 +87,34 @@ CSA_DEV void select_top(const KT* keys, int n, int kk, EmitF emit)
             __syncthreads();
             for (int i = tid; i < n; i += nt) {                 // strided: conflict-free LDS reads
                 const uint32_t k = keys[i];
-                if ((k & mask) == prefix) atomicAdd(&hist[((k >> shift) & (uint32_t)(nb - 1)) * COPIES + (tid & 3)], 1u);
+                if (k >= lo && (k & mask) == prefix) atomicAdd(&hist[((k >> shift) & (uint32_t)(nb - 1)) * COPIES + (tid & 3)], 1u);
             }
             __syncthreads();
-            // two bins per thread, from the top: bA = nb-1-2*tid, bB = bA-1
-            const int bA = nb - 1 - 2 * tid, bB = bA - 1;
-            uint32_t cA = 0, cB = 0;
-            if (bA >= 0)
-                for (int c = 0; c < COPIES; ++c) cA += hist[bA * COPIES + c];
-            if (bB >= 0)
-                for (int c = 0; c < COPIES; ++c) cB += hist[bB * COPIES + c];
+            // bpt consecutive bins per thread, from the top: thread tid owns
+            // bins nb-1-bpt*tid down to nb-bpt*(tid+1)
+            const int bpt = (nb + nt - 1) / nt;
+            const int btop = nb - 1 - bpt * tid;
+            uint32_t cnt = 0;
+            for (int j = 0; j < bpt; ++j) {
+                const int b = btop - j;
+                if (b >= 0)
+                    for (int c = 0; c < COPIES; ++c) cnt += hist[b * COPIES + c];
+            }
             int tot;
-            const uint32_t above = (uint32_t)block_exscan((int)(cA + cB), scan_sh, &tot);
-            if (bA >= 0 && above < rem && rem <= above + cA) {
-                sh_prefix = prefix | ((uint32_t)bA << shift);
-                sh_rem = rem - above;
-            } else if (bB >= 0 && above + cA < rem && rem <= above + cA + cB) {
-                sh_prefix = prefix | ((uint32_t)bB << shift);
-                sh_rem = rem - above - cA;
+            uint32_t above = (uint32_t)block_exscan((int)cnt, scan_sh, &tot);
+            if (above < rem && rem <= above + cnt) {
+                for (int j = 0; j < bpt; ++j) {
+                    const int b = btop - j;
+                    if (b < 0) break;
+                    uint32_t cb = 0;
+                    for (int c = 0; c < COPIES; ++c) cb += hist[b * COPIES + c];
+                    if (rem <= above + cb) {
+                        sh_prefix = prefix | ((uint32_t)b << shift);
+                        sh_rem = rem - above;
+                        break;
+                    }
+                    above += cb;
+                }
             }
             __syncthreads();
             prefix = sh_prefix;
@@ -217,22 +230,47 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_merge_kernel(const int32_t*
     const int n = n_chunks * k;
     const uint32_t* ck = cand_key + (size_t)row * n;
     const int32_t* ci = cand_idx + (size_t)row * n;
+    __shared__ uint32_t floor_sh;
+    if (threadIdx.x == 0) floor_sh = 0u;
     for (int i = threadIdx.x; i < n; i += blockDim.x) keys[i] = (KT)ck[i];
     __syncthreads();
+    // Each chunk holds k keys >= its smallest candidate key (a chunk with
+    // fewer valid keys is padded with key 0), so the row's k-th largest key is
+    // at least the largest of these minima: keys below it cannot be selected.
+    const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+    for (int c = threadIdx.x >> 6; c < n_chunks; c += nw) {
+        uint32_t mn = 0xFFFFFFFFu;
+        for (int i = lane; i < k; i += 64) mn = min(mn, (uint32_t)keys[c * k + i]);
+        for (int o = 32; o > 0; o >>= 1) mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
+        if (lane == 0) atomicMax(&floor_sh, mn);
+    }
+    __syncthreads();
+    const uint32_t lo = floor_sh;
+    // selected positions go to LDS first, so that the index lookups below
+    // are issued together rather than one dependent load after another
+    __shared__ int32_t spos[MAX_K];
+    select_top<BF16 ? 16 : 32>(keys, n, kk, [&](int r, int i) { spos[r] = i; }, lo);
+    __syncthreads();
     int32_t* o = out + (size_t)row * k;
-    select_top<BF16 ? 16 : 32>(keys, n, kk, [&](int r, int i) { o[r] = ci[i]; });
-    for (int r = kk + threadIdx.x; r < k; r += blockDim.x) o[r] = -1;
+    for (int r = threadIdx.x; r < k; r += blockDim.x) o[r] = r < kk ? ci[spos[r]] : -1;
 }
 
-static int chunk_for(int max_cols, bool bf16)
+// Chunk length per first-stage workgroup: at most the LDS capacity; when
+// there are few rows the chunks shrink (down to 4k keys each) so that more
+// workgroups share the work, as long as the candidates still fit one
+// second-stage workgroup.
+static int chunk_for(int n_rows, int max_cols, int k, bool bf16)
 {
     const int cap = bf16 ? CAP16 : CAP32;
-    return max_cols <= cap ? (max_cols > 0 ? max_cols : 1) : cap;
+    int chunk = max_cols <= cap ? (max_cols > 0 ? max_cols : 1) : cap;
+    auto nch = [&](int c) { return (max_cols + c - 1) / c; };
+    while ((long)n_rows * nch(chunk) < 256 && chunk / 2 >= 4 * k && (long)nch(chunk / 2) * k <= cap) chunk /= 2;
+    return chunk;
 }
 
 size_t topk_workspace(int n_rows, int max_cols, int k, bool bf16)
 {
-    const int chunk = chunk_for(max_cols, bf16);
+    const int chunk = chunk_for(n_rows, max_cols, k, bf16);
     const int n_chunks = (max_cols + chunk - 1) / chunk;
     if (n_chunks <= 1) return 0;
     return (size_t)n_rows * n_chunks * k * 8;
@@ -240,9 +278,10 @@ size_t topk_workspace(int n_rows, int max_cols, int k, bool bf16)
 
 bool topk_supported(int max_cols, int k, bool bf16)
 {
-    const int chunk = chunk_for(max_cols, bf16);
+    const int cap = bf16 ? CAP16 : CAP32;
+    const int chunk = max_cols <= cap ? max_cols : cap;
     const int n_chunks = (max_cols + chunk - 1) / chunk;
-    return n_chunks <= 1 || (long)n_chunks * k <= (bf16 ? CAP16 : CAP32);
+    return n_chunks <= 1 || (long)n_chunks * k <= cap;
 }
 
 hipError_t launch_topk(hipStream_t st, int score_bf16, int n_rows, const void* scores, int ld,
@@ -250,13 +289,14 @@ hipError_t launch_topk(hipStream_t st, int score_bf16, int n_rows, const void* s
 {
     if (n_rows <= 0) return hipSuccess;
     const bool bf = score_bf16 != 0;
-    const int chunk = chunk_for(max_cols, bf);
+    const int chunk = chunk_for(n_rows, max_cols, k, bf);
     const int n_chunks = max(1, (max_cols + chunk - 1) / chunk);
+    const int threads1 = chunk <= 8192 ? 256 : TOPK_THREADS;
     uint32_t* ck = (uint32_t*)ws;
     int32_t* ci = n_chunks > 1 ? (int32_t*)((char*)ws + (size_t)n_rows * n_chunks * k * 4) : nullptr;
     dim3 g1(n_chunks, n_rows);
-    if (bf) topk_chunk_kernel<true><<<g1, TOPK_THREADS, 0, st>>>(scores, ld, n_valid, k, chunk, n_chunks, out, ck, ci);
-    else topk_chunk_kernel<false><<<g1, TOPK_THREADS, 0, st>>>(scores, ld, n_valid, k, chunk, n_chunks, out, ck, ci);
+    if (bf) topk_chunk_kernel<true><<<g1, threads1, 0, st>>>(scores, ld, n_valid, k, chunk, n_chunks, out, ck, ci);
+    else topk_chunk_kernel<false><<<g1, threads1, 0, st>>>(scores, ld, n_valid, k, chunk, n_chunks, out, ck, ci);
     if (n_chunks > 1) {
         if (bf) topk_merge_kernel<true><<<n_rows, TOPK_THREADS, 0, st>>>(n_valid, k, n_chunks, ck, ci, out);
         else topk_merge_kernel<false><<<n_rows, TOPK_THREADS, 0, st>>>(n_valid, k, n_chunks, ck, ci, out);

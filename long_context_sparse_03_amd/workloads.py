@@ -164,6 +164,13 @@ class DecodeWorkload:
             abi.hca_attention(desc, bi.batch, n, b["q"], P["q_gamma"], st.kv, st.state, P["sinks"], b["out"],
                               b["ws_a"], stream=s)
 
+    def index_call(self, li: int):
+        """Only the index_scores call of CSA layer li (same buffers as the step)."""
+        st, _ = self.layers[li]
+        b = self.bufs[li]
+        abi.index_scores(st.desc, self.bi.batch, self.n_req, b["qI"], b["w"], st.idx, b["scores"], b["ld"],
+                         b["n_valid"])
+
     def step(self, hooks=None):
         """One decode step: every layer, then the positions advance by one."""
         for li in range(len(self.layers)):

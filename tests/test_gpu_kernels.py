@@ -119,7 +119,8 @@ def test_window_ring_rows():
 @pytest.mark.parametrize("fmt,V,k", [("bf16", [0, 5, 512, 513, 4096, 32768, 100000, 1000], 512),
                                      ("f32", [64, 63, 1, 0, 700, 70000], 64),
                                      ("bf16", [262144, 33000, 1024, 1025], 1024),
-                                     ("bf16", [3, 2000], 2048)])
+                                     ("bf16", [3, 2000], 2048),
+                                     ("bf16", [32768, 32768, 32768, 20000], 512)])
 def test_topk_exact(fmt, V, k):
     _flush(f"topk {fmt} k={k} V={V}")
     g = synth.rng(102)
