@@ -133,12 +133,26 @@ struct MmaF32 {
 
 CSA_DEV f32x4_t zero4() { f32x4_t z = {0.f, 0.f, 0.f, 0.f}; return z; }
 
-// 16-byte load as one dwordx4 (the address must be 16-byte aligned).
+// Loads from global memory.  The pointer is cast to the global address space
+// so that the load is a global (not flat) instruction even when the address
+// was read back from LDS: flat loads also count against the LDS wait
+// counter, which would make every LDS wait also wait for them.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+#define CSA_GLOBAL __attribute__((address_space(1)))
+
+// 16-byte load as one dwordx4 (the address must be 16-byte aligned).
 CSA_DEV uint4 ld16(const void* p)
 {
-    u32x4_t v = *(const u32x4_t*)p;
+    u32x4_t v = *(const CSA_GLOBAL u32x4_t*)p;
     return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// 8-byte load (8-byte aligned).
+CSA_DEV uint2 ld8(const void* p)
+{
+    u32x2_t v = *(const CSA_GLOBAL u32x2_t*)p;
+    return make_uint2(v.x, v.y);
 }
 
 CSA_DEV uint4 sel16(bool keep, uint4 v)
