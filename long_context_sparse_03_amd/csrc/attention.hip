@@ -11,18 +11,24 @@
 // Work split: a workgroup (4 waves) owns one query, a group of 16*HT heads
 // and a contiguous range of 32-row KV tiles (a split).  Rows are the query's
 // selected entries (sparse) or all visible entries (dense), then its window.
-// Each tile is gathered once into LDS for the whole workgroup:
-//   Kt [32][C]  row-major (A operand of S^T = K . Q^T),
-//   Vt [C][32]  transposed (A operand of O^T = V^T . P^T),
-// with FP8 codes expanded exactly to bf16; the per-row block scale is applied
-// to the fp32 logits of the FP8 channels and folded into P for the FP8 value
-// channels.  The four waves split the channels: wave w contracts its quarter
-// of the channels for every head of the group (so each K element is read from
-// LDS once per workgroup), the four partial logits are summed through LDS in
-// wave order, the softmax of head tile h runs on wave h, and wave w then
-// accumulates the output channels of its quarter for every head.  Online
-// softmax in base 2; splits write (max, sum, O) partials that a combine kernel
-// merges in split order, so the output does not depend on scheduling.
+//
+// Tile pipeline: while tile n computes, the rows of tile n+1 are loaded as
+// stored (FP8 entry record or bf16 / fp32 row) into registers, one row per
+// load instruction (16 contiguous bytes per lane); a tile is expanded once
+// into Kt [32][C]
+// (row-major, FP8 codes converted exactly to bf16), which serves both as the
+// A operand of S^T = K . Q^T and, through the LDS transpose read, as the A
+// operand of O^T = V^T . P^T (keys and values are the same rows).  The
+// per-row FP8 block scale is applied to the fp32 logits of the FP8 channels
+// and folded into P for the FP8 value channels.
+//
+// The four waves split the channels: wave w contracts its quarter of the
+// channels for every head of the group (each K element is read from LDS once
+// per workgroup), the partial logits are summed through LDS in wave order,
+// the softmax of head tile h runs on wave h, and wave w then accumulates the
+// output channels of its quarter for every head.  Online softmax in base 2;
+// splits write (max, sum, O) partials that a combine kernel merges in split
+// order, so the output does not depend on scheduling.
 #include <type_traits>
 
 #include "common.hpp"
@@ -43,7 +49,9 @@ struct AttnCfg {
     static constexpr int KSW = DW / MMA::K;                              // contraction steps per wave
     static constexpr int DTW = DW / 16;                                  // 16-channel output tiles per wave
     static constexpr int KP = C + (F32 ? 4 : 8);                         // Kt row stride (elements)
-    static constexpr int VP = 32 + (F32 ? 4 : 8);                        // Vt row stride (elements)
+    static constexpr int WB = C * (F32 ? 4 : 2);                         // bytes of a window row (and of a
+                                                                         // bf16 / fp32 entry)
+    static constexpr int EB = KVF == 2 ? (C - R) + 2 * R : WB;           // bytes of an entry record
     // bf16 KV with fp32 accumulation: the normalised query and the softmax
     // weights enter the bf16 MFMAs as hi + lo bf16 pairs (about 16
     // significant bits) instead of one rounded bf16 value
@@ -52,16 +60,22 @@ struct AttnCfg {
     // P^T fragments per head tile: fp32 two 16-row steps; FP8 plain + scaled
     // (value channels of FP8 entries); bf16 hi (+ lo)
     static constexpr int NPF = F32 ? 2 : (KVF == 2 ? 2 : QPARTS);
-    static constexpr int PF = C / 64;                                    // gather items per thread per tile
-    static constexpr int NV = F32 ? 2 : 1;                               // 16-byte loads per item
+    static constexpr int NCH = (C - R) / 16;                             // 16-byte chunks of FP8 codes
+    static constexpr int SLOTS = KVF == 2 ? 5 : 4;                       // partial-logit slots
     static_assert(DW % MMA::K == 0 && DW % 16 == 0, "channel split");
     static_assert(R <= DW && R % MMA::K == 0, "the rotary channels lie in the last wave's quarter");
+    static_assert(WB <= 1024, "one 64-lane 16-byte load per row");
+    static_assert(KVF != 2 || (C - R) % 16 == 0, "FP8 codes in 16-byte chunks");
 };
 
-// Column of tile row r in Vt (bf16): lane group g's P^T fragment holds the
-// rows its S^T accumulators hold, 4g..4g+3 and 16+4g..16+4g+3, as the 8
-// consecutive contraction indices 8g..8g+7.
-CSA_DEV int vt_col16(int r) { return ((r & 15) >> 2) * 8 + (r >> 4) * 4 + (r & 3); }
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// Pins an MFMA accumulator to the accumulation registers (an empty asm
+// statement with an AGPR operand), so that the register allocator keeps the
+// output accumulators there across the tile loop instead of moving them
+// through the general registers every iteration.
+CSA_DEV void keep_in_acc(f32x4_t& x) { asm("" : "+a"(x)); }
+#define CSA_LDS __attribute__((address_space(3)))
 
 template <int KVF, int C, int R, int HT>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
@@ -69,16 +83,15 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
     using Cfg = AttnCfg<KVF, C, R, HT>;
     using MMA = typename Cfg::MMA;
     using ET = typename Cfg::ET;
-    constexpr int EPF = Cfg::EPF, KP = Cfg::KP, VP = Cfg::VP, DW = Cfg::DW, KSW = Cfg::KSW, DTW = Cfg::DTW;
-    constexpr int PF = Cfg::PF, NV = Cfg::NV, NPF = Cfg::NPF;
+    constexpr int EPF = Cfg::EPF, KP = Cfg::KP, DW = Cfg::DW, KSW = Cfg::KSW, DTW = Cfg::DTW;
+    constexpr int NPF = Cfg::NPF;
     constexpr int DESC = 256;                                  // rows described at a time
     constexpr int nf = Cfg::NF;
 
     __shared__ __attribute__((aligned(16))) ET Kt[32 * KP];
-    __shared__ __attribute__((aligned(16))) ET Vt[C * VP];
     // partial logits: slot w = wave w (FP8: its non-rotary channels), slot 4 =
     // the rotary channels (FP8 only; they lie in wave 3's quarter)
-    __shared__ __attribute__((aligned(16))) f32x4_t Sbuf[KVF == 2 ? 5 : 4][HT][2][64];
+    __shared__ __attribute__((aligned(16))) f32x4_t Sbuf[Cfg::SLOTS][HT][2][64];
     __shared__ __attribute__((aligned(16))) uint4 Pbuf[HT][NPF][64];      // P^T fragments per head tile
     __shared__ float Abuf[HT][16];                             // rescale factor per head
     __shared__ float Mbuf[HT][16], Lbuf[HT][16];               // final (max, sum) per head
@@ -86,9 +99,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
     __shared__ int Rflag[HT];
     __shared__ const char* rptr[DESC];                         // row start (null: masked row)
     __shared__ float rscl[DESC];                               // fp8 block scale (1 otherwise)
+    __shared__ float tmeta[4][32];                             // loaded tiles (ring): scale, -1 = masked row
+    // normalised, rotated, scaled query fragments of each wave
+    __shared__ __attribute__((aligned(16))) uint4 qf[4][HT][KSW][Cfg::QPARTS][64];
+    __shared__ float tscl[32];                                 // the current tile's scales
+    __shared__ int tval[32];                                   // ... and valid rows
     __shared__ float rcs[R / 2], rsn[R / 2];
-    __shared__ float qg[C];
-    __shared__ int cu_sh[1025];
+    __shared__ int cu_sh[257];
 
     const int lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -98,8 +115,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
     const int dw0 = wave * DW;                                 // first channel of this wave
 
     // query fragments (B operand of S^T) of head hbase + 16*ht + li, channels
-    // dw0 + s*K + g*EPF ..; loaded first so that their latency overlaps the
-    // request lookup
+    // dw0 + s*K + g*EPF ..; loaded first, with the norm gains of the same
+    // channels, so that their latency overlaps the request lookup
     uint4 QB[HT][KSW];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
@@ -108,9 +125,14 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
 #pragma unroll
         for (int s = 0; s < KSW; ++s) QB[ht][s] = ld16(qp + (size_t)(dw0 + s * MMA::K + g * EPF) * sizeof(ET));
     }
+    uint4 GB[KSW][EPF / 4];
+#pragma unroll
+    for (int s = 0; s < KSW; ++s)
+#pragma unroll
+        for (int h = 0; h < EPF / 4; ++h) GB[s][h] = ld16(a.q_gamma + dw0 + s * MMA::K + g * EPF + 4 * h);
 
-    const int req = find_request_block(a.cu_new, a.n_req, gq, cu_sh);
-    const int t = a.start_pos[req] + (gq - (a.n_req < 1024 ? cu_sh[req] : a.cu_new[req]));
+    const int req = find_request_block(a.cu_new, a.n_req, gq, cu_sh, 256);
+    const int t = a.start_pos[req] + (gq - (a.n_req < 256 ? cu_sh[req] : a.cu_new[req]));
     const bool dense = a.sel == nullptr;
     const int V = (t + 1) / a.m;
     const int K0 = dense ? V : a.k;                            // entry slots before the window
@@ -147,76 +169,57 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
             rscl[j] = sc;
         }
     };
-    // ---- gather of one tile: PF items (8 channels of one row) per thread,
-    //      rows fastest.  Loads are branch-free so that they stay in flight
-    //      together: masked rows read a valid dummy address and are zeroed
-    //      when stored (not when loaded, so that a prefetch is not waited for
-    //      early); an FP8 channel chunk is 8 bytes, every other chunk 16.
+    // ---- loads of one tile into registers: wave w loads rows w, w+4, ..,
+    //      w+28, one row per instruction, lane l the row's bytes 16l..16l+15
+    //      (clamped to the row, so the loads are branch-free; masked rows
+    //      read a valid dummy row)
     const char* dummy = (const char*)a.kv;
-    auto load_tile = [&](int tile, int drow0, uint4 (&raw)[PF][NV]) {
+    auto load_tile = [&](int tile, int drow0, uint4 (&raw)[8]) {
         const int slot0 = tile * 32;
+        if (threadIdx.x < 32)
+            tmeta[tile & 3][threadIdx.x] = rptr[drow0 + threadIdx.x] != nullptr ? rscl[drow0 + threadIdx.x] : -1.0f;
 #pragma unroll
-        for (int u = 0; u < PF; ++u) {
-            const int idx = threadIdx.x + u * 256;
-            const int row = idx & 31, d0 = (idx >> 5) * 8;
+        for (int j = 0; j < 8; ++j) {
+            const int row = wave + 4 * j;
             const char* p = rptr[drow0 + row];
-            const char* base = p != nullptr ? p : dummy;
-            if constexpr (KVF == 2) {
-                const bool entry = slot0 + row < K0;
-                const char* a0 = entry ? (d0 < nf ? base + d0 : base + nf + 2 * (size_t)(d0 - nf)) : base + 2 * (size_t)d0;
-                const char* a1 = (entry && d0 < nf) ? a0 : a0 + 8;
-                const uint2 lo = ld8(a0), hi = ld8(a1);
-                raw[u][0] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            } else if constexpr (KVF == 1) {
-                raw[u][0] = ld16(base + 2 * (size_t)d0);
-            } else {
-                raw[u][0] = ld16(base + 4 * (size_t)d0);
-                raw[u][NV - 1] = ld16(base + 4 * (size_t)d0 + 16);
-            }
+            const int bytes = (slot0 + row < K0) ? Cfg::EB : Cfg::WB;
+            raw[j] = ld16((p != nullptr ? p : dummy) + min(lane * 16, bytes - 16));
         }
     };
-    auto store_tile = [&](int tile, int drow0, uint4 (&raw)[PF][NV]) {
+    // ---- expand a loaded tile into Kt (masked rows become zeros) and keep
+    //      its row flags and scales
+    auto store_tile = [&](int tile, const uint4 (&raw)[8]) {
         const int slot0 = tile * 32;
+        if (threadIdx.x < 32) {
+            const float m = tmeta[tile & 3][threadIdx.x];
+            tval[threadIdx.x] = m >= 0.f;
+            tscl[threadIdx.x] = m >= 0.f ? m : 1.0f;
+        }
 #pragma unroll
-        for (int u = 0; u < PF; ++u) {
-            const int idx = threadIdx.x + u * 256;
-            const int row = idx & 31, d0 = (idx >> 5) * 8;
-            const bool entry = slot0 + row < K0;
-            const bool ok = rptr[drow0 + row] != nullptr;
-            ET* kr = Kt + row * KP + d0;
-            if constexpr (Cfg::F32) {
-                const uint4 v0 = sel16(ok, raw[u][0]), v1 = sel16(ok, raw[u][NV - 1]);
-                *(uint4*)kr = v0;
-                *(uint4*)(kr + 4) = v1;
-                const uint32_t f4[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-                for (int j = 0; j < 8; ++j) Vt[(d0 + j) * VP + row] = __uint_as_float(f4[j]);
-            } else {
-                uint4 b;
-                if (KVF == 2 && entry && d0 < nf) {
-                    const uint2 b0 = e4m3x4_to_bf16x4(raw[u][0].x), b1 = e4m3x4_to_bf16x4(raw[u][0].y);
-                    b = make_uint4(b0.x, b0.y, b1.x, b1.y);
-                } else {
-                    b = raw[u][0];
+        for (int j = 0; j < 8; ++j) {
+            const int row = wave + 4 * j;
+            const bool ok = tmeta[tile & 3][row] >= 0.f;
+            const uint4 v = sel16(ok, raw[j]);
+            ET* kr = Kt + row * KP;
+            if (KVF == 2 && slot0 + row < K0) {
+                // FP8 record: 16 codes per lane, then the bf16 rotary channels
+                if (lane < Cfg::NCH) {
+                    const uint2 b0 = e4m3x4_to_bf16x4(v.x), b1 = e4m3x4_to_bf16x4(v.y);
+                    const uint2 b2 = e4m3x4_to_bf16x4(v.z), b3 = e4m3x4_to_bf16x4(v.w);
+                    *(uint4*)(kr + 16 * lane) = make_uint4(b0.x, b0.y, b1.x, b1.y);
+                    *(uint4*)(kr + 16 * lane + 8) = make_uint4(b2.x, b2.y, b3.x, b3.y);
+                } else if (lane < Cfg::NCH + R / 8) {
+                    *(uint4*)(kr + nf + 8 * (lane - Cfg::NCH)) = v;
                 }
-                b = sel16(ok, b);
-                *(uint4*)kr = b;
-                const int col = vt_col16(row);
-                const uint32_t w4[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    Vt[(d0 + 2 * h) * VP + col] = (uint16_t)(w4[h] & 0xFFFF);
-                    Vt[(d0 + 2 * h + 1) * VP + col] = (uint16_t)(w4[h] >> 16);
-                }
+            } else if (lane * 16 < Cfg::WB) {
+                *(uint4*)(kr + lane * EPF) = v;                // 8 bf16 or 4 fp32 channels
             }
         }
     };
 
-    // ---- prologue: RoPE table at +t, query gains, first descriptors, and the
-    //      partial sums of squares of the query heads over this wave's channels
+    // ---- prologue: RoPE table at +t, the first descriptors and the partial
+    //      sums of squares of the query heads over this wave's channels
     for (int j = threadIdx.x; j < R / 2; j += 256) rope_cs((double)t, j, R, a.theta, &rcs[j], &rsn[j]);
-    for (int j = threadIdx.x; j < C; j += 256) qg[j] = a.q_gamma[j];
-    if (tile0 < tile1) describe(tile0 * 32);
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
         float ss = 0.f;
@@ -238,12 +241,14 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
         ss += __shfl_xor(ss, 32, 64);
         if (g == 0) SSbuf[wave][ht][li] = ss;
     }
-    __syncthreads();                                           // table, gains, descriptors, sums ready
-    uint4 raw[PF][NV];
-    if (tile0 < tile1) load_tile(tile0, 0, raw);               // in flight while the query is prepared
+    if (tile0 < tile1) describe(tile0 * 32);
+    __syncthreads();                                           // prologue: table, descriptors, sums ready
+    // the first tile's loads are in flight while the query is prepared
+    uint4 raw[8];
+    if (tile0 < tile1) load_tile(tile0, 0, raw);
 
-    // normalised, rotated, scaled query fragments (registers)
-    uint4 QF[HT][KSW][Cfg::QPARTS];
+    // normalised, rotated, scaled query fragments; each lane writes and later
+    // reads only its own, so no barrier is needed
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
         const float ssum = ((SSbuf[0][ht][li] + SSbuf[1][ht][li]) + SSbuf[2][ht][li]) + SSbuf[3][ht][li];
@@ -252,6 +257,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
         for (int s = 0; s < KSW; ++s) {
             const int d0 = dw0 + s * MMA::K + g * EPF;
             const uint32_t w4[4] = {QB[ht][s].x, QB[ht][s].y, QB[ht][s].z, QB[ht][s].w};
+            const float* gm = (const float*)&GB[s][0];
             float x[EPF];
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
@@ -263,7 +269,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
                 }
             }
 #pragma unroll
-            for (int j = 0; j < EPF; ++j) x[j] = qg[d0 + j] * (x[j] * inv);
+            for (int j = 0; j < EPF; ++j) x[j] = gm[j] * (x[j] * inv);
             if (d0 >= nf) {
 #pragma unroll
                 for (int j = 0; j < EPF; j += 2) {
@@ -274,8 +280,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
                 }
             }
             if constexpr (Cfg::F32) {
-                QF[ht][s][0] = make_uint4(__float_as_uint(x[0] * a.scale_log2), __float_as_uint(x[1] * a.scale_log2),
-                                          __float_as_uint(x[2] * a.scale_log2), __float_as_uint(x[3] * a.scale_log2));
+                qf[wave][ht][s][0][lane] = make_uint4(__float_as_uint(x[0] * a.scale_log2), __float_as_uint(x[1] * a.scale_log2),
+                                                      __float_as_uint(x[2] * a.scale_log2), __float_as_uint(x[3] * a.scale_log2));
             } else {
                 uint32_t w[4], wl[4];
 #pragma unroll
@@ -284,8 +290,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
                     w[h] = pack_bf16x2(v0, v1);
                     wl[h] = pack_bf16x2(v0 - bf16_to_f32(w[h] & 0xFFFF), v1 - bf16_to_f32(w[h] >> 16));
                 }
-                QF[ht][s][0] = make_uint4(w[0], w[1], w[2], w[3]);
-                if constexpr (Cfg::SPLIT) QF[ht][s][Cfg::QPARTS - 1] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+                qf[wave][ht][s][0][lane] = make_uint4(w[0], w[1], w[2], w[3]);
+                if constexpr (Cfg::SPLIT) qf[wave][ht][s][Cfg::QPARTS - 1][lane] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
             }
         }
     }
@@ -303,13 +309,19 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
     bool raise_loc = false;
 
     for (int tile = tile0; tile < tile1; ++tile) {
-        const int drow0 = ((tile - tile0) * 32) % DESC;
         const int slot0 = tile * 32;
-        store_tile(tile, drow0, raw);
-        __syncthreads();                                       // (A) tile in LDS
-        // prefetch the next tile while this one computes
-        const bool next_same_window = tile + 1 < tile1 && drow0 + 32 < DESC;
-        if (next_same_window) load_tile(tile + 1, drow0 + 32, raw);
+        __syncthreads();                                       // the previous tile is done with Kt
+        store_tile(tile, raw);
+        __syncthreads();                                       // (A) tile in Kt
+        // load the next tile while this one computes
+        if (tile + 1 < tile1) {
+            const int drow = ((tile + 1 - tile0) * 32) % DESC;
+            if (drow == 0) {                                   // the next DESC rows
+                describe((tile + 1) * 32);
+                __syncthreads();
+            }
+            load_tile(tile + 1, drow, raw);
+        }
 
         // ---- partial S^T over this wave's channels, rows 16*rt + li of the tile.
         //      FP8: the non-rotary part goes to slot `wave`, the rotary part
@@ -333,8 +345,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
             for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
                 for (int part = 0; part < Cfg::QPARTS; ++part) {
-                    acc[ht][0] = MMA::step(ka, QF[ht][s][part], acc[ht][0]);
-                    acc[ht][1] = MMA::step(kb, QF[ht][s][part], acc[ht][1]);
+                    const uint4 qb = qf[wave][ht][s][part][lane];
+                    acc[ht][0] = MMA::step(ka, qb, acc[ht][0]);
+                    acc[ht][1] = MMA::step(kb, qb, acc[ht][1]);
                 }
         }
         {
@@ -359,7 +372,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) rsc[rt][i] = KVF == 2 ? rscl[drow0 + 16 * rt + 4 * g + i] : 1.f;
+            for (int i = 0; i < 4; ++i) rsc[rt][i] = KVF == 2 ? tscl[16 * rt + 4 * g + i] : 1.f;
         __syncthreads();                                       // (B) partial logits in LDS
 
         // ---- softmax of head tile hs: sum the partials in wave order
@@ -370,13 +383,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
                 f32x4_t v = ((Sbuf[0][hs][rt][lane] + Sbuf[1][hs][rt][lane]) + Sbuf[2][hs][rt][lane]) +
                             Sbuf[3][hs][rt][lane];
                 if constexpr (KVF == 2) {
-                    const f32x4_t vr = Sbuf[KVF == 2 ? 4 : 0][hs][rt][lane];
+                    const f32x4_t vr = Sbuf[Cfg::SLOTS - 1][hs][rt][lane];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) v[i] = rsc[rt][i] * v[i] + vr[i];
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const bool valid = rptr[drow0 + 16 * rt + 4 * g + i] != nullptr;
+                    const bool valid = tval[16 * rt + 4 * g + i] != 0;
                     sv[4 * rt + i] = valid ? v[i] : -INFINITY;
                 }
             }
@@ -390,12 +403,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
             // are rescaled rarely; the final normalisation uses the same
             // reference.
             const bool raise = mx > m_run + 8.0f;
+            const bool rescale = raise && m_run != -INFINITY;   // nothing accumulated yet otherwise
             const float m_new = raise ? mx : m_run;
             const float m_use = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = raise ? exp2f(m_run - m_use) : 1.0f;
+            const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.0f;
             float p[8], ps = 0.f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) { p[i] = exp2f(sv[i] - m_use); ps += p[i]; }
+            for (int i = 0; i < 8; ++i) { p[i] = __builtin_amdgcn_exp2f(sv[i] - m_use); ps += p[i]; }
             ps += __shfl_xor(ps, 16, 64);
             ps += __shfl_xor(ps, 32, 64);
             l_run = l_run * alpha + ps;
@@ -430,19 +444,22 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
 #pragma unroll
                 for (int v = 0; v < NPF; ++v) Ploc[v] = pf[v];
                 alpha_loc = alpha;
-                raise_loc = __any(raise);
+                raise_loc = __any(rescale);
             } else {
 #pragma unroll
                 for (int v = 0; v < NPF; ++v) Pbuf[hs][v][lane] = pf[v];
                 if (g == 0) Abuf[hs][li] = alpha;
-                const bool any_raise = __any(raise);
-                if (lane == 0) Rflag[hs] = any_raise;
+                const bool any_rescale = __any(rescale);
+                if (lane == 0) Rflag[hs] = any_rescale;
             }
         }
         if constexpr (HT > 1) __syncthreads();                 // (C) P^T and rescale factors in LDS
 
-        // ---- O^T += V^T . P^T for this wave's channels and every head tile
-        //      (each V^T fragment is read once and used for all head tiles)
+        // ---- O^T += V^T . P^T for this wave's channels and every head tile.
+        //      The V^T fragment of lane (li, g) holds channel c0 + li of rows
+        //      4g..4g+3 and 16+4g..16+4g+3 (contraction order 8g..8g+7), read
+        //      from the row-major tile with two LDS transpose reads; it is
+        //      read once and used for all head tiles.
         uint4 pf[HT][NPF];
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
@@ -464,33 +481,50 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
                 for (int dt = 0; dt < DTW; ++dt) O[ht][dt] *= al;
             }
         }
+        // P^T fragment for output tile dt: FP8 non-rotary channels take the
+        // scaled weights.  Only the last wave's quarter holds rotary channels,
+        // so the choice is made at compile time per (kind of wave, dt).
+        auto pv_all = [&](auto mode) {
+            constexpr int MODE = decltype(mode)::value;        // 0: not FP8, 1: scaled, 2: last wave
 #pragma unroll
-        for (int dt = 0; dt < DTW; ++dt) {
-            const int c0 = dw0 + 16 * dt;
-            const ET* vr = Vt + (c0 + li) * VP;
-            if constexpr (Cfg::F32) {
-                const uint4 va = *(const uint4*)(vr + 4 * g), vb = *(const uint4*)(vr + 16 + 4 * g);
+            for (int dt = 0; dt < DTW; ++dt) {
+                const int c0 = dw0 + 16 * dt;
+                if constexpr (Cfg::F32) {
+                    float va[4], vb[4];
 #pragma unroll
-                for (int ht = 0; ht < HT; ++ht) {
-                    O[ht][dt] = MMA::step(va, pf[ht][0], O[ht][dt]);
-                    O[ht][dt] = MMA::step(vb, pf[ht][1], O[ht][dt]);
-                }
-            } else {
-                const uint4 va = *(const uint4*)(vr + 8 * g);
-                const int pv = (KVF == 2 && c0 < nf) ? 1 : 0;   // wave-uniform
+                    for (int j = 0; j < 4; ++j) {
+                        va[j] = Kt[(4 * g + j) * KP + c0 + li];
+                        vb[j] = Kt[(16 + 4 * g + j) * KP + c0 + li];
+                    }
+                    const uint4 fa = make_uint4(__float_as_uint(va[0]), __float_as_uint(va[1]), __float_as_uint(va[2]), __float_as_uint(va[3]));
+                    const uint4 fb = make_uint4(__float_as_uint(vb[0]), __float_as_uint(vb[1]), __float_as_uint(vb[2]), __float_as_uint(vb[3]));
 #pragma unroll
-                for (int ht = 0; ht < HT; ++ht) {
-                    O[ht][dt] = MMA::step(va, pv ? pf[ht][NPF - 1] : pf[ht][0], O[ht][dt]);
-                    if constexpr (Cfg::SPLIT) O[ht][dt] = MMA::step(va, pf[ht][NPF - 1], O[ht][dt]);
+                    for (int ht = 0; ht < HT; ++ht) {
+                        O[ht][dt] = MMA::step(fa, pf[ht][0], O[ht][dt]);
+                        O[ht][dt] = MMA::step(fb, pf[ht][1], O[ht][dt]);
+                    }
+                } else {
+                    // lane m of a 16-lane group points at 4 channels of one row:
+                    // row 4g + m/4 (+16 for the second read), channels c0 + 4*(m%4)
+                    const ET* base = Kt + (4 * g + (li >> 2)) * KP + c0 + 4 * (li & 3);
+                    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS s16x4_t*)base);
+                    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS s16x4_t*)(base + 16 * KP));
+                    const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+                    const uint4 va = make_uint4(l2.x, l2.y, h2.x, h2.y);
+                    const bool scaled_last = 3 * DW + 16 * dt < nf;   // constant once unrolled
+                    const int v = KVF != 2 ? 0 : (MODE == 1 ? 1 : (MODE == 2 && scaled_last ? 1 : 0));
+#pragma unroll
+                    for (int ht = 0; ht < HT; ++ht) {
+                        O[ht][dt] = MMA::step(va, pf[ht][v], O[ht][dt]);
+                        if constexpr (Cfg::SPLIT) O[ht][dt] = MMA::step(va, pf[ht][NPF - 1], O[ht][dt]);
+                        keep_in_acc(O[ht][dt]);
+                    }
                 }
             }
-        }
-        __syncthreads();                                       // (D) Kt, Vt, Sbuf, Pbuf, rptr are rewritten next
-        if (tile + 1 < tile1 && !next_same_window) {
-            describe((tile + 1) * 32);
-            __syncthreads();
-            load_tile(tile + 1, 0, raw);
-        }
+        };
+        if constexpr (KVF != 2) pv_all(std::integral_constant<int, 0>());
+        else if (dw0 + DW <= nf) pv_all(std::integral_constant<int, 1>());
+        else pv_all(std::integral_constant<int, 2>());
     }
 
     // ---- per-head (max, sum) of every head tile

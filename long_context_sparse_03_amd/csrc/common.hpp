@@ -25,9 +25,14 @@ CSA_DEV uint16_t f32_to_bf16(float x)
     return (uint16_t)(u >> 16);
 }
 
+// Two floats to bf16 (round to nearest even) in one dword, low half first;
+// one hardware conversion.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 CSA_DEV uint32_t pack_bf16x2(float a, float b)
 {
-    return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // OCP E4M3FN -> fp32 (exact).  0x7F/0xFF (NaN) never occur in stored data.
@@ -229,11 +234,12 @@ CSA_DEV void rope_cs(double pos, int j, int r, float theta, float* cs, float* sn
 }
 
 // Request of global token row g, found by all threads of the block together:
-// cu_new is staged in LDS (sh, >= n_req + 1 ints when n_req < 1024), then
-// searched there.  Every thread of the block must call it.
-CSA_DEV int find_request_block(const int32_t* cu_new, int n_req, int g, int* sh)
+// cu_new is staged in LDS (sh, >= n_req + 1 ints when n_req < cap), then
+// searched there (in global memory otherwise).  Every thread of the block
+// must call it.
+CSA_DEV int find_request_block(const int32_t* cu_new, int n_req, int g, int* sh, int cap = 1024)
 {
-    if (n_req >= 1024) return find_request(cu_new, n_req, g);
+    if (n_req >= cap) return find_request(cu_new, n_req, g);
     for (int i = threadIdx.x; i <= n_req; i += blockDim.x) sh[i] = cu_new[i];
     __syncthreads();
     int lo = 0, hi = n_req - 1;
