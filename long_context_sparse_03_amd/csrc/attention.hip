@@ -8,27 +8,29 @@
 // uncompressed window, and the sink logit that only enters the softmax
 // denominator); yunpan.plus explainer eq. (9).
 //
-// Work split: a workgroup (4 waves) owns one query, a group of 16*HT heads
-// and a contiguous range of 32-row KV tiles (a split).  Rows are the query's
-// selected entries (sparse) or all visible entries (dense), then its window.
+// Work split: a workgroup of NW waves (8 for c >= 256, two per SIMD, else 4)
+// owns one query, a group of 16*HT heads and a contiguous range of 32-row KV
+// tiles (a split).  Rows are the query's selected entries (sparse) or all
+// visible entries (dense), then its window.
 //
 // Tile pipeline: while tile n computes, the rows of tile n+1 are loaded as
 // stored (FP8 entry record or bf16 / fp32 row) into registers, one row per
-// load instruction (16 contiguous bytes per lane); a tile is expanded once
-// into Kt [32][C]
-// (row-major, FP8 codes converted exactly to bf16), which serves both as the
-// A operand of S^T = K . Q^T and, through the LDS transpose read, as the A
-// operand of O^T = V^T . P^T (keys and values are the same rows).  The
-// per-row FP8 block scale is applied to the fp32 logits of the FP8 channels
-// and folded into P for the FP8 value channels.
+// load instruction (16 contiguous bytes per lane), with the FP8 block scale
+// of each row; a tile is expanded once into Kt [32][C] (row-major, FP8 codes
+// converted exactly to bf16), which serves both as the A operand of
+// S^T = K . Q^T and, through the LDS transpose read, as the A operand of
+// O^T = V^T . P^T (keys and values are the same rows).  The per-row FP8 block
+// scale is applied to the fp32 logits of the FP8 channels and folded into P
+// for the FP8 value channels.
 //
-// The four waves split the channels: wave w contracts its quarter of the
-// channels for every head of the group (each K element is read from LDS once
-// per workgroup), the partial logits are summed through LDS in wave order,
-// the softmax of head tile h runs on wave h, and wave w then accumulates the
-// output channels of its quarter for every head.  Online softmax in base 2;
-// splits write (max, sum, O) partials that a combine kernel merges in split
-// order, so the output does not depend on scheduling.
+// The waves split the channels: wave w contracts its C/NW channels for every
+// head of the group (each K element is read from LDS once per workgroup), the
+// partial logits are summed through LDS in wave order, the softmax of head
+// tile h runs on wave h, and wave w then accumulates the output channels of
+// its slice for every head.  The rotary channels fill whole waves' slices, so
+// each wave's logits are either all FP8-scaled or all not.  Online softmax in
+// base 2; splits write (max, sum, O) partials that a combine kernel merges in
+// split order, so the output does not depend on scheduling.
 #include <type_traits>
 
 #include "common.hpp"
@@ -45,13 +47,18 @@ struct AttnCfg {
     using MMA = typename std::conditional<F32, MmaF32, MmaBF16>::type;
     using ET = typename std::conditional<F32, float, uint16_t>::type;   // LDS element type
     static constexpr int EPF = 16 / sizeof(ET);                          // elements per fragment
-    static constexpr int DW = C / 4;                                     // channels per wave
+    static constexpr int NW = C >= 256 ? 8 : 4;                          // waves
+    static constexpr int NT = 64 * NW;                                   // threads
+    static constexpr int DW = C / NW;                                    // channels per wave
     static constexpr int KSW = DW / MMA::K;                              // contraction steps per wave
     static constexpr int DTW = DW / 16;                                  // 16-channel output tiles per wave
+    static constexpr int NNW = NF / DW;                                  // waves holding non-rotary channels
+    static constexpr int RPW = 32 / NW;                                  // tile rows loaded per wave
     static constexpr int KP = C + (F32 ? 4 : 8);                         // Kt row stride (elements)
     static constexpr int WB = C * (F32 ? 4 : 2);                         // bytes of a window row (and of a
                                                                          // bf16 / fp32 entry)
-    static constexpr int EB = KVF == 2 ? (C - R) + 2 * R : WB;           // bytes of an entry record
+    static constexpr int EB = KVF == 2 ? NF + 2 * R : WB;                // bytes of an entry record
+    static constexpr int NCH = NF / 16;                                  // 16-byte chunks of FP8 codes
     // bf16 KV with fp32 accumulation: the normalised query and the softmax
     // weights enter the bf16 MFMAs as hi + lo bf16 pairs (about 16
     // significant bits) instead of one rounded bf16 value
@@ -60,48 +67,36 @@ struct AttnCfg {
     // P^T fragments per head tile: fp32 two 16-row steps; FP8 plain + scaled
     // (value channels of FP8 entries); bf16 hi (+ lo)
     static constexpr int NPF = F32 ? 2 : (KVF == 2 ? 2 : QPARTS);
-    static constexpr int NCH = (C - R) / 16;                             // 16-byte chunks of FP8 codes
-    static constexpr int SLOTS = KVF == 2 ? 5 : 4;                       // partial-logit slots
-    static_assert(DW % MMA::K == 0 && DW % 16 == 0, "channel split");
-    static_assert(R <= DW && R % MMA::K == 0, "the rotary channels lie in the last wave's quarter");
+    static_assert(KSW >= 1 && DW % MMA::K == 0 && DW % 16 == 0, "channel split");
+    static_assert(NF % DW == 0, "the rotary channels fill whole waves' slices");
     static_assert(WB <= 1024, "one 64-lane 16-byte load per row");
-    static_assert(KVF != 2 || (C - R) % 16 == 0, "FP8 codes in 16-byte chunks");
+    static_assert(KVF != 2 || NF % 16 == 0, "FP8 codes in 16-byte chunks");
+    static_assert(HT <= NW, "one softmax wave per head tile");
 };
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
-
-// Pins an MFMA accumulator to the accumulation registers (an empty asm
-// statement with an AGPR operand), so that the register allocator keeps the
-// output accumulators there across the tile loop instead of moving them
-// through the general registers every iteration.
-CSA_DEV void keep_in_acc(f32x4_t& x) { asm("" : "+a"(x)); }
 #define CSA_LDS __attribute__((address_space(3)))
 
 template <int KVF, int C, int R, int HT>
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
+__global__ __launch_bounds__((AttnCfg<KVF, C, R, HT>::NT)) void attn_kernel(AttnArgs a)
 {
     using Cfg = AttnCfg<KVF, C, R, HT>;
     using MMA = typename Cfg::MMA;
     using ET = typename Cfg::ET;
     constexpr int EPF = Cfg::EPF, KP = Cfg::KP, DW = Cfg::DW, KSW = Cfg::KSW, DTW = Cfg::DTW;
-    constexpr int NPF = Cfg::NPF;
+    constexpr int NW = Cfg::NW, NT = Cfg::NT, RPW = Cfg::RPW, NPF = Cfg::NPF, NNW = Cfg::NNW;
     constexpr int DESC = 256;                                  // rows described at a time
     constexpr int nf = Cfg::NF;
 
     __shared__ __attribute__((aligned(16))) ET Kt[32 * KP];
-    // partial logits: slot w = wave w (FP8: its non-rotary channels), slot 4 =
-    // the rotary channels (FP8 only; they lie in wave 3's quarter)
-    __shared__ __attribute__((aligned(16))) f32x4_t Sbuf[Cfg::SLOTS][HT][2][64];
+    __shared__ __attribute__((aligned(16))) f32x4_t Sbuf[NW][HT][2][64];  // partial logits per wave
     __shared__ __attribute__((aligned(16))) uint4 Pbuf[HT][NPF][64];      // P^T fragments per head tile
     __shared__ float Abuf[HT][16];                             // rescale factor per head
     __shared__ float Mbuf[HT][16], Lbuf[HT][16];               // final (max, sum) per head
-    __shared__ float SSbuf[4][HT][16];                         // partial sums of squares of the query heads
+    __shared__ float SSbuf[NW][HT][16];                        // partial sums of squares of the query heads
     __shared__ int Rflag[HT];
     __shared__ const char* rptr[DESC];                         // row start (null: masked row)
-    __shared__ float rscl[DESC];                               // fp8 block scale (1 otherwise)
-    __shared__ float tmeta[4][32];                             // loaded tiles (ring): scale, -1 = masked row
-    // normalised, rotated, scaled query fragments of each wave
-    __shared__ __attribute__((aligned(16))) uint4 qf[4][HT][KSW][Cfg::QPARTS][64];
+    __shared__ const char* rblk[DESC];                         // FP8 entry rows: their block (scale at byte 0)
     __shared__ float tscl[32];                                 // the current tile's scales
     __shared__ int tval[32];                                   // ... and valid rows
     __shared__ float rcs[R / 2], rsn[R / 2];
@@ -148,60 +143,63 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
     const size_t hdr = KVF == 2 ? 64 : 0;
     const char* ring = (const char*)a.state + (size_t)req * a.state_stride;
 
-    // ---- row descriptors: source pointer and scale of DESC consecutive slots
+    // ---- row descriptors of DESC consecutive slots: row start and (FP8
+    //      entries) the block whose header holds the scale
     auto describe = [&](int first_slot) {
-        for (int j = threadIdx.x; j < DESC; j += 256) {
+        for (int j = threadIdx.x; j < DESC; j += NT) {
             const int slot = first_slot + j;
             const char* p = nullptr;
-            float sc = 1.0f;
+            const char* blk = nullptr;
             if (slot < K0) {
                 const int e = dense ? slot : a.sel[(size_t)gq * a.k + slot];
                 if (e >= 0 && e < V) {
                     const int phys = a.block_table[(size_t)req * a.max_blocks + (e >> a.epb_log2)];
-                    const char* blk = (const char*)a.kv + (size_t)phys * a.kv_block_bytes;
-                    p = blk + hdr + (size_t)(e & (a.epb - 1)) * rec;
-                    if (KVF == 2) sc = *(const float*)blk;
+                    const char* b = (const char*)a.kv + (size_t)phys * a.kv_block_bytes;
+                    p = b + hdr + (size_t)(e & (a.epb - 1)) * rec;
+                    if (KVF == 2) blk = b;
                 }
             } else if (slot < n_slots && slot - K0 < nwr) {
                 p = ring + (size_t)((w0 + slot - K0) % a.win_cap) * C * win_es;
             }
             rptr[j] = p;
-            rscl[j] = sc;
+            rblk[j] = blk;
         }
     };
-    // ---- loads of one tile into registers: wave w loads rows w, w+4, ..,
-    //      w+28, one row per instruction, lane l the row's bytes 16l..16l+15
+    // ---- loads of one tile into registers: wave w loads rows w, w+NW, ..,
+    //      one row per instruction, lane l the row's bytes 16l..16l+15
     //      (clamped to the row, so the loads are branch-free; masked rows
-    //      read a valid dummy row)
+    //      read a valid dummy row), and each FP8 entry row's block scale
     const char* dummy = (const char*)a.kv;
-    auto load_tile = [&](int tile, int drow0, uint4 (&raw)[8]) {
+    auto load_tile = [&](int tile, int drow0, uint4 (&raw)[RPW], float (&rsr)[RPW]) {
         const int slot0 = tile * 32;
-        if (threadIdx.x < 32)
-            tmeta[tile & 3][threadIdx.x] = rptr[drow0 + threadIdx.x] != nullptr ? rscl[drow0 + threadIdx.x] : -1.0f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int row = wave + 4 * j;
+        for (int j = 0; j < RPW; ++j) {
+            const int row = wave + NW * j;
             const char* p = rptr[drow0 + row];
             const int bytes = (slot0 + row < K0) ? Cfg::EB : Cfg::WB;
             raw[j] = ld16((p != nullptr ? p : dummy) + min(lane * 16, bytes - 16));
+            if constexpr (KVF == 2) {
+                const char* b = rblk[drow0 + row];
+                rsr[j] = *(const CSA_GLOBAL float*)(b != nullptr ? b : dummy);
+            }
         }
     };
     // ---- expand a loaded tile into Kt (masked rows become zeros) and keep
     //      its row flags and scales
-    auto store_tile = [&](int tile, const uint4 (&raw)[8]) {
+    auto store_tile = [&](int tile, int drow0, const uint4 (&raw)[RPW], const float (&rsr)[RPW]) {
         const int slot0 = tile * 32;
-        if (threadIdx.x < 32) {
-            const float m = tmeta[tile & 3][threadIdx.x];
-            tval[threadIdx.x] = m >= 0.f;
-            tscl[threadIdx.x] = m >= 0.f ? m : 1.0f;
-        }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int row = wave + 4 * j;
-            const bool ok = tmeta[tile & 3][row] >= 0.f;
+        for (int j = 0; j < RPW; ++j) {
+            const int row = wave + NW * j;
+            const bool ok = rptr[drow0 + row] != nullptr;
+            const bool entry = slot0 + row < K0;
+            if (lane == 0) {
+                tval[row] = ok;
+                tscl[row] = (KVF == 2 && ok && entry) ? rsr[j] : 1.0f;
+            }
             const uint4 v = sel16(ok, raw[j]);
             ET* kr = Kt + row * KP;
-            if (KVF == 2 && slot0 + row < K0) {
+            if (KVF == 2 && entry) {
                 // FP8 record: 16 codes per lane, then the bf16 rotary channels
                 if (lane < Cfg::NCH) {
                     const uint2 b0 = e4m3x4_to_bf16x4(v.x), b1 = e4m3x4_to_bf16x4(v.y);
@@ -219,7 +217,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
 
     // ---- prologue: RoPE table at +t, the first descriptors and the partial
     //      sums of squares of the query heads over this wave's channels
-    for (int j = threadIdx.x; j < R / 2; j += 256) rope_cs((double)t, j, R, a.theta, &rcs[j], &rsn[j]);
+    for (int j = threadIdx.x; j < R / 2; j += NT) rope_cs_f((double)t, a.inv_freq[j], &rcs[j], &rsn[j]);
+    if (tile0 < tile1) describe(tile0 * 32);
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
         float ss = 0.f;
@@ -241,17 +240,19 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
         ss += __shfl_xor(ss, 32, 64);
         if (g == 0) SSbuf[wave][ht][li] = ss;
     }
-    if (tile0 < tile1) describe(tile0 * 32);
     __syncthreads();                                           // prologue: table, descriptors, sums ready
     // the first tile's loads are in flight while the query is prepared
-    uint4 raw[8];
-    if (tile0 < tile1) load_tile(tile0, 0, raw);
+    uint4 raw[RPW];
+    float rsr[RPW];
+    if (tile0 < tile1) load_tile(tile0, 0, raw, rsr);
 
-    // normalised, rotated, scaled query fragments; each lane writes and later
-    // reads only its own, so no barrier is needed
+    // normalised, rotated, scaled query fragments (registers)
+    uint4 QF[HT][KSW][Cfg::QPARTS];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-        const float ssum = ((SSbuf[0][ht][li] + SSbuf[1][ht][li]) + SSbuf[2][ht][li]) + SSbuf[3][ht][li];
+        float ssum = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) ssum += SSbuf[w][ht][li];
         const float inv = (hbase + 16 * ht + li < a.nh) ? 1.0f / sqrtf(ssum / (float)C + a.eps) : 0.f;
 #pragma unroll
         for (int s = 0; s < KSW; ++s) {
@@ -280,8 +281,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
                 }
             }
             if constexpr (Cfg::F32) {
-                qf[wave][ht][s][0][lane] = make_uint4(__float_as_uint(x[0] * a.scale_log2), __float_as_uint(x[1] * a.scale_log2),
-                                                      __float_as_uint(x[2] * a.scale_log2), __float_as_uint(x[3] * a.scale_log2));
+                QF[ht][s][0] = make_uint4(__float_as_uint(x[0] * a.scale_log2), __float_as_uint(x[1] * a.scale_log2),
+                                          __float_as_uint(x[2] * a.scale_log2), __float_as_uint(x[3] * a.scale_log2));
             } else {
                 uint32_t w[4], wl[4];
 #pragma unroll
@@ -290,8 +291,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
                     w[h] = pack_bf16x2(v0, v1);
                     wl[h] = pack_bf16x2(v0 - bf16_to_f32(w[h] & 0xFFFF), v1 - bf16_to_f32(w[h] >> 16));
                 }
-                qf[wave][ht][s][0][lane] = make_uint4(w[0], w[1], w[2], w[3]);
-                if constexpr (Cfg::SPLIT) qf[wave][ht][s][Cfg::QPARTS - 1][lane] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+                QF[ht][s][0] = make_uint4(w[0], w[1], w[2], w[3]);
+                if constexpr (Cfg::SPLIT) QF[ht][s][Cfg::QPARTS - 1] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
             }
         }
     }
@@ -301,8 +302,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
     for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
         for (int i = 0; i < DTW; ++i) O[ht][i] = zero4();
-    // online softmax state of head tile hs (this wave's), per head li
-    const int hs = HT == 1 ? 0 : wave;
+    // online softmax state of head tile hs (waves < HT), per head li
+    const int hs = HT == 1 ? 0 : (wave < HT ? wave : 0);
+    const bool softmax_wave = HT == 1 || wave < HT;
     float m_run = -INFINITY, l_run = 0.f;
     uint4 Ploc[NPF];                                           // P^T fragments when HT == 1
     float alpha_loc = 1.f;
@@ -310,8 +312,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
 
     for (int tile = tile0; tile < tile1; ++tile) {
         const int slot0 = tile * 32;
+        const int drow0 = ((tile - tile0) * 32) % DESC;
         __syncthreads();                                       // the previous tile is done with Kt
-        store_tile(tile, raw);
+        store_tile(tile, drow0, raw, rsr);
         __syncthreads();                                       // (A) tile in Kt
         // load the next tile while this one computes
         if (tile + 1 < tile1) {
@@ -320,77 +323,55 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
                 describe((tile + 1) * 32);
                 __syncthreads();
             }
-            load_tile(tile + 1, drow, raw);
+            load_tile(tile + 1, drow, raw, rsr);
         }
 
-        // ---- partial S^T over this wave's channels, rows 16*rt + li of the tile.
-        //      FP8: the non-rotary part goes to slot `wave`, the rotary part
-        //      (wave 3's last R channels) to slot 4, so that the block scale can
-        //      be applied to the former alone.
+        // ---- partial S^T over this wave's channels, rows 16*rt + li of the tile
         f32x4_t acc[HT][2];
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) { acc[ht][0] = zero4(); acc[ht][1] = zero4(); }
 #pragma unroll
         for (int s = 0; s < KSW; ++s) {
             const int d0 = dw0 + s * MMA::K;
-            if (KVF == 2 && d0 == nf) {                        // wave-uniform: the first rotary step
-#pragma unroll
-                for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-                    for (int rt = 0; rt < 2; ++rt) { Sbuf[wave][ht][rt][lane] = acc[ht][rt]; acc[ht][rt] = zero4(); }
-            }
             const uint4 ka = *(const uint4*)(Kt + li * KP + d0 + g * EPF);
             const uint4 kb = *(const uint4*)(Kt + (16 + li) * KP + d0 + g * EPF);
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
                 for (int part = 0; part < Cfg::QPARTS; ++part) {
-                    const uint4 qb = qf[wave][ht][s][part][lane];
-                    acc[ht][0] = MMA::step(ka, qb, acc[ht][0]);
-                    acc[ht][1] = MMA::step(kb, qb, acc[ht][1]);
+                    acc[ht][0] = MMA::step(ka, QF[ht][s][part], acc[ht][0]);
+                    acc[ht][1] = MMA::step(kb, QF[ht][s][part], acc[ht][1]);
                 }
         }
-        {
-            // FP8: the last wave ends on rotary channels (slot 4); a quarter with
-            // rotary channels only left slot 3 empty
-            const bool to_rope = KVF == 2 && dw0 + DW > nf;
-            const int slot = to_rope ? 4 : wave;
-            if (KVF == 2 && dw0 >= nf) {
 #pragma unroll
-                for (int ht = 0; ht < HT; ++ht)
+        for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-                    for (int rt = 0; rt < 2; ++rt) Sbuf[wave][ht][rt][lane] = zero4();
-            }
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt) Sbuf[slot][ht][rt][lane] = acc[ht][rt];
-        }
-        // lane holds rows 16*rt + 4g + i of head li; the FP8 block scale applies
-        // to the non-rotary channels of entry rows (window rows carry scale 1)
-        float rsc[2][4];
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) rsc[rt][i] = KVF == 2 ? tscl[16 * rt + 4 * g + i] : 1.f;
+            for (int rt = 0; rt < 2; ++rt) Sbuf[wave][ht][rt][lane] = acc[ht][rt];
         __syncthreads();                                       // (B) partial logits in LDS
 
-        // ---- softmax of head tile hs: sum the partials in wave order
-        {
+        // ---- softmax of head tile hs: the partials summed in wave order; the
+        //      FP8 block scale multiplies the non-rotary waves' sum (window
+        //      rows carry scale 1).  Lane holds rows 16*rt + 4g + i of head li.
+        if (softmax_wave) {
+            float rsc[2][4];
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) rsc[rt][i] = KVF == 2 ? tscl[16 * rt + 4 * g + i] : 1.f;
             float sv[8];
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
-                f32x4_t v = ((Sbuf[0][hs][rt][lane] + Sbuf[1][hs][rt][lane]) + Sbuf[2][hs][rt][lane]) +
-                            Sbuf[3][hs][rt][lane];
-                if constexpr (KVF == 2) {
-                    const f32x4_t vr = Sbuf[Cfg::SLOTS - 1][hs][rt][lane];
+                f32x4_t vn = Sbuf[0][hs][rt][lane];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) v[i] = rsc[rt][i] * v[i] + vr[i];
-                }
+                for (int w = 1; w < NNW; ++w) vn += Sbuf[w][hs][rt][lane];
+                f32x4_t vr = Sbuf[NNW][hs][rt][lane];
+#pragma unroll
+                for (int w = NNW + 1; w < NW; ++w) vr += Sbuf[w][hs][rt][lane];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const bool valid = tval[16 * rt + 4 * g + i] != 0;
-                    sv[4 * rt + i] = valid ? v[i] : -INFINITY;
+                    const float v = KVF == 2 ? rsc[rt][i] * vn[i] + vr[i] : vn[i] + vr[i];
+                    sv[4 * rt + i] = valid ? v : -INFINITY;
                 }
             }
             float mx = sv[0];
@@ -427,8 +408,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
 #pragma unroll
                     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            q8[4 * rt + i] = slot0 + 16 * rt + 4 * g + i < K0 ? p[4 * rt + i] * rsc[rt][i] : p[4 * rt + i];
+                        for (int i = 0; i < 4; ++i) q8[4 * rt + i] = p[4 * rt + i] * rsc[rt][i];
                     pf[1] = make_uint4(pack_bf16x2(q8[0], q8[1]), pack_bf16x2(q8[2], q8[3]),
                                        pack_bf16x2(q8[4], q8[5]), pack_bf16x2(q8[6], q8[7]));
                 } else if constexpr (Cfg::SPLIT) {
@@ -481,11 +461,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
                 for (int dt = 0; dt < DTW; ++dt) O[ht][dt] *= al;
             }
         }
-        // P^T fragment for output tile dt: FP8 non-rotary channels take the
-        // scaled weights.  Only the last wave's quarter holds rotary channels,
-        // so the choice is made at compile time per (kind of wave, dt).
-        auto pv_all = [&](auto mode) {
-            constexpr int MODE = decltype(mode)::value;        // 0: not FP8, 1: scaled, 2: last wave
+        // FP8: the non-rotary waves take the scaled weights (a wave-uniform choice)
+        auto pv_all = [&](auto sel) {
+            constexpr int VSEL = decltype(sel)::value;
 #pragma unroll
             for (int dt = 0; dt < DTW; ++dt) {
                 const int c0 = dw0 + 16 * dt;
@@ -511,28 +489,27 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
                     const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS s16x4_t*)(base + 16 * KP));
                     const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
                     const uint4 va = make_uint4(l2.x, l2.y, h2.x, h2.y);
-                    const bool scaled_last = 3 * DW + 16 * dt < nf;   // constant once unrolled
-                    const int v = KVF != 2 ? 0 : (MODE == 1 ? 1 : (MODE == 2 && scaled_last ? 1 : 0));
 #pragma unroll
                     for (int ht = 0; ht < HT; ++ht) {
-                        O[ht][dt] = MMA::step(va, pf[ht][v], O[ht][dt]);
+                        O[ht][dt] = MMA::step(va, pf[ht][VSEL], O[ht][dt]);
                         if constexpr (Cfg::SPLIT) O[ht][dt] = MMA::step(va, pf[ht][NPF - 1], O[ht][dt]);
-                        keep_in_acc(O[ht][dt]);
                     }
                 }
             }
         };
-        if constexpr (KVF != 2) pv_all(std::integral_constant<int, 0>());
-        else if (dw0 + DW <= nf) pv_all(std::integral_constant<int, 1>());
-        else pv_all(std::integral_constant<int, 2>());
+        if (KVF == 2 && dw0 < nf) pv_all(std::integral_constant<int, KVF == 2 ? 1 : 0>());
+        else pv_all(std::integral_constant<int, 0>());
     }
 
     // ---- per-head (max, sum) of every head tile
     if constexpr (HT > 1) {
-        if (g == 0) { Mbuf[hs][li] = m_run; Lbuf[hs][li] = l_run; }
+        if (softmax_wave && g == 0) { Mbuf[hs][li] = m_run; Lbuf[hs][li] = l_run; }
         __syncthreads();
     }
-    // lane holds O^T[dw0 + 16*dt + 4g + i][head hbase + 16*ht + li]
+    // lane holds O^T[dw0 + 16*dt + 4g + i][head hbase + 16*ht + li].  Split
+    // partial per (query, head, split): max, sum (fp32) at bytes 0 and 4, the
+    // C channels from byte 16, in the output format.
+    const size_t pstride = a.out_bf16 ? 2 * (size_t)C + 16 : 4 * (size_t)C + 16;
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
         const int head = hbase + 16 * ht + li;
@@ -565,12 +542,16 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
                 }
             }
         } else {
-            float* pp = a.ws + (((size_t)gq * a.nh + head) * a.n_splits + split) * (C + 4);
-            if (wave == 0 && g == 0) { pp[0] = mh; pp[1] = lh; }
+            char* pp = (char*)a.ws + (((size_t)gq * a.nh + head) * a.n_splits + split) * pstride;
+            if (wave == 0 && g == 0) { ((float*)pp)[0] = mh; ((float*)pp)[1] = lh; }
 #pragma unroll
             for (int dt = 0; dt < DTW; ++dt) {
                 const int d = dw0 + 16 * dt + 4 * g;
-                *(float4*)(pp + 4 + d) = make_float4(O[ht][dt][0], O[ht][dt][1], O[ht][dt][2], O[ht][dt][3]);
+                if (a.out_bf16)
+                    *(uint2*)(pp + 16 + 2 * (size_t)d) = make_uint2(pack_bf16x2(O[ht][dt][0], O[ht][dt][1]),
+                                                                    pack_bf16x2(O[ht][dt][2], O[ht][dt][3]));
+                else
+                    *(float4*)(pp + 16 + 4 * (size_t)d) = make_float4(O[ht][dt][0], O[ht][dt][1], O[ht][dt][2], O[ht][dt][3]);
             }
         }
     }
@@ -578,46 +559,55 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
 
 // Merge the split partials of one (query, head) in split order, add the sink,
 // normalise, rotate back at -t and store.  One workgroup of 128 threads per
-// (query, head); each thread owns 4 consecutive channels.  Partial layout per
-// (query, head, split): max, sum, 2 unused floats, then the C channels.
+// (query, head); each thread owns 4 consecutive channels.
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a)
 {
     __shared__ float w_sh[256];
     __shared__ float o_sh[512];
-    __shared__ float rc[64], rs[64];
+    __shared__ float rc[32], rs[32];
     __shared__ float m_sh, inv_sh;
     const int gq = blockIdx.x, head = blockIdx.y;
     const int C = a.c, S = a.n_splits, nf = C - a.r;
     const int req = find_request(a.cu_new, a.n_req, gq);
     const int t = a.start_pos[req] + (gq - a.cu_new[req]);
-    const float* pp = a.ws + ((size_t)gq * a.nh + head) * S * (C + 4);
+    const size_t pstride = a.out_bf16 ? 2 * (size_t)C + 16 : 4 * (size_t)C + 16;
+    const char* pp = (const char*)a.ws + ((size_t)gq * a.nh + head) * S * pstride;
     const float zs = a.sinks[head] * LOG2E;
-    for (int j = threadIdx.x; j < a.r / 2; j += blockDim.x) rope_cs((double)t, j, a.r, a.theta, &rc[j], &rs[j]);
+    for (int j = threadIdx.x; j < a.r / 2; j += blockDim.x) rope_cs_f((double)t, a.inv_freq[j], &rc[j], &rs[j]);
     if (threadIdx.x < 64) {                                    // one wave: the common reference max
         float M = zs;
-        for (int s = threadIdx.x; s < S; s += 64) M = fmaxf(M, pp[(size_t)s * (C + 4)]);
+        for (int s = threadIdx.x; s < S; s += 64) M = fmaxf(M, *(const float*)(pp + s * pstride));
         for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
         if (threadIdx.x == 0) m_sh = M;
     }
     __syncthreads();
     const float M = m_sh;
-    for (int s = threadIdx.x; s < S; s += blockDim.x) w_sh[s] = exp2f(pp[(size_t)s * (C + 4)] - M);
+    for (int s = threadIdx.x; s < S; s += blockDim.x) w_sh[s] = exp2f(*(const float*)(pp + s * pstride) - M);
     __syncthreads();
     if (threadIdx.x == 0) {                                    // the denominator, in split order
         float L = exp2f(zs - M);
-        for (int s = 0; s < S; ++s) L += pp[(size_t)s * (C + 4) + 1] * w_sh[s];
+        for (int s = 0; s < S; ++s) L += *(const float*)(pp + s * pstride + 4) * w_sh[s];
         inv_sh = 1.0f / L;
     }
     __syncthreads();
     const float inv = inv_sh;
     for (int d4 = threadIdx.x; d4 < C / 4; d4 += blockDim.x) {
-        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+        float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
         for (int s = 0; s < S; ++s) {
-            const float4 v = *(const float4*)(pp + (size_t)s * (C + 4) + 4 + 4 * d4);
+            const char* src = pp + s * pstride + 16;
+            float v0, v1, v2, v3;
+            if (a.out_bf16) {
+                const uint2 u = *(const uint2*)(src + 8 * (size_t)d4);
+                v0 = bf16_to_f32(u.x & 0xFFFF); v1 = bf16_to_f32(u.x >> 16);
+                v2 = bf16_to_f32(u.y & 0xFFFF); v3 = bf16_to_f32(u.y >> 16);
+            } else {
+                const float4 u = *(const float4*)(src + 16 * (size_t)d4);
+                v0 = u.x; v1 = u.y; v2 = u.z; v3 = u.w;
+            }
             const float w = w_sh[s];
-            o.x += v.x * w; o.y += v.y * w; o.z += v.z * w; o.w += v.w * w;
+            o0 += v0 * w; o1 += v1 * w; o2 += v2 * w; o3 += v3 * w;
         }
-        o_sh[4 * d4] = o.x * inv; o_sh[4 * d4 + 1] = o.y * inv; o_sh[4 * d4 + 2] = o.z * inv; o_sh[4 * d4 + 3] = o.w * inv;
+        o_sh[4 * d4] = o0 * inv; o_sh[4 * d4 + 1] = o1 * inv; o_sh[4 * d4 + 2] = o2 * inv; o_sh[4 * d4 + 3] = o3 * inv;
     }
     __syncthreads();
     for (int d = threadIdx.x; d < C; d += blockDim.x) {
@@ -649,11 +639,12 @@ int attention_splits(int n_tokens, int n_heads, int rows_max)
     return splits;
 }
 
+// Bytes of split partials (fp32 layout, the larger of the two).
 size_t attention_workspace(int n_tokens, int n_heads, int c, int rows_max)
 {
     const int s = attention_splits(n_tokens, n_heads, rows_max);
     if (s <= 1) return 0;
-    return (size_t)n_tokens * n_heads * s * (c + 4) * sizeof(float);
+    return (size_t)n_tokens * n_heads * s * (4 * (size_t)c + 16);
 }
 
 // (c, rope) shapes: (128, 32), (256, 64), (512, 64); fp32 KV up to c = 256
@@ -661,10 +652,10 @@ template <int KVF, int HT>
 static void launch_c(hipStream_t st, const AttnArgs& a, dim3 grid)
 {
     switch (a.c) {
-    case 128: attn_kernel<KVF, 128, 32, HT><<<grid, 256, 0, st>>>(a); break;
-    case 256: attn_kernel<KVF, 256, 64, HT><<<grid, 256, 0, st>>>(a); break;
+    case 128: attn_kernel<KVF, 128, 32, HT><<<grid, AttnCfg<KVF, 128, 32, HT>::NT, 0, st>>>(a); break;
+    case 256: attn_kernel<KVF, 256, 64, HT><<<grid, AttnCfg<KVF, 256, 64, HT>::NT, 0, st>>>(a); break;
     case 512:
-        if constexpr (KVF != 0) attn_kernel<KVF, 512, 64, HT><<<grid, 256, 0, st>>>(a);
+        if constexpr (KVF != 0) attn_kernel<KVF, 512, 64, HT><<<grid, AttnCfg<KVF, 512, 64, HT>::NT, 0, st>>>(a);
         break;
     default: break;
     }
@@ -686,6 +677,7 @@ hipError_t launch_attention(hipStream_t st, AttnArgs a)
     const int tiles = (a.rows_max + 31) / 32;
     a.n_splits = attention_splits(a.n_tokens, a.nh, a.rows_max);
     a.tiles_per_split = (tiles + a.n_splits - 1) / a.n_splits;
+    for (int j = 0; j < a.r / 2 && j < 32; ++j) a.inv_freq[j] = rope_inv_freq(j, a.r, (double)a.theta);
     const dim3 grid(a.n_tokens, hg, a.n_splits);
     if (ht == 4) launch_ht<4>(st, a, grid);
     else launch_ht<1>(st, a, grid);

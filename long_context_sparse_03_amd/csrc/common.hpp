@@ -222,12 +222,27 @@ CSA_DEV float block_max(float v, float* red)
     return t;
 }
 
-// RoPE angle for pair j of r rotary channels at position pos: the angle is
-// formed and reduced to [-pi, pi] in double (positions reach millions), then
-// its sine and cosine are taken in fp32.
+// RoPE frequency of pair j of r rotary channels, theta^(-2j/r) (the same
+// expression is used on the host to fill frequency tables).
+__host__ __device__ inline double rope_inv_freq(int j, int r, double theta)
+{
+    return exp2(-2.0 * (double)j / (double)r * log2(theta));
+}
+
+// cos / sin of pos * inv_freq: the angle is formed and reduced to [-pi, pi]
+// in double (positions reach millions), then its sine and cosine are taken
+// in fp32.
+CSA_DEV void rope_cs_f(double pos, double inv_freq, float* cs, float* sn)
+{
+    double ang = pos * inv_freq;
+    ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
+    sincosf((float)ang, sn, cs);
+}
+
+// The same for pair j of r rotary channels at position pos.
 CSA_DEV void rope_cs(double pos, int j, int r, float theta, float* cs, float* sn)
 {
-    const double inv_freq = exp2(-2.0 * (double)j / (double)r * log2((double)theta));
+    const double inv_freq = rope_inv_freq(j, r, (double)theta);
     double ang = pos * inv_freq;
     ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
     sincosf((float)ang, sn, cs);

@@ -104,6 +104,7 @@ struct AttnArgs {
     int rows_max;              // rows per query (slots): k + n_win, or max entries + n_win
     int n_splits;
     int tiles_per_split;
+    double inv_freq[32];       // RoPE frequencies theta^(-2j/r), j < r/2 (filled by launch_attention)
 };
 
 int attention_splits(int n_tokens, int n_heads, int rows_max);
