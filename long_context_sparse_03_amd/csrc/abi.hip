@@ -233,6 +233,7 @@ int csa_compress_kv(void* stream, const csa_layer_desc* layer, const csa_batch* 
     a.out_count = out_count;
     a.max_entries = max_entries;
     a.out_win = out_win;
+    a.max_new = batch->max_new;
     const int n_main = csa ? 4 * layer->c : 2 * layer->c;
     return hip_status(csa::launch_compress((hipStream_t)stream, a, H, W, csa ? W_idx : W, n_main, d,
                                            layer->act_fmt == CSA_FMT_BF16, n_tokens),

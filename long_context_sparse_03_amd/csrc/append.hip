@@ -5,21 +5,18 @@
 // §7: state cache + paged cache of lcm(m, m') raw tokens per block; §1.5:
 // RoPE channels in BF16, the rest in FP8; §6.2: FP4 indexer keys).
 //
-// entries_kernel: one workgroup per new entry.  For the FP8 format the first
-//   new entry of each (request, block) leads: it applies the block-scale rule
-//   to all of that block's new entries of this call, in slot order, so the
-//   result does not depend on how workgroups are scheduled.
-// window_kernel: one workgroup per new token.
+// One launch: a workgroup per new entry, then one per new token's window row.
+// For the FP8 format the first new entry of each (request, block) leads: it
+// applies the block-scale rule to all of that block's new entries of this
+// call, in slot order, so the result does not depend on how workgroups are
+// scheduled.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace csa {
 
-__global__ __launch_bounds__(256) void entries_kernel(AppendArgs a)
+CSA_DEV void append_entry(const AppendArgs& a, int e, float* red, float* s_sh)
 {
-    __shared__ float red[16];
-    __shared__ float s_sh[2];
-    const int e = blockIdx.x;
     const int count = min(*a.count, a.max_entries);
     if (e >= count) return;
     const int req = a.meta[2 * e], ent = a.meta[2 * e + 1];
@@ -104,9 +101,8 @@ __global__ __launch_bounds__(256) void entries_kernel(AppendArgs a)
     }
 }
 
-__global__ __launch_bounds__(256) void window_kernel(AppendArgs a)
+CSA_DEV void append_window_row(const AppendArgs& a, int gtok)
 {
-    const int gtok = blockIdx.x;
     const int req = find_request(a.cu_new, a.n_req, gtok);
     const int pos = a.start_pos[req] + (gtok - a.cu_new[req]);
     const int slot = pos % a.win_cap;
@@ -121,10 +117,20 @@ __global__ __launch_bounds__(256) void window_kernel(AppendArgs a)
     }
 }
 
+// Blocks [0, max_entries) store entries, the next n_tokens blocks window rows.
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a)
+{
+    __shared__ float red[16];
+    __shared__ float s_sh[2];
+    if ((int)blockIdx.x < a.max_entries) append_entry(a, blockIdx.x, red, s_sh);
+    else append_window_row(a, blockIdx.x - a.max_entries);
+}
+
 hipError_t launch_append(hipStream_t st, const AppendArgs& a)
 {
-    if (a.max_entries > 0) entries_kernel<<<a.max_entries, 256, 0, st>>>(a);
-    if (a.n_tokens > 0 && a.win != nullptr) window_kernel<<<a.n_tokens, 256, 0, st>>>(a);
+    const int nw = (a.n_tokens > 0 && a.win != nullptr) ? a.n_tokens : 0;
+    const int me = a.max_entries > 0 ? a.max_entries : 0;
+    if (me + nw > 0) append_kernel<<<me + nw, 256, 0, st>>>(a);
     return hipGetLastError();
 }
 

@@ -155,11 +155,8 @@ CSA_DEV void norm_rope_store(float* xs, float* red, int c, int r, const float* g
 // merge: one workgroup per entry completed in this call
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(256) void merge_kernel(CompressArgs a)
+CSA_DEV void merge_entry(const CompressArgs& a, int e, float* xs, float* red)
 {
-    __shared__ float xs[512];
-    __shared__ float red[16];
-    const int e = blockIdx.x;
     // locate the entry: requests in order, entries of a request in index order
     int total = 0, req = -1, ent = 0;
     for (int rr = 0; rr < a.n_req; ++rr) {
@@ -227,17 +224,30 @@ __global__ __launch_bounds__(256) void merge_kernel(CompressArgs a)
     }
 }
 
+__global__ __launch_bounds__(256) void merge_kernel(CompressArgs a)
+{
+    __shared__ float xs[512];
+    __shared__ float red[16];
+    merge_entry(a, blockIdx.x, xs, red);
+}
+
+// window row of new token gtok: its C^a (CSA) or C (HCA) row, normalised and
+// rotated at its position
+CSA_DEV void window_row(const CompressArgs& a, int gtok, int pos, float* xs, float* red)
+{
+    const float* row = a.P + (size_t)gtok * a.ncols;       // C^a (CSA) or C (HCA) at column 0
+    for (int ch = threadIdx.x; ch < a.c; ch += blockDim.x) xs[ch] = row[ch];
+    __syncthreads();
+    norm_rope_store(xs, red, a.c, a.r, a.gamma, a.eps, (double)pos, a.theta, a.out_win + (size_t)gtok * a.c);
+}
+
 __global__ __launch_bounds__(256) void window_rows_kernel(CompressArgs a)
 {
     __shared__ float xs[512];
     __shared__ float red[16];
     const int gtok = blockIdx.x;
     const int req = find_request(a.cu_new, a.n_req, gtok);
-    const int pos = a.start_pos[req] + (gtok - a.cu_new[req]);
-    const float* row = a.P + (size_t)gtok * a.ncols;       // C^a (CSA) or C (HCA) at column 0
-    for (int ch = threadIdx.x; ch < a.c; ch += blockDim.x) xs[ch] = row[ch];
-    __syncthreads();
-    norm_rope_store(xs, red, a.c, a.r, a.gamma, a.eps, (double)pos, a.theta, a.out_win + (size_t)gtok * a.c);
+    window_row(a, gtok, a.start_pos[req] + (gtok - a.cu_new[req]), xs, red);
 }
 
 __global__ __launch_bounds__(256) void tail_update_kernel(CompressArgs a)
@@ -250,6 +260,29 @@ __global__ __launch_bounds__(256) void tail_update_kernel(CompressArgs a)
     float* tail = (float*)((char*)a.state + (size_t)req * a.state_stride + a.tail_off);
     const float* src = a.P + (size_t)(cu + n - keep + j) * a.ncols;
     float* dst = tail + (size_t)(p % a.R) * a.ncols;
+    for (int ch = threadIdx.x; ch < a.ncols; ch += blockDim.x) dst[ch] = src[ch];
+}
+
+// At most one new token per request: the merges, the window rows and the
+// tail update in one launch.  Blocks [0, nm) merge entries; block nm + g
+// handles token g: its window row, and its projected row into the tail ring.
+// The tail slot written (position p) is never one a merge of this call reads:
+// an entry completed by the token at p reads positions p-R+1 .. p only.
+__global__ __launch_bounds__(256) void post_decode_kernel(CompressArgs a, int nm)
+{
+    __shared__ float xs[512];
+    __shared__ float red[16];
+    if ((int)blockIdx.x < nm) {
+        merge_entry(a, blockIdx.x, xs, red);
+        return;
+    }
+    const int gtok = blockIdx.x - nm;
+    const int req = find_request(a.cu_new, a.n_req, gtok);
+    const int pos = a.start_pos[req] + (gtok - a.cu_new[req]);
+    window_row(a, gtok, pos, xs, red);
+    float* tail = (float*)((char*)a.state + (size_t)req * a.state_stride + a.tail_off);
+    const float* src = a.P + (size_t)gtok * a.ncols;
+    float* dst = tail + (size_t)(pos % a.R) * a.ncols;
     for (int ch = threadIdx.x; ch < a.ncols; ch += blockDim.x) dst[ch] = src[ch];
 }
 
@@ -280,10 +313,15 @@ hipError_t launch_compress(hipStream_t st, const CompressArgs& a, const void* H,
                                                                 n_main, N, M, d, a.P);
         }
     }
-    merge_kernel<<<a.max_entries > 0 ? a.max_entries : 1, 256, 0, st>>>(a);
-    if (M > 0) {
-        window_rows_kernel<<<M, 256, 0, st>>>(a);
-        tail_update_kernel<<<dim3(a.R, a.n_req), 256, 0, st>>>(a);
+    const int nm = a.max_entries > 0 ? a.max_entries : 1;
+    if (a.max_new <= 1) {
+        post_decode_kernel<<<nm + M, 256, 0, st>>>(a, nm);
+    } else {
+        merge_kernel<<<nm, 256, 0, st>>>(a);
+        if (M > 0) {
+            window_rows_kernel<<<M, 256, 0, st>>>(a);
+            tail_update_kernel<<<dim3(a.R, a.n_req), 256, 0, st>>>(a);
+        }
     }
     return hipGetLastError();
 }

@@ -26,6 +26,7 @@ struct CompressArgs {
     int32_t* out_count;
     int max_entries;
     float* out_win;
+    int max_new;               // largest number of new tokens of one request
 };
 
 hipError_t launch_compress(hipStream_t st, const CompressArgs& a, const void* H, const void* W, const void* Wi,
