@@ -5,9 +5,10 @@
 // rounded to the score format (BF16 scores: "DeepSeek-V4 内部机制" §6.2).
 //
 // The contraction is an MFMA product with the indexer heads as the M
-// dimension and 16 keys as N: lane l of a wave holds head (key) l%16 and a
-// contiguous quarter of the key width, so a wave loads 16 keys as one
-// contiguous run of a paged block.  ReLU, the head weights and the head sum
+// dimension and 16 keys as N: lane l of a wave holds head (key) l%16; in the
+// decode kernel, step s of the contraction covers 64 bytes of the key and
+// lane group l/16 the 16 bytes at 16*(l/16) of them, so the four lanes of a
+// key read 64 contiguous bytes per load.  ReLU, the head weights and the head sum
 // are applied to the accumulators in registers; the sum over the four lane
 // groups is a fixed butterfly, so the result is deterministic.
 //
@@ -87,8 +88,10 @@ CSA_DEV f32x4_t mfma_fp4(uint4 a, int sa, uint4 b, int sb)
 // scores 64 entries per iteration as four 16-key tiles and keeps the next
 // iteration's key loads in flight while it computes the current one.
 // HT = head tiles (<= 4), S = fragments per lane group.
-constexpr int IDX_EPW = 1024;                 // entries per workgroup
-constexpr int IDX_ITERS = IDX_EPW / 256;      // iterations of 256 entries (64 per wave)
+constexpr int IDX_EPW = 1024;                 // entries per workgroup (MXFP4 kernel)
+constexpr int IDXD_EPW = 1024;                // entries per workgroup (fp32 / bf16 kernel)
+constexpr int IDXD_ITERS = IDXD_EPW / 256;    // iterations of 256 entries (64 per wave)
+constexpr int IDX_ITERS = IDX_EPW / 256;      // the same for the MXFP4 kernel
 
 template <int IDXF, int S>
 CSA_DEV void load_keys(const IndexArgs& a, const int* bt, int blk0, int e0, int V, int g, int li, uint4 (&B)[4][S])
@@ -104,96 +107,130 @@ CSA_DEV void load_keys(const IndexArgs& a, const int* bt, int blk0, int e0, int 
         const int phys = bt[(e >> a.epb_log2) - blk0];
         const int slot = (e & (a.epb - 1));
         const char* kb = (const char*)a.keys + (size_t)phys * a.key_block_bytes;
-        const char* kp = kb + (size_t)slot * kbytes + (size_t)g * quarter * (IDXF == 0 ? 4 : 2);
+        // step s covers 64 bytes of the key, lane group g the 16 bytes at 16g
+        // of them: the four lanes of a key read 64 contiguous bytes
+        const char* kp = kb + (size_t)slot * kbytes + (size_t)g * 16;
 #pragma unroll
-        for (int s = 0; s < S; ++s) B[tile][s] = ld16(kp + 16 * s);
+        for (int s = 0; s < S; ++s) B[tile][s] = ld16(kp + 64 * s);
     }
 }
 
 template <int IDXF, int HT, int S>
-__global__ __launch_bounds__(256) void index_decode_kernel(IndexArgs a)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S <= 4 ? 2 : 1))) void index_decode_kernel(IndexArgs a)
 {
     // IDXF 0: fp32 keys and queries; 1: bf16 keys and queries.
     using MMA = typename std::conditional<IDXF == 0, MmaF32, MmaBF16>::type;
-    __shared__ int bt[IDX_EPW + 1];             // physical blocks of this workgroup's entries
+    __shared__ int bt[IDXD_EPW + 1];             // physical blocks of this workgroup's entries
+    // the query's MFMA fragments, shared by the four waves (in LDS rather than
+    // registers, so that two workgroups fit on a compute unit and twice the
+    // key bytes are in flight)
+    __shared__ uint4 qfrag[HT][S][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
     const int gq = blockIdx.y;
-    __shared__ int cu_sh[1025];
-    const int req = find_request_block(a.cu_new, a.n_req, gq, cu_sh);
-    const int t = a.start_pos[req] + (gq - cu_sh[req]);
-    const int V = (t + 1) / a.m;
-    if (blockIdx.x == 0 && threadIdx.x == 0) a.n_valid[gq] = V;
-    const int wg0 = blockIdx.x * IDX_EPW;
-    if (wg0 >= V) return;
-    const int cI = a.cI, nh = a.nh, quarter = cI / 4;
+    const int wg0 = blockIdx.x * IDXD_EPW;
+    const int cI = a.cI, nh = a.nh;
     constexpr int QES = IDXF == 0 ? 4 : 2;      // query element size
-
-    // ---- prologue: block-table slice, query fragments and head weights,
-    //      all loads issued together (clamped indices, masked afterwards)
-    const int blk0 = wg0 >> a.epb_log2;
-    const int nblk = ((min(V, wg0 + IDX_EPW) - 1) >> a.epb_log2) - blk0 + 1;
-    int btv[(IDX_EPW + 255) / 256];
-#pragma unroll
-    for (int i = 0; i < (IDX_EPW + 255) / 256; ++i) {
-        const int j = min((int)threadIdx.x + 256 * i, nblk - 1);
-        btv[i] = a.block_table[(size_t)req * a.max_blocks + blk0 + j];
+    __shared__ int cu_sh[1025];
+    int req, tok;
+    if (a.one_per_req) {                         // token gq is request gq's only new token
+        req = gq;
+        tok = 0;
+    } else {
+        req = find_request_block(a.cu_new, a.n_req, gq, cu_sh);
+        tok = gq - cu_sh[req];
     }
-    uint4 A[HT][S];
+
+    // ---- prologue: position, block-table slice, query fragments and head
+    //      weights, all loads issued together (the slice covers every block
+    //      the workgroup can touch, clamped to the table row; indices
+    //      clamped, values masked afterwards)
+    const int blk0 = wg0 >> a.epb_log2;
+    const int nbw = ((wg0 + IDXD_EPW - 1) >> a.epb_log2) - blk0 + 1;
+    const int sp = a.start_pos[req];
+    int btv[(IDXD_EPW + 255) / 256];
+#pragma unroll
+    for (int i = 0; i < (IDXD_EPW + 255) / 256; ++i) {
+        const int j = min(blk0 + min((int)threadIdx.x + 256 * i, nbw - 1), a.max_blocks - 1);
+        btv[i] = a.block_table[(size_t)req * a.max_blocks + j];
+    }
+    // wave ht (< HT) stages head tile ht of the query
+    uint4 A[S];
+    if (wave < HT) {
+        const int head = min(16 * wave + li, nh - 1);
+        const char* qp = (const char*)a.q + ((size_t)gq * nh + head) * cI * QES + (size_t)g * 16;
+#pragma unroll
+        for (int s = 0; s < S; ++s) A[s] = ld16(qp + 64 * s);
+    }
     float wv[HT][4];
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-        const int head = min(16 * ht + li, nh - 1);
-        const char* qp = (const char*)a.q + ((size_t)gq * nh + head) * cI * QES + (size_t)g * quarter * QES;
-#pragma unroll
-        for (int s = 0; s < S; ++s) A[ht][s] = ld16(qp + 16 * s);
+    for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
         for (int i = 0; i < 4; ++i) wv[ht][i] = a.w[(size_t)gq * nh + min(16 * ht + 4 * g + i, nh - 1)];
+    const int t = sp + tok;
+    const int V = (t + 1) / a.m;
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.n_valid[gq] = V;
+    if (wg0 >= V) return;                        // workgroup-uniform
+#pragma unroll
+    for (int i = 0; i < (IDXD_EPW + 255) / 256; ++i)
+        if ((int)threadIdx.x + 256 * i < nbw) bt[threadIdx.x + 256 * i] = btv[i];
+    if (wave < HT) {
+        const bool hv = 16 * wave + li < nh;
+#pragma unroll
+        for (int s = 0; s < S; ++s) qfrag[wave][s][lane] = sel16(hv, A[s]);
     }
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < (IDX_EPW + 255) / 256; ++i)
-        if ((int)threadIdx.x + 256 * i < nblk) bt[threadIdx.x + 256 * i] = btv[i];
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-        const bool hv = 16 * ht + li < nh;
-#pragma unroll
-        for (int s = 0; s < S; ++s) A[ht][s] = sel16(hv, A[ht][s]);
+    for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
         for (int i = 0; i < 4; ++i) wv[ht][i] = 16 * ht + 4 * g + i < nh ? wv[ht][i] : 0.f;
-    }
     __syncthreads();
 
     // ---- main loop: 256 entries per iteration (64 per wave); the next
-    //      iteration's key loads are issued before this one's arithmetic
-    uint4 B[2][4][S];
-    load_keys<IDXF, S>(a, bt, blk0, wg0 + wave * 64, V, g, li, B[0]);
+    //      iterations' key loads are issued before this one's arithmetic
+    constexpr int NB = 2;                       // key buffers (NB-1 iterations in flight)
+    uint4 B[NB][4][S];
+    // The loads are unconditional (clamped to the last visible entry): loads
+    // under a branch would make the wait counts below pessimistic.
 #pragma unroll
-    for (int it = 0; it < IDX_ITERS; ++it) {
-        const int cur = it & 1;
+    for (int j = 0; j < NB - 1; ++j) {
+        if (j < IDXD_ITERS) load_keys<IDXF, S>(a, bt, blk0, wg0 + 256 * j + wave * 64, V, g, li, B[j]);
+        __builtin_amdgcn_sched_barrier(0);            // keep the loads in iteration order
+    }
+#pragma unroll
+    for (int it = 0; it < IDXD_ITERS; ++it) {
+        const int cur = it % NB;
         const int e_base = wg0 + it * 256 + wave * 64;
-        if (it + 1 < IDX_ITERS && e_base + 256 < V)
-            load_keys<IDXF, S>(a, bt, blk0, e_base + 256, V, g, li, B[cur ^ 1]);
+        if (it + NB - 1 < IDXD_ITERS)
+            load_keys<IDXF, S>(a, bt, blk0, e_base + 256 * (NB - 1), V, g, li, B[(it + NB - 1) % NB]);
         __builtin_amdgcn_sched_barrier(0);
         if (e_base >= V) break;                  // wave-uniform
+        // head tiles outermost: each query fragment is read from LDS once
+        // per iteration and serves the four key tiles; every tile's score
+        // still sums the head tiles in order
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int tile = 0; tile < 4; ++tile) {
-            if (e_base + 16 * tile >= V) break;  // wave-uniform: the whole tile is past V
-            const int e = e_base + 16 * tile + li;
-            float v = 0.f;
+        for (int ht = 0; ht < HT; ++ht) {
+            uint4 qf[S];
 #pragma unroll
-            for (int ht = 0; ht < HT; ++ht) {
+            for (int s = 0; s < S; ++s) qf[s] = qfrag[ht][s][lane];
+#pragma unroll
+            for (int tile = 0; tile < 4; ++tile) {
                 f32x4_t acc = zero4();
 #pragma unroll
-                for (int s = 0; s < S; ++s) acc = MMA::step(A[ht][s], B[cur][tile][s], acc);
+                for (int s = 0; s < S; ++s) acc = MMA::step(qf[s], B[cur][tile][s], acc);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) v += wv[ht][i] * fmaxf(acc[i], 0.f);
+                for (int i = 0; i < 4; ++i) v[tile] += wv[ht][i] * fmaxf(acc[i], 0.f);
             }
-            v += __shfl_xor(v, 16, 64);
-            v += __shfl_xor(v, 32, 64);
+        }
+#pragma unroll
+        for (int tile = 0; tile < 4; ++tile) {
+            const int e = e_base + 16 * tile + li;
+            float x = v[tile];
+            x += __shfl_xor(x, 16, 64);
+            x += __shfl_xor(x, 32, 64);
             if (g == 0 && e < V) {
-                if (v == 0.0f) v = 0.0f;                // -0 is stored as +0
-                if (a.score_bf16) ((uint16_t*)a.scores)[(size_t)gq * a.ld + e] = f32_to_bf16(v);
-                else ((float*)a.scores)[(size_t)gq * a.ld + e] = v;
+                if (x == 0.0f) x = 0.0f;                // -0 is stored as +0
+                if (a.score_bf16) ((uint16_t*)a.scores)[(size_t)gq * a.ld + e] = f32_to_bf16(x);
+                else ((float*)a.scores)[(size_t)gq * a.ld + e] = x;
             }
         }
     }
@@ -332,8 +369,14 @@ __global__ __launch_bounds__(256) void index_decode_fp4_kernel(IndexArgs a)
     __shared__ int cu_sh[1025];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
     const int gq = blockIdx.y;
-    const int req = find_request_block(a.cu_new, a.n_req, gq, cu_sh);
-    const int t = a.start_pos[req] + (gq - cu_sh[req]);
+    int req, t;
+    if (a.one_per_req) {                         // token gq is request gq's only new token
+        req = gq;
+        t = a.start_pos[gq];
+    } else {
+        req = find_request_block(a.cu_new, a.n_req, gq, cu_sh);
+        t = a.start_pos[req] + (gq - cu_sh[req]);
+    }
     const int V = (t + 1) / a.m;
     if (blockIdx.x == 0 && threadIdx.x == 0) a.n_valid[gq] = V;
     const int wg0 = blockIdx.x * IDX_EPW;
@@ -449,9 +492,12 @@ static void launch_fmt(hipStream_t st, const IndexArgs& a, dim3 grid)
     }
 }
 
-hipError_t launch_index(hipStream_t st, const IndexArgs& a, int max_visible, int max_new)
+hipError_t launch_index(hipStream_t st, const IndexArgs& args, int max_visible, int max_new)
 {
-    if (a.n_tokens <= 0) return hipSuccess;
+    if (args.n_tokens <= 0) return hipSuccess;
+    IndexArgs a = args;
+    // n_tokens tokens over n_req requests with at most one each: one apiece
+    a.one_per_req = max_new <= 1 && a.n_tokens == a.n_req;
     if (a.idx_fmt == 1 && a.cI == 128 && a.nh <= 64 && max_new >= 2 * PF_QPW && a.n_req < 1024) {
         const int groups = (max_new + PF_QPW - 1) / PF_QPW;
         dim3 grid(max_visible > 0 ? (max_visible + PF_ECH - 1) / PF_ECH : 1, a.n_req * groups);
@@ -462,7 +508,8 @@ hipError_t launch_index(hipStream_t st, const IndexArgs& a, int max_visible, int
         else index_prefill_kernel<1, 4><<<grid, 512, 0, st>>>(a, groups);
         return hipGetLastError();
     }
-    dim3 grid(max_visible > 0 ? (max_visible + IDX_EPW - 1) / IDX_EPW : 1, a.n_tokens);
+    const int epw = a.idx_fmt == 2 ? IDX_EPW : IDXD_EPW;
+    dim3 grid(max_visible > 0 ? (max_visible + epw - 1) / epw : 1, a.n_tokens);
     if (a.idx_fmt == 0) launch_fmt<0>(st, a, grid);
     else if (a.idx_fmt == 1) launch_fmt<1>(st, a, grid);
     else {

@@ -72,6 +72,7 @@ struct IndexArgs {
     int ld;
     int32_t* n_valid;
     int n_tokens;
+    int one_per_req;           // set by launch_index: every request has exactly one new token
 };
 
 hipError_t launch_index(hipStream_t st, const IndexArgs& a, int max_visible, int max_new);
