@@ -24,6 +24,10 @@ constexpr int TOPK_THREADS = 1024;
 constexpr int MAX_K = 2048;                                  // largest k the entry points accept
 constexpr int CAP16 = 40960;             // bf16 keys per workgroup (16-bit keys in LDS)
 constexpr int CAP32 = 20480;             // fp32 keys per workgroup
+constexpr int KPT16 = CAP16 / TOPK_THREADS;   // keys per thread at the capacity
+constexpr int KPT32 = CAP32 / TOPK_THREADS;
+constexpr int SMALL_NT = 256, SMALL_KPT = 32;  // workgroups of up to 8192 keys
+constexpr int SURV_CAP = 4096;                 // keys kept after the lower bound (1024-thread workgroups)
 
 // Order-preserving key of a score: sign-magnitude flip; -0 and +0 share the key.
 CSA_DEV uint32_t key16(uint32_t b)
@@ -38,19 +42,20 @@ CSA_DEV uint32_t key32(uint32_t u)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix sum over the block (fixed order); *total gets the sum.
-CSA_DEV int block_exscan(int v, int* sh, int* total)
+// Exclusive prefix sum over the block (fixed order, modulo 2^32); *total
+// gets the sum.
+CSA_DEV uint32_t block_exscan(uint32_t v, uint32_t* sh, uint32_t* total)
 {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    int inc = v;
+    uint32_t inc = v;
     for (int o = 1; o < 64; o <<= 1) {
-        int y = __shfl_up(inc, o, 64);
+        const uint32_t y = (uint32_t)__shfl_up((int)inc, o, 64);
         if (lane >= o) inc += y;
     }
     __syncthreads();
     if (lane == 63) sh[w] = inc;
     __syncthreads();
-    int off = 0, tot = 0;
+    uint32_t off = 0, tot = 0;
     for (int i = 0; i < nw; ++i) {
         if (i < w) off += sh[i];
         tot += sh[i];
@@ -59,115 +64,132 @@ CSA_DEV int block_exscan(int v, int* sh, int* total)
     return off + inc - v;
 }
 
-// Select the top kk of the n keys in LDS (order: key descending, position
-// ascending) and emit the selected positions in ascending order through
-// emit(rank, position).  BITS = key width (16 or 32).  The threshold is
-// found MSB first with an 11-bit first digit (sign, exponent and the top
-// mantissa bits, so that clustered scores spread over many bins) and
-// histograms kept in four interleaved copies to cut atomic contention.
-// Keys below lo are known to lie under the threshold: the histograms skip
-// them (the caller guarantees at least kk keys >= lo).
-template <int BITS, class KT, class EmitF>
-CSA_DEV void select_top(const KT* keys, int n, int kk, EmitF emit, uint32_t lo = 0u)
+// Selection works on keys held in registers: thread tid holds the keys of
+// positions tid*KPT .. tid*KPT+KPT-1, so the passes below read no memory and
+// a thread's positions are consecutive; positions >= n hold key 0, and every
+// real key is >= 1 (see keys_to_regs), so kk <= n keeps them out of the
+// selection.  The order is (key descending, position ascending).
+constexpr int HIST_COPIES = 4;
+__shared__ uint32_t topk_hist[2048 * HIST_COPIES];  // digit histograms (four interleaved copies)
+__shared__ uint32_t topk_scan[32];                  // block scan partials
+__shared__ uint32_t topk_digit[2];                  // chosen prefix, remaining rank
+
+// Threshold of the top kk (kk < number of real keys): T = the kk-th largest
+// key, rem = how many keys equal to T belong to the top kk.  BITS = key width
+// (16 or 32).  The threshold is found MSB first with an 11-bit first digit
+// (sign, exponent and the top mantissa bits, so that clustered scores spread
+// over many bins).  Keys below lo are known to lie under the threshold: the
+// histograms skip them (the caller guarantees at least kk keys >= lo).
+template <int BITS, int KPT>
+CSA_DEV void find_threshold(const uint32_t (&kr)[KPT], int kk, uint32_t lo, uint32_t& T, uint32_t& rem_out)
 {
-    constexpr int COPIES = 4;
-    __shared__ uint32_t hist[2048 * COPIES];
-    __shared__ uint32_t sh_prefix, sh_rem;
-    __shared__ int scan_sh[32];
     const int tid = threadIdx.x, nt = blockDim.x;
     uint32_t prefix = 0, mask = 0, rem = (uint32_t)kk;
-    const bool all = kk >= n;
-    if (!all) {
-        int hi = BITS;                                          // digits: 11, then 5 (16-bit) or 11, 10 (32-bit)
-        while (hi > 0) {
-            const int width = hi == BITS ? 11 : (hi > 11 ? 11 : hi);
-            const int shift = hi - width;
-            const int nb = 1 << width;
-            for (int b = tid; b < nb * COPIES; b += nt) hist[b] = 0;
-            __syncthreads();
-            for (int i = tid; i < n; i += nt) {                 // strided: conflict-free LDS reads
-                const uint32_t k = keys[i];
-                if (k >= lo && (k & mask) == prefix) atomicAdd(&hist[((k >> shift) & (uint32_t)(nb - 1)) * COPIES + (tid & 3)], 1u);
-            }
-            __syncthreads();
-            // bpt consecutive bins per thread, from the top: thread tid owns
-            // bins nb-1-bpt*tid down to nb-bpt*(tid+1)
-            const int bpt = (nb + nt - 1) / nt;
-            const int btop = nb - 1 - bpt * tid;
-            uint32_t cnt = 0;
+    int hi = BITS;                                              // digits: 11, then 5 (16-bit) or 11, 10 (32-bit)
+    while (hi > 0) {
+        const int width = hi == BITS ? 11 : (hi > 11 ? 11 : hi);
+        const int shift = hi - width;
+        const int nb = 1 << width;
+        for (int b = tid; b < nb * HIST_COPIES; b += nt) topk_hist[b] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const uint32_t k = kr[j];
+            if (k >= lo && (k & mask) == prefix)
+                atomicAdd(&topk_hist[((k >> shift) & (uint32_t)(nb - 1)) * HIST_COPIES + (tid & 3)], 1u);
+        }
+        __syncthreads();
+        // bpt consecutive bins per thread, from the top: thread tid owns
+        // bins nb-1-bpt*tid down to nb-bpt*(tid+1)
+        const int bpt = (nb + nt - 1) / nt;
+        const int btop = nb - 1 - bpt * tid;
+        uint32_t cnt = 0;
+        for (int j = 0; j < bpt; ++j) {
+            const int b = btop - j;
+            if (b >= 0)
+                for (int c = 0; c < HIST_COPIES; ++c) cnt += topk_hist[b * HIST_COPIES + c];
+        }
+        uint32_t tot;
+        uint32_t above = block_exscan(cnt, topk_scan, &tot);
+        if (above < rem && rem <= above + cnt) {
             for (int j = 0; j < bpt; ++j) {
                 const int b = btop - j;
-                if (b >= 0)
-                    for (int c = 0; c < COPIES; ++c) cnt += hist[b * COPIES + c];
-            }
-            int tot;
-            uint32_t above = (uint32_t)block_exscan((int)cnt, scan_sh, &tot);
-            if (above < rem && rem <= above + cnt) {
-                for (int j = 0; j < bpt; ++j) {
-                    const int b = btop - j;
-                    if (b < 0) break;
-                    uint32_t cb = 0;
-                    for (int c = 0; c < COPIES; ++c) cb += hist[b * COPIES + c];
-                    if (rem <= above + cb) {
-                        sh_prefix = prefix | ((uint32_t)b << shift);
-                        sh_rem = rem - above;
-                        break;
-                    }
-                    above += cb;
+                if (b < 0) break;
+                uint32_t cb = 0;
+                for (int c = 0; c < HIST_COPIES; ++c) cb += topk_hist[b * HIST_COPIES + c];
+                if (rem <= above + cb) {
+                    topk_digit[0] = prefix | ((uint32_t)b << shift);
+                    topk_digit[1] = rem - above;
+                    break;
                 }
+                above += cb;
             }
-            __syncthreads();
-            prefix = sh_prefix;
-            rem = sh_rem;
-            mask |= (uint32_t)(nb - 1) << shift;
-            hi = shift;
         }
+        __syncthreads();
+        prefix = topk_digit[0];
+        rem = topk_digit[1];
+        mask |= (uint32_t)(nb - 1) << shift;
+        hi = shift;
     }
-    // prefix = threshold key T (keys above T are all taken); rem = how many
-    // keys equal to T to take, lowest positions first.
-    const int per = (n + nt - 1) / nt;
-    const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
-    int eq = 0;
-    if (!all)
-        for (int i = i0; i < i1; ++i) eq += (uint32_t)keys[i] == prefix;
-    int tot;
-    const int eq_before = block_exscan(eq, scan_sh, &tot);
-    int sel = 0;
-    {
-        int er = eq_before;
-        for (int i = i0; i < i1; ++i) {
-            uint32_t k = keys[i];
-            sel += all || k > prefix || (k == prefix && (uint32_t)(er++) < rem);
-        }
+    T = prefix;
+    rem_out = rem;
+}
+
+// Emit the keys above T and the first rem keys equal to T, in position
+// order, through emit(rank, position) (kk >= n: T = 0, rem = 0 takes every
+// real key).  Equal keys are taken in position order, so the threads before
+// this one took min(eq_before, rem) of them: one scan of the packed counts
+// (gt, eq) gives every thread its first output rank.  Equal keys are only
+// counted when some are taken (rem > 0, so T >= 1 and the key-0 positions are
+// not among them); both counts are then at most 40960, so the packed sums
+// stay below 2^32.
+template <int KPT, class EmitF>
+CSA_DEV void emit_selected(const uint32_t (&kr)[KPT], int kk, uint32_t T, uint32_t rem, EmitF emit)
+{
+    const int tid = threadIdx.x;
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        gt += kr[j] > T;
+        eq += rem > 0u && kr[j] == T;
     }
-    const int out_before = block_exscan(sel, scan_sh, &tot);
-    {
-        int er = eq_before, o = out_before;
-        for (int i = i0; i < i1; ++i) {
-            uint32_t k = keys[i];
-            if (all || k > prefix || (k == prefix && (uint32_t)(er++) < rem)) emit(o++, i);
-        }
+    uint32_t tot;
+    const uint32_t packed = block_exscan(gt | (eq << 16), topk_scan, &tot);
+    const int gt_before = (int)(packed & 0xFFFFu), eq_before = (int)(packed >> 16);
+    int o = gt_before + min(eq_before, (int)rem);
+    const int take_eq = min(max((int)rem - eq_before, 0), (int)eq);   // this thread's equal keys taken
+    // an opaque copy of T: the compiler recomputes the comparisons instead of
+    // keeping 2*KPT lane masks alive (they would spill)
+    uint32_t t2 = T;
+    asm volatile("" : "+v"(t2));
+    int te = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const uint32_t k = kr[j];
+        const bool e = k == t2;
+        if ((k > t2 || (e && te < take_eq)) && o < kk) emit(o++, tid * KPT + j);   // ranks stay below kk
+        te += e;
     }
 }
 
-// Stage 1 (or the only stage): chunk blockIdx.x of row blockIdx.y.
-template <bool BF16>
-__global__ __launch_bounds__(TOPK_THREADS) void topk_chunk_kernel(const void* scores, int ld,
-                                                                  const int32_t* n_valid, int k, int chunk,
-                                                                  int n_chunks, int32_t* out, uint32_t* cand_key,
-                                                                  int32_t* cand_idx)
+// Select the top kk of n keys and emit the selected positions in ascending
+// order through emit(rank, position).
+template <int BITS, int KPT, class EmitF>
+CSA_DEV void select_top(const uint32_t (&kr)[KPT], int n, int kk, EmitF emit, uint32_t lo = 0u)
 {
-    using KT = typename std::conditional<BF16, uint16_t, uint32_t>::type;
-    __shared__ KT keys[BF16 ? CAP16 : CAP32];
-    const int row = blockIdx.y, ch = blockIdx.x;
-    const int V = n_valid[row];
-    const int start = ch * chunk;
-    const int n = max(0, min(V, start + chunk) - start);
-    const int kk = min(k, n);
-    // stage the chunk's keys in LDS; 16-byte loads, four in flight per thread
-    const size_t off = (size_t)row * ld + start;
+    uint32_t T = 0, rem = 0;
+    if (kk < n) find_threshold<BITS, KPT>(kr, kk, lo, T, rem);
+    emit_selected<KPT>(kr, kk, T, rem, emit);
+}
+
+// Stage n scores (starting at element off of the score array) as keys in
+// LDS: 16-byte loads, four in flight per thread, after a scalar prologue up
+// to 16-byte alignment.
+template <bool BF16, class KT>
+CSA_DEV void stage_keys(const void* scores, size_t off, int n, KT* keys)
+{
     constexpr int EPL = BF16 ? 8 : 4;                       // scores per 16-byte load
-    const int head = (int)min((size_t)n, (EPL - off % EPL) % EPL);   // scalar prologue up to alignment
+    const int head = (int)min((size_t)n, (EPL - off % EPL) % EPL);
     const char* base = (const char*)scores + off * (BF16 ? 2 : 4);
     for (int i = threadIdx.x; i < head; i += blockDim.x)
         keys[i] = (KT)(BF16 ? key16(((const uint16_t*)base)[i]) : key32(((const uint32_t*)base)[i]));
@@ -199,15 +221,107 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_chunk_kernel(const void* sc
     }
     for (int i = head + nvec * EPL + threadIdx.x; i < n; i += blockDim.x)
         keys[i] = (KT)(BF16 ? key16(((const uint16_t*)base)[i]) : key32(((const uint32_t*)base)[i]));
+}
+
+// Thread tid's KPT consecutive keys from LDS into registers (16-byte reads:
+// KPT * sizeof(KT) is a multiple of 16 and the array is 16-byte aligned).
+// Positions >= n get key 0.  With RAISE, keys are raised to at least 1 (only
+// the order among NaNs of one sign changes: keys 0 and 1 are both NaN);
+// second-stage candidates are already raised, and their padding keeps key 0.
+template <bool RAISE, int KPT, class KT>
+CSA_DEV void keys_to_regs(const KT* keys, int n, uint32_t (&kr)[KPT])
+{
+    constexpr int PER = 16 / (int)sizeof(KT);
+    static_assert(KPT % PER == 0, "whole 16-byte reads");
+    const uint4* p = (const uint4*)(keys + threadIdx.x * KPT);
+    const int nv = n - (int)threadIdx.x * KPT;              // keys of this thread below n
+#pragma unroll
+    for (int v = 0; v < KPT / PER; ++v) {
+        const uint4 q = p[v];
+        const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            if (sizeof(KT) == 2) {
+                kr[v * PER + 2 * h] = w4[h] & 0xFFFFu;
+                kr[v * PER + 2 * h + 1] = w4[h] >> 16;
+            } else {
+                kr[v * PER + h] = w4[h];
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) kr[j] = j < nv ? (RAISE ? max(kr[j], 1u) : kr[j]) : 0u;
+}
+
+// Stage 1 (or the only stage): chunk blockIdx.x of row blockIdx.y, NT
+// threads of KPT keys each (chunk <= NT * KPT).
+template <bool BF16, int NT, int KPT>
+__global__ __launch_bounds__(NT) void topk_chunk_kernel(const void* scores, int ld, const int32_t* n_valid, int k,
+                                                        int chunk, int n_chunks, int32_t* out, uint32_t* cand_key,
+                                                        int32_t* cand_idx)
+{
+    using KT = typename std::conditional<BF16, uint16_t, uint32_t>::type;
+    __shared__ __attribute__((aligned(16))) KT keys[NT * KPT];
+    const int row = blockIdx.y, ch = blockIdx.x;
+    const int V = n_valid[row];
+    const int start = ch * chunk;
+    const int n = max(0, min(V, start + chunk) - start);
+    const int kk = min(k, n);
+    stage_keys<BF16>(scores, (size_t)row * ld + start, n, keys);
     __syncthreads();
+    uint32_t kr[KPT];
+    keys_to_regs<true, KPT>(keys, n, kr);
     // one stage: final indices; first of two: candidates (key, index) per chunk
     const bool single = n_chunks == 1;
     int32_t* o = single ? out + (size_t)row * k : cand_idx + ((size_t)row * n_chunks + ch) * k;
     uint32_t* ck = single ? nullptr : cand_key + ((size_t)row * n_chunks + ch) * k;
-    select_top<BF16 ? 16 : 32>(keys, n, kk, [&](int r, int i) {
+    auto emit = [&](int r, int i) {
         o[r] = start + i;
-        if (!single) ck[r] = keys[i];
-    });
+        if (!single) ck[r] = max((uint32_t)keys[i], 1u);
+    };
+    constexpr int BITS = BF16 ? 16 : 32;
+    bool done = false;
+    if constexpr (NT == TOPK_THREADS) {
+        // Lower bound first: kk threads hold a key >= the kk-th largest of the
+        // per-thread maxima, so the threshold is at least that bound L.  The
+        // keys >= L (typically a few per cent of the row) are compacted in
+        // position order and the selection runs over them alone, unless there
+        // are more than SURV_CAP of them (ties, adversarial rows).
+        constexpr int SPT = SURV_CAP / NT;
+        __shared__ uint32_t skey[SURV_CAP];
+        __shared__ int32_t spos[SURV_CAP];
+        if (kk < n && kk <= NT) {
+            uint32_t m[1] = {0u};
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) m[0] = max(m[0], kr[j]);
+            uint32_t L, remL;
+            find_threshold<BITS, 1>(m, kk, 0u, L, remL);
+            uint32_t cnt = 0;
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) cnt += kr[j] >= L;
+            uint32_t S;
+            uint32_t at = block_exscan(cnt, topk_scan, &S);
+            if (S <= (uint32_t)SURV_CAP) {                  // workgroup-uniform
+#pragma unroll
+                for (int j = 0; j < KPT; ++j)
+                    if (kr[j] >= L) {
+                        skey[at] = kr[j];
+                        spos[at] = threadIdx.x * KPT + j;
+                        ++at;
+                    }
+                __syncthreads();
+                uint32_t k2[SPT];
+#pragma unroll
+                for (int q = 0; q < SPT; ++q) {
+                    const int i = threadIdx.x * SPT + q;
+                    k2[q] = i < (int)S ? skey[i] : 0u;
+                }
+                select_top<BITS, SPT>(k2, (int)S, kk, [&](int r, int i) { emit(r, spos[i]); }, L);
+                done = true;
+            }
+        }
+    }
+    if (!done) select_top<BITS, KPT>(kr, n, kk, emit);
     for (int r = kk + threadIdx.x; r < k; r += blockDim.x) {
         o[r] = -1;
         if (!single) ck[r] = 0u;
@@ -223,7 +337,8 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_merge_kernel(const int32_t*
                                                                   int32_t* out)
 {
     using KT = typename std::conditional<BF16, uint16_t, uint32_t>::type;
-    __shared__ KT keys[BF16 ? CAP16 : CAP32];
+    constexpr int KPT = BF16 ? KPT16 : KPT32;
+    __shared__ __attribute__((aligned(16))) KT keys[TOPK_THREADS * KPT];
     const int row = blockIdx.x;
     const int V = n_valid[row];
     const int kk = min(k, V);
@@ -234,6 +349,8 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_merge_kernel(const int32_t*
     if (threadIdx.x == 0) floor_sh = 0u;
     for (int i = threadIdx.x; i < n; i += blockDim.x) keys[i] = (KT)ck[i];
     __syncthreads();
+    uint32_t kr[KPT];
+    keys_to_regs<false, KPT>(keys, n, kr);
     // Each chunk holds k keys >= its smallest candidate key (a chunk with
     // fewer valid keys is padded with key 0), so the row's k-th largest key is
     // at least the largest of these minima: keys below it cannot be selected.
@@ -249,20 +366,22 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_merge_kernel(const int32_t*
     // selected positions go to LDS first, so that the index lookups below
     // are issued together rather than one dependent load after another
     __shared__ int32_t spos[MAX_K];
-    select_top<BF16 ? 16 : 32>(keys, n, kk, [&](int r, int i) { spos[r] = i; }, lo);
+    select_top<BF16 ? 16 : 32, KPT>(kr, n, kk, [&](int r, int i) { spos[r] = i; }, lo);
     __syncthreads();
     int32_t* o = out + (size_t)row * k;
     for (int r = threadIdx.x; r < k; r += blockDim.x) o[r] = r < kk ? ci[spos[r]] : -1;
 }
 
-// Chunk length per first-stage workgroup: at most the LDS capacity; when
-// there are few rows the chunks shrink (down to 4k keys each) so that more
-// workgroups share the work, as long as the candidates still fit one
-// second-stage workgroup.
+// Chunk length per first-stage workgroup.  A row that fits one workgroup is
+// one chunk (one stage, no candidates).  Longer rows split into chunks of at
+// most the capacity; when there are few rows the chunks shrink (down to 4k
+// keys each) so that more workgroups share the work, as long as the
+// candidates still fit one second-stage workgroup.
 static int chunk_for(int n_rows, int max_cols, int k, bool bf16)
 {
     const int cap = bf16 ? CAP16 : CAP32;
-    int chunk = max_cols <= cap ? (max_cols > 0 ? max_cols : 1) : cap;
+    if (max_cols <= cap) return max_cols > 0 ? max_cols : 1;
+    int chunk = cap;
     auto nch = [&](int c) { return (max_cols + c - 1) / c; };
     while ((long)n_rows * nch(chunk) < 256 && chunk / 2 >= 4 * k && (long)nch(chunk / 2) * k <= cap) chunk /= 2;
     return chunk;
@@ -284,6 +403,18 @@ bool topk_supported(int max_cols, int k, bool bf16)
     return n_chunks <= 1 || (long)n_chunks * k <= cap;
 }
 
+template <bool BF16>
+static void launch_chunks(hipStream_t st, dim3 grid, int chunk, const void* scores, int ld, const int32_t* n_valid,
+                          int k, int n_chunks, int32_t* out, uint32_t* ck, int32_t* ci)
+{
+    if (chunk <= SMALL_NT * SMALL_KPT)
+        topk_chunk_kernel<BF16, SMALL_NT, SMALL_KPT><<<grid, SMALL_NT, 0, st>>>(scores, ld, n_valid, k, chunk,
+                                                                                n_chunks, out, ck, ci);
+    else
+        topk_chunk_kernel<BF16, TOPK_THREADS, BF16 ? KPT16 : KPT32><<<grid, TOPK_THREADS, 0, st>>>(
+            scores, ld, n_valid, k, chunk, n_chunks, out, ck, ci);
+}
+
 hipError_t launch_topk(hipStream_t st, int score_bf16, int n_rows, const void* scores, int ld,
                        const int32_t* n_valid, int k, int32_t* out, void* ws, int max_cols)
 {
@@ -291,12 +422,11 @@ hipError_t launch_topk(hipStream_t st, int score_bf16, int n_rows, const void* s
     const bool bf = score_bf16 != 0;
     const int chunk = chunk_for(n_rows, max_cols, k, bf);
     const int n_chunks = max(1, (max_cols + chunk - 1) / chunk);
-    const int threads1 = chunk <= 8192 ? 256 : TOPK_THREADS;
     uint32_t* ck = (uint32_t*)ws;
     int32_t* ci = n_chunks > 1 ? (int32_t*)((char*)ws + (size_t)n_rows * n_chunks * k * 4) : nullptr;
     dim3 g1(n_chunks, n_rows);
-    if (bf) topk_chunk_kernel<true><<<g1, threads1, 0, st>>>(scores, ld, n_valid, k, chunk, n_chunks, out, ck, ci);
-    else topk_chunk_kernel<false><<<g1, threads1, 0, st>>>(scores, ld, n_valid, k, chunk, n_chunks, out, ck, ci);
+    if (bf) launch_chunks<true>(st, g1, chunk, scores, ld, n_valid, k, n_chunks, out, ck, ci);
+    else launch_chunks<false>(st, g1, chunk, scores, ld, n_valid, k, n_chunks, out, ck, ci);
     if (n_chunks > 1) {
         if (bf) topk_merge_kernel<true><<<n_rows, TOPK_THREADS, 0, st>>>(n_valid, k, n_chunks, ck, ci, out);
         else topk_merge_kernel<false><<<n_rows, TOPK_THREADS, 0, st>>>(n_valid, k, n_chunks, ck, ci, out);

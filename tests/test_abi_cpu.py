@@ -109,8 +109,9 @@ def test_calls_reject_bad_arguments_before_launch():
 def test_workspace_sizes():
     d = presets.csa_flash_decode()
     assert P.workspace_size(d, abi.OP_COMPRESS, 16) == 16 * (4 * 512 + 4 * 128) * 4
-    assert P.workspace_size(d, abi.OP_TOPK, 4096, 32768, 512) == 0        # many rows: one chunk per row
-    assert P.workspace_size(d, abi.OP_TOPK, 16, 32768, 512) == 16 * 16 * 512 * 8   # few rows: 16 chunks of 2048
+    assert P.workspace_size(d, abi.OP_TOPK, 4096, 32768, 512) == 0        # rows that fit a workgroup: one stage
+    assert P.workspace_size(d, abi.OP_TOPK, 16, 32768, 512) == 0
+    assert P.workspace_size(d, abi.OP_TOPK, 16, 40961, 512) == 16 * 17 * 512 * 8   # few long rows: 17 chunks of 2560
     assert P.workspace_size(d, abi.OP_TOPK, 4, 262144, 1024) == 4 * 26 * 1024 * 8  # 26 chunks of 10240
     assert P.workspace_size(d, abi.OP_ATTENTION, 16, 640) > 0               # few queries: split-KV partials
     assert P.workspace_size(d, abi.OP_ATTENTION, 4096, 640) == 0

@@ -116,11 +116,37 @@ def test_window_ring_rows():
 # a4: top-k, bit-exact on given scores
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("fmt,V,k,levels", [("bf16", [32768, 32768, 32000, 40957], 512, 64),
+                                            ("bf16", [32768, 32768, 32000, 40957], 512, 6),
+                                            ("bf16", [32768, 20000, 4000], 1024, 300)])
+def test_topk_quantised_scores(fmt, V, k, levels):
+    """Scores on a few levels: long tie runs at the threshold (the lower-bound
+    pass keeps few or very many keys)."""
+    _flush(f"topk quantised {fmt} k={k} V={V} levels={levels}")
+    g = synth.rng(103)
+    ld = max(V)
+    sc = O.bf16_round(g.integers(0, levels, size=(len(V), ld)).astype(np.float32) / 4)
+    nv = np.array(V, np.int32)
+    want = O.topk(sc, nv, k)
+    scores = to_dev(sc, torch.bfloat16)
+    out = torch.full((len(V), k), -7, dtype=torch.int32, device="cuda")
+    desc = presets.csa_flash_decode()
+    ws = torch.empty(max(abi.workspace_size(desc, abi.OP_TOPK, len(V), ld, k), 1), dtype=torch.uint8, device="cuda")
+    abi.topk_select(abi.ACT_BF16, len(V), scores, ld, i32(nv), k, out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for t in range(len(V)):
+        assert np.array_equal(got[t], want[t]), f"row {t} (V={V[t]}) differs"
+
+
 @pytest.mark.parametrize("fmt,V,k", [("bf16", [0, 5, 512, 513, 4096, 32768, 100000, 1000], 512),
                                      ("f32", [64, 63, 1, 0, 700, 70000], 64),
                                      ("bf16", [262144, 33000, 1024, 1025], 1024),
                                      ("bf16", [3, 2000], 2048),
-                                     ("bf16", [32768, 32768, 32768, 20000], 512)])
+                                     ("bf16", [32768, 32768, 32768, 20000], 512),
+                                     ("bf16", [40957, 40000, 32784, 7], 512),
+                                     ("f32", [20000, 15000, 9000, 20000], 256),
+                                     ("f32", [40000 - 37 * i for i in range(128)], 256)])
 def test_topk_exact(fmt, V, k):
     _flush(f"topk {fmt} k={k} V={V}")
     g = synth.rng(102)
