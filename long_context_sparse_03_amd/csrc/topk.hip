@@ -4,12 +4,16 @@
 //
 // Scores become order-preserving unsigned keys (sign-magnitude flip; -0 and
 // +0 map to the same key), so selection is integer work and bit-exact.  The
-// order is (key descending, index ascending): the k-th element is found by
-// an MSB-first radix select with 8-bit digits (histograms in LDS), and the
-// selected set is compacted in index order with two block-wide prefix sums,
-// which also breaks ties at the threshold toward lower indices.
+// order is (key descending, index ascending).  A workgroup holds its keys in
+// registers, each thread a run of consecutive positions.  The k-th key is
+// found by an MSB-first radix select with 4-bit digits whose counts come from
+// wave ballots (one barrier per digit), and the selected set is emitted in
+// index order from one block-wide scan, which also breaks ties at the
+// threshold toward lower indices.  Before the radix select, a lower bound
+// from the per-thread maxima usually leaves only a few per cent of the keys
+// in play.
 //
-// Rows longer than one chunk run in two stages: each chunk keeps its own
+// Rows longer than one workgroup run in two stages: each chunk keeps its own
 // top-k (in index order) as candidates, and a second pass selects from the
 // concatenated candidates.  Every element of the global top-k is in its
 // chunk's top-k under the same total order, so the result is the same.
@@ -21,13 +25,13 @@
 namespace csa {
 
 constexpr int TOPK_THREADS = 1024;
-constexpr int MAX_K = 2048;                                  // largest k the entry points accept
-constexpr int CAP16 = 40960;             // bf16 keys per workgroup (16-bit keys in LDS)
-constexpr int CAP32 = 20480;             // fp32 keys per workgroup
+constexpr int MAX_K = 2048;                   // largest k the entry points accept
+constexpr int CAP16 = 40960;                  // bf16 keys per workgroup
+constexpr int CAP32 = 20480;                  // fp32 keys per workgroup
 constexpr int KPT16 = CAP16 / TOPK_THREADS;   // keys per thread at the capacity
 constexpr int KPT32 = CAP32 / TOPK_THREADS;
-constexpr int SMALL_NT = 256, SMALL_KPT = 32;  // workgroups of up to 8192 keys
-constexpr int SURV_CAP = 4096;                 // keys kept after the lower bound (1024-thread workgroups)
+constexpr int SMALL_NT = 256, SMALL_KPT = 32; // workgroups of up to 8192 keys
+constexpr int SURV_CAP = 4096;                // keys kept after the lower bound (1024-thread workgroups)
 
 // Order-preserving key of a score: sign-magnitude flip; -0 and +0 share the key.
 CSA_DEV uint32_t key16(uint32_t b)
@@ -42,109 +46,260 @@ CSA_DEV uint32_t key32(uint32_t u)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix sum over the block (fixed order, modulo 2^32); *total
-// gets the sum.
-CSA_DEV uint32_t block_exscan(uint32_t v, uint32_t* sh, uint32_t* total)
+// Inclusive prefix sum over the 64 lanes of a wave: steps of 1, 2, 4, 8
+// within each row of 16 lanes, then the row totals carried across rows
+// (DPP row shifts and row broadcasts; lanes without a source add 0).
+CSA_DEV uint32_t wave_incl_scan(uint32_t v)
 {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    uint32_t inc = v;
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = (uint32_t)__shfl_up((int)inc, o, 64);
-        if (lane >= o) inc += y;
-    }
-    __syncthreads();
-    if (lane == 63) sh[w] = inc;
-    __syncthreads();
-    uint32_t off = 0, tot = 0;
-    for (int i = 0; i < nw; ++i) {
-        if (i < w) off += sh[i];
-        tot += sh[i];
-    }
-    *total = tot;
-    return off + inc - v;
+    int x = (int)v;
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15 into rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31 into rows 2, 3
+    return (uint32_t)x;
 }
 
-// Selection works on keys held in registers: thread tid holds the keys of
-// positions tid*KPT .. tid*KPT+KPT-1, so the passes below read no memory and
-// a thread's positions are consecutive; positions >= n hold key 0, and every
-// real key is >= 1 (see keys_to_regs), so kk <= n keeps them out of the
-// selection.  The order is (key descending, position ascending).
-constexpr int HIST_COPIES = 4;
-__shared__ uint32_t topk_hist[2048 * HIST_COPIES];  // digit histograms (four interleaved copies)
-__shared__ uint32_t topk_scan[32];                  // block scan partials
-__shared__ uint32_t topk_digit[2];                  // chosen prefix, remaining rank
+// Exclusive prefix sums over the workgroup (fixed order, modulo 2^32), one
+// barrier each: the wave totals alternate between two LDS slots, and a slot
+// is written again only after every wave has passed the barrier of the scan
+// in between.
+struct BlockScan {
+    int parity = 0;
+    CSA_DEV uint32_t exscan(uint32_t v, uint32_t* total)
+    {
+        __shared__ uint32_t part[2][16];
+        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+        const uint32_t inc = wave_incl_scan(v);
+        if (lane == 63) part[parity][w] = inc;
+        __syncthreads();
+        uint32_t off = 0, tot = 0;
+        for (int i = 0; i < nw; ++i) {
+            const uint32_t x = part[parity][i];
+            tot += x;
+            off += i < w ? x : 0u;
+        }
+        parity ^= 1;
+        *total = tot;
+        return off + inc - v;
+    }
+};
 
-// Threshold of the top kk (kk < number of real keys): T = the kk-th largest
+constexpr int HIST_COPIES = 4;
+__shared__ uint32_t topk_hist[2048 * HIST_COPIES];  // range histograms (four interleaved copies)
+__shared__ uint32_t topk_digit[2];                  // chosen bin, remaining rank
+
+// Selection works on keys held in registers: thread tid holds the keys of
+// positions tid*KPT .. tid*KPT+KPT-1, so a thread's positions are
+// consecutive; positions >= n hold key 0, and every real key is >= 1 (see
+// raise_keys), so kk <= n keeps them out of the selection.
+
+// Threshold of the top kk (at least kk keys >= lo): T = the kk-th largest
 // key, rem = how many keys equal to T belong to the top kk.  BITS = key width
-// (16 or 32).  The threshold is found MSB first with an 11-bit first digit
-// (sign, exponent and the top mantissa bits, so that clustered scores spread
-// over many bins).  Keys below lo are known to lie under the threshold: the
-// histograms skip them (the caller guarantees at least kk keys >= lo).
+// (16 or 32).  Digits of 4 bits from the top.  Each wave counts its keys per
+// digit value into its own 16 LDS counters (LDS atomics for a few keys per
+// thread; per-thread 6-bit counters summed over the wave for many), the
+// waves' counts are summed after one barrier, and every wave takes the same
+// decision with lane-parallel arithmetic (a scan over the 16 digit totals and
+// one ballot).  The counters alternate between two buffers, as in BlockScan.
+// Keys below lo are known to lie under the threshold and are not counted.
 template <int BITS, int KPT>
 CSA_DEV void find_threshold(const uint32_t (&kr)[KPT], int kk, uint32_t lo, uint32_t& T, uint32_t& rem_out)
 {
-    const int tid = threadIdx.x, nt = blockDim.x;
+    __shared__ uint32_t cnt[2][16][16];          // [buffer][wave][digit value]
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
     uint32_t prefix = 0, mask = 0, rem = (uint32_t)kk;
-    int hi = BITS;                                              // digits: 11, then 5 (16-bit) or 11, 10 (32-bit)
-    while (hi > 0) {
-        const int width = hi == BITS ? 11 : (hi > 11 ? 11 : hi);
-        const int shift = hi - width;
-        const int nb = 1 << width;
-        for (int b = tid; b < nb * HIST_COPIES; b += nt) topk_hist[b] = 0;
-        __syncthreads();
+#pragma unroll 1
+    for (int r = 0; r < BITS / 4; ++r) {
+        const int shift = BITS - 4 * (r + 1);
+        auto digit = [&](uint32_t k) { return (k >= lo && (k & mask) == prefix) ? (k >> shift) & 15u : 16u; };
+        uint32_t* my = cnt[r & 1][w];
+        if constexpr (KPT <= 4) {
+            // a wave's LDS operations run in order: clear, then count
+            if (lane < 16) my[lane] = 0u;
 #pragma unroll
-        for (int j = 0; j < KPT; ++j) {
-            const uint32_t k = kr[j];
-            if (k >= lo && (k & mask) == prefix)
-                atomicAdd(&topk_hist[((k >> shift) & (uint32_t)(nb - 1)) * HIST_COPIES + (tid & 3)], 1u);
-        }
-        __syncthreads();
-        // bpt consecutive bins per thread, from the top: thread tid owns
-        // bins nb-1-bpt*tid down to nb-bpt*(tid+1)
-        const int bpt = (nb + nt - 1) / nt;
-        const int btop = nb - 1 - bpt * tid;
-        uint32_t cnt = 0;
-        for (int j = 0; j < bpt; ++j) {
-            const int b = btop - j;
-            if (b >= 0)
-                for (int c = 0; c < HIST_COPIES; ++c) cnt += topk_hist[b * HIST_COPIES + c];
-        }
-        uint32_t tot;
-        uint32_t above = block_exscan(cnt, topk_scan, &tot);
-        if (above < rem && rem <= above + cnt) {
-            for (int j = 0; j < bpt; ++j) {
-                const int b = btop - j;
-                if (b < 0) break;
-                uint32_t cb = 0;
-                for (int c = 0; c < HIST_COPIES; ++c) cb += topk_hist[b * HIST_COPIES + c];
-                if (rem <= above + cb) {
-                    topk_digit[0] = prefix | ((uint32_t)b << shift);
-                    topk_digit[1] = rem - above;
-                    break;
-                }
-                above += cb;
+            for (int j = 0; j < KPT; ++j) {
+                const uint32_t d = digit(kr[j]);
+                if (d < 16u) atomicAdd(&my[d], 1u);
+            }
+        } else {
+            // per-thread counts in 6-bit fields (digit values 0-9 in c0,
+            // 10-15 in c1; KPT <= 63), then one wave sum per digit value
+            static_assert(KPT <= 63, "6-bit counters");
+            uint64_t c0 = 0, c1 = 0;
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) {
+                const uint32_t d = digit(kr[j]);
+                c0 += d < 10u ? 1ull << (6 * d) : 0ull;
+                c1 += d - 10u < 6u ? 1ull << (6 * (d - 10u)) : 0ull;
+            }
+#pragma unroll 1
+            for (int v = 0; v < 16; ++v) {
+                const uint32_t x = (uint32_t)((v < 10 ? c0 >> (6 * v) : c1 >> (6 * (v - 10))) & 63u);
+                const uint32_t sum = wave_incl_scan(x);
+                if (lane == 63) my[v] = sum;
             }
         }
         __syncthreads();
-        prefix = topk_digit[0];
-        rem = topk_digit[1];
-        mask |= (uint32_t)(nb - 1) << shift;
-        hi = shift;
+        uint32_t bin = 0;                        // lane v < 16: the workgroup's count of digit v
+        if (lane < 16)
+            for (int i = 0; i < nw; ++i) bin += cnt[r & 1][i][lane];
+        // keys in digits above v: total - inclusive prefix up to v; the digit
+        // holding the rem-th largest key is the one lane where rem falls
+        const uint32_t incl = wave_incl_scan(bin);
+        const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 15);
+        const uint32_t above = total - incl;
+        const uint64_t hit = __ballot(lane < 16 && above < rem && rem <= above + bin);
+        const int d = (int)__builtin_ctzll(hit);
+        prefix |= (uint32_t)d << shift;
+        rem -= (uint32_t)__builtin_amdgcn_readlane((int)above, d);
+        mask |= 15u << shift;
     }
     T = prefix;
     rem_out = rem;
 }
 
+// Running maximum / minimum over the lanes of a wave, in DPP steps as in
+// wave_incl_scan (lanes without a source see the identity); lane 63 ends
+// with the wave's extreme.
+CSA_DEV uint32_t wave_max63(uint32_t v)
+{
+    int x = (int)v;
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false));
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false));
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false));
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false));
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false));
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false));
+    return (uint32_t)x;
+}
+
+CSA_DEV uint32_t wave_min63(uint32_t v)
+{
+    int x = (int)v;
+    x = (int)min((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(-1, x, 0x111, 0xf, 0xf, false));
+    x = (int)min((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(-1, x, 0x112, 0xf, 0xf, false));
+    x = (int)min((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(-1, x, 0x114, 0xf, 0xf, false));
+    x = (int)min((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(-1, x, 0x118, 0xf, 0xf, false));
+    x = (int)min((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(-1, x, 0x142, 0xa, 0xf, false));
+    x = (int)min((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(-1, x, 0x143, 0xc, 0xf, false));
+    return (uint32_t)x;
+}
+
+// Largest and smallest value over the workgroup (DPP within waves, then the
+// wave results through LDS after one barrier; the slots alternate as in
+// BlockScan, whose parity this shares).
+CSA_DEV void block_max_min(uint32_t& mx, uint32_t& mn, BlockScan& bs)
+{
+    __shared__ uint32_t part[2][2][16];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const uint32_t a = wave_max63(mx), b = wave_min63(mn);
+    if (lane == 63) {
+        part[bs.parity][0][w] = a;
+        part[bs.parity][1][w] = b;
+    }
+    __syncthreads();
+    uint32_t x = 0u, y = 0xFFFFFFFFu;
+    for (int i = 0; i < nw; ++i) {
+        x = max(x, part[bs.parity][0][i]);
+        y = min(y, part[bs.parity][1][i]);
+    }
+    bs.parity ^= 1;
+    mx = x;
+    mn = y;
+}
+
+// Histogram select over the keys in [lo, hi] (others ignored; at least rem
+// of them): bins of 2^shift consecutive keys from lo, at most 2048 of them,
+// counted with LDS atomics (four interleaved copies).  Returns the bin
+// holding the rem-th largest key and updates rem to its rank inside the bin.
+// Keys spread over the range, so few lanes hit one counter at a time.
+template <int KPT>
+CSA_DEV void range_bin(const uint32_t (&kr)[KPT], uint32_t lo, uint32_t hi, int shift, uint32_t& rem, BlockScan& bs,
+                       uint32_t& bin)
+{
+    const int tid = threadIdx.x, nt = blockDim.x;
+    const int nb = (int)((hi - lo) >> shift) + 1;              // <= 2048
+    for (int b = tid; b < nb * HIST_COPIES; b += nt) topk_hist[b] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const uint32_t k = kr[j];
+        if (k >= lo && k <= hi) atomicAdd(&topk_hist[((k - lo) >> shift) * HIST_COPIES + (tid & 3)], 1u);
+    }
+    __syncthreads();
+    // bpt consecutive bins per thread, from the top: thread tid owns bins
+    // nb-1-bpt*tid down to nb-bpt*(tid+1)
+    const int bpt = (nb + nt - 1) / nt;
+    const int btop = nb - 1 - bpt * tid;
+    uint32_t cnt = 0;
+    for (int j = 0; j < bpt; ++j) {
+        const int b = btop - j;
+        if (b >= 0)
+            for (int c = 0; c < HIST_COPIES; ++c) cnt += topk_hist[b * HIST_COPIES + c];
+    }
+    uint32_t tot;
+    uint32_t above = bs.exscan(cnt, &tot);
+    if (above < rem && rem <= above + cnt) {
+        for (int j = 0; j < bpt; ++j) {
+            const int b = btop - j;
+            if (b < 0) break;
+            uint32_t cb = 0;
+            for (int c = 0; c < HIST_COPIES; ++c) cb += topk_hist[b * HIST_COPIES + c];
+            if (rem <= above + cb) {
+                topk_digit[0] = (uint32_t)b;
+                topk_digit[1] = rem - above;
+                break;
+            }
+            above += cb;
+        }
+    }
+    __syncthreads();
+    bin = topk_digit[0];
+    rem = topk_digit[1];
+}
+
+// Bins of 2^shift keys covering [lo, hi] in at most 2048 bins.
+CSA_DEV int range_shift(uint32_t lo, uint32_t hi)
+{
+    int shift = 0;
+    while (((hi - lo) >> shift) >= 2048u) ++shift;
+    return shift;
+}
+
+// Exact threshold of the top rem keys among those in [lo, hi]: narrow the
+// range to the selected bin until bins are single keys (one pass when the
+// range spans at most 2048 keys).
+template <int KPT>
+CSA_DEV void range_threshold(const uint32_t (&kr)[KPT], uint32_t lo, uint32_t hi, uint32_t rem, BlockScan& bs,
+                             uint32_t& T, uint32_t& rem_out)
+{
+    while (true) {
+        const int shift = range_shift(lo, hi);
+        uint32_t b;
+        range_bin<KPT>(kr, lo, hi, shift, rem, bs, b);
+        const uint32_t nlo = lo + (b << shift);
+        if (shift == 0) {
+            T = nlo;
+            rem_out = rem;
+            return;
+        }
+        hi = min(hi, nlo + ((1u << shift) - 1u));
+        lo = nlo;
+    }
+}
+
 // Emit the keys above T and the first rem keys equal to T, in position
-// order, through emit(rank, position) (kk >= n: T = 0, rem = 0 takes every
-// real key).  Equal keys are taken in position order, so the threads before
-// this one took min(eq_before, rem) of them: one scan of the packed counts
-// (gt, eq) gives every thread its first output rank.  Equal keys are only
-// counted when some are taken (rem > 0, so T >= 1 and the key-0 positions are
-// not among them); both counts are then at most 40960, so the packed sums
-// stay below 2^32.
+// order, through emit(rank, position, key) (T = 0, rem = 0 takes every real
+// key).  Equal keys are taken in position order, so the threads before this
+// one took min(eq_before, rem) of them: one scan of the packed counts (gt,
+// eq) gives every thread its first output rank.  Equal keys are only counted
+// when some are taken (rem > 0, so T >= 1 and the key-0 positions are not
+// among them); both counts are then at most 40960, so the packed sums stay
+// below 2^32.
 template <int KPT, class EmitF>
-CSA_DEV void emit_selected(const uint32_t (&kr)[KPT], int kk, uint32_t T, uint32_t rem, EmitF emit)
+CSA_DEV void emit_selected(const uint32_t (&kr)[KPT], int kk, uint32_t T, uint32_t rem, BlockScan& bs, EmitF emit)
 {
     const int tid = threadIdx.x;
     uint32_t gt = 0, eq = 0;
@@ -154,7 +309,7 @@ CSA_DEV void emit_selected(const uint32_t (&kr)[KPT], int kk, uint32_t T, uint32
         eq += rem > 0u && kr[j] == T;
     }
     uint32_t tot;
-    const uint32_t packed = block_exscan(gt | (eq << 16), topk_scan, &tot);
+    const uint32_t packed = bs.exscan(gt | (eq << 16), &tot);
     const int gt_before = (int)(packed & 0xFFFFu), eq_before = (int)(packed >> 16);
     int o = gt_before + min(eq_before, (int)rem);
     const int take_eq = min(max((int)rem - eq_before, 0), (int)eq);   // this thread's equal keys taken
@@ -167,19 +322,68 @@ CSA_DEV void emit_selected(const uint32_t (&kr)[KPT], int kk, uint32_t T, uint32
     for (int j = 0; j < KPT; ++j) {
         const uint32_t k = kr[j];
         const bool e = k == t2;
-        if ((k > t2 || (e && te < take_eq)) && o < kk) emit(o++, tid * KPT + j);   // ranks stay below kk
+        if ((k > t2 || (e && te < take_eq)) && o < kk) emit(o++, tid * KPT + j, k);   // ranks stay below kk
         te += e;
     }
 }
 
 // Select the top kk of n keys and emit the selected positions in ascending
-// order through emit(rank, position).
+// order through emit(rank, position, key).
 template <int BITS, int KPT, class EmitF>
-CSA_DEV void select_top(const uint32_t (&kr)[KPT], int n, int kk, EmitF emit, uint32_t lo = 0u)
+CSA_DEV void select_top(const uint32_t (&kr)[KPT], int n, int kk, BlockScan& bs, EmitF emit, uint32_t lo = 0u)
 {
     uint32_t T = 0, rem = 0;
     if (kk < n) find_threshold<BITS, KPT>(kr, kk, lo, T, rem);
-    emit_selected<KPT>(kr, kk, T, rem, emit);
+    emit_selected<KPT>(kr, kk, T, rem, bs, emit);
+}
+
+// Positions >= n get key 0.  With RAISE, keys are raised to at least 1 (only
+// the order among NaNs of one sign changes: keys 0 and 1 are both NaN);
+// second-stage candidates are already raised, and their padding keeps key 0.
+template <bool RAISE, int KPT>
+CSA_DEV void raise_keys(int n, uint32_t (&kr)[KPT])
+{
+    const int nv = n - (int)threadIdx.x * KPT;              // keys of this thread below n
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) kr[j] = j < nv ? (RAISE ? max(kr[j], 1u) : kr[j]) : 0u;
+}
+
+// Unpack one 16-byte vector of scores (BF16: 8 bf16, else 4 fp32) into keys.
+template <bool BF16, int KPT>
+CSA_DEV void unpack_keys(uint4 q, int at, uint32_t (&kr)[KPT])
+{
+    const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        if (BF16) {
+            kr[at + 2 * h] = key16(w4[h] & 0xFFFFu);
+            kr[at + 2 * h + 1] = key16(w4[h] >> 16);
+        } else {
+            kr[at + h] = key32(w4[h]);
+        }
+    }
+}
+
+// Scores straight into registers (16-byte aligned run whose last, partial
+// vector lies inside the row): thread tid reads the vectors of its KPT
+// positions; vectors past the run are clamped to its last one and masked.
+template <bool BF16, int KPT>
+CSA_DEV void load_keys_direct(const void* scores, size_t off, int n, uint32_t (&kr)[KPT])
+{
+    constexpr int EPL = BF16 ? 8 : 4, NV = KPT / EPL;
+    static_assert(KPT % EPL == 0, "whole vectors per thread");
+    const int nvec = (n + EPL - 1) / EPL;
+    const char* base = (const char*)scores + off * (BF16 ? 2 : 4);
+    uint4 q[NV];
+    if (nvec > 0) {                                         // workgroup-uniform
+#pragma unroll
+        for (int v = 0; v < NV; ++v) q[v] = ld16(base + (size_t)min((int)threadIdx.x * NV + v, nvec - 1) * 16);
+    } else {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) q[v] = make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int v = 0; v < NV; ++v) unpack_keys<BF16>(q[v], v * EPL, kr);
 }
 
 // Stage n scores (starting at element off of the score array) as keys in
@@ -225,16 +429,12 @@ CSA_DEV void stage_keys(const void* scores, size_t off, int n, KT* keys)
 
 // Thread tid's KPT consecutive keys from LDS into registers (16-byte reads:
 // KPT * sizeof(KT) is a multiple of 16 and the array is 16-byte aligned).
-// Positions >= n get key 0.  With RAISE, keys are raised to at least 1 (only
-// the order among NaNs of one sign changes: keys 0 and 1 are both NaN);
-// second-stage candidates are already raised, and their padding keeps key 0.
-template <bool RAISE, int KPT, class KT>
-CSA_DEV void keys_to_regs(const KT* keys, int n, uint32_t (&kr)[KPT])
+template <int KPT, class KT>
+CSA_DEV void keys_to_regs(const KT* keys, uint32_t (&kr)[KPT])
 {
     constexpr int PER = 16 / (int)sizeof(KT);
     static_assert(KPT % PER == 0, "whole 16-byte reads");
     const uint4* p = (const uint4*)(keys + threadIdx.x * KPT);
-    const int nv = n - (int)threadIdx.x * KPT;              // keys of this thread below n
 #pragma unroll
     for (int v = 0; v < KPT / PER; ++v) {
         const uint4 q = p[v];
@@ -249,8 +449,6 @@ CSA_DEV void keys_to_regs(const KT* keys, int n, uint32_t (&kr)[KPT])
             }
         }
     }
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) kr[j] = j < nv ? (RAISE ? max(kr[j], 1u) : kr[j]) : 0u;
 }
 
 // Stage 1 (or the only stage): chunk blockIdx.x of row blockIdx.y, NT
@@ -261,46 +459,63 @@ __global__ __launch_bounds__(NT) void topk_chunk_kernel(const void* scores, int 
                                                         int32_t* cand_idx)
 {
     using KT = typename std::conditional<BF16, uint16_t, uint32_t>::type;
-    __shared__ __attribute__((aligned(16))) KT keys[NT * KPT];
+    constexpr int BITS = BF16 ? 16 : 32;
+    constexpr int EPL = BF16 ? 8 : 4;
     const int row = blockIdx.y, ch = blockIdx.x;
     const int V = n_valid[row];
     const int start = ch * chunk;
     const int n = max(0, min(V, start + chunk) - start);
     const int kk = min(k, n);
-    stage_keys<BF16>(scores, (size_t)row * ld + start, n, keys);
-    __syncthreads();
+    const size_t off = (size_t)row * ld + start;
     uint32_t kr[KPT];
-    keys_to_regs<true, KPT>(keys, n, kr);
+    // 16-byte aligned run whose partial last vector stays inside the row:
+    // scores straight into registers; otherwise staged through LDS
+    const bool aligned = ((uintptr_t)scores + off * (BF16 ? 2 : 4)) % 16 == 0;
+    if (aligned && (n % EPL == 0 || start + (n / EPL + 1) * EPL <= ld)) {
+        load_keys_direct<BF16, KPT>(scores, off, n, kr);
+    } else {
+        __shared__ __attribute__((aligned(16))) KT keys[NT * KPT];
+        stage_keys<BF16>(scores, off, n, keys);
+        __syncthreads();
+        keys_to_regs<KPT>(keys, kr);
+    }
+    raise_keys<true, KPT>(n, kr);
     // one stage: final indices; first of two: candidates (key, index) per chunk
     const bool single = n_chunks == 1;
     int32_t* o = single ? out + (size_t)row * k : cand_idx + ((size_t)row * n_chunks + ch) * k;
     uint32_t* ck = single ? nullptr : cand_key + ((size_t)row * n_chunks + ch) * k;
-    auto emit = [&](int r, int i) {
+    auto emit = [&](int r, int i, uint32_t key) {
         o[r] = start + i;
-        if (!single) ck[r] = max((uint32_t)keys[i], 1u);
+        if (!single) ck[r] = key;
     };
-    constexpr int BITS = BF16 ? 16 : 32;
+    BlockScan bs;
     bool done = false;
     if constexpr (NT == TOPK_THREADS) {
-        // Lower bound first: kk threads hold a key >= the kk-th largest of the
-        // per-thread maxima, so the threshold is at least that bound L.  The
-        // keys >= L (typically a few per cent of the row) are compacted in
-        // position order and the selection runs over them alone, unless there
-        // are more than SURV_CAP of them (ties, adversarial rows).
+        // Lower bound first: when kk threads hold a key >= L, the threshold
+        // is at least L.  L is the lower edge of the histogram bin (over the
+        // range of the per-thread maxima) that holds the kk-th largest
+        // maximum.  The keys >= L (typically a few per cent of the row) are
+        // compacted in position order and the exact selection runs over them
+        // alone, unless there are more than SURV_CAP of them (ties,
+        // adversarial rows).
         constexpr int SPT = SURV_CAP / NT;
         __shared__ uint32_t skey[SURV_CAP];
         __shared__ int32_t spos[SURV_CAP];
-        if (kk < n && kk <= NT) {
-            uint32_t m[1] = {0u};
+        if (kk < n && kk <= (n + KPT - 1) / KPT) {          // workgroup-uniform: kk threads hold keys
+            uint32_t m = 0u;
 #pragma unroll
-            for (int j = 0; j < KPT; ++j) m[0] = max(m[0], kr[j]);
-            uint32_t L, remL;
-            find_threshold<BITS, 1>(m, kk, 0u, L, remL);
+            for (int j = 0; j < KPT; ++j) m = max(m, kr[j]);
+            uint32_t kmax = m, mmin = m > 0u ? m : 0xFFFFFFFFu;   // smallest maximum of a thread with keys
+            block_max_min(kmax, mmin, bs);
+            uint32_t mr[1] = {m}, remL = (uint32_t)kk, b;
+            const int shift = range_shift(mmin, kmax);
+            range_bin<1>(mr, mmin, kmax, shift, remL, bs, b);
+            const uint32_t L = mmin + (b << shift);
             uint32_t cnt = 0;
 #pragma unroll
             for (int j = 0; j < KPT; ++j) cnt += kr[j] >= L;
             uint32_t S;
-            uint32_t at = block_exscan(cnt, topk_scan, &S);
+            uint32_t at = bs.exscan(cnt, &S);
             if (S <= (uint32_t)SURV_CAP) {                  // workgroup-uniform
 #pragma unroll
                 for (int j = 0; j < KPT; ++j)
@@ -316,12 +531,14 @@ __global__ __launch_bounds__(NT) void topk_chunk_kernel(const void* scores, int 
                     const int i = threadIdx.x * SPT + q;
                     k2[q] = i < (int)S ? skey[i] : 0u;
                 }
-                select_top<BITS, SPT>(k2, (int)S, kk, [&](int r, int i) { emit(r, spos[i]); }, L);
+                uint32_t T = 0, rem = 0;
+                if (kk < (int)S) range_threshold<SPT>(k2, L, kmax, (uint32_t)kk, bs, T, rem);
+                emit_selected<SPT>(k2, kk, T, rem, bs, [&](int r, int i, uint32_t key) { emit(r, spos[i], key); });
                 done = true;
             }
         }
     }
-    if (!done) select_top<BITS, KPT>(kr, n, kk, emit);
+    if (!done) select_top<BITS, KPT>(kr, n, kk, bs, emit);
     for (int r = kk + threadIdx.x; r < k; r += blockDim.x) {
         o[r] = -1;
         if (!single) ck[r] = 0u;
@@ -350,7 +567,8 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_merge_kernel(const int32_t*
     for (int i = threadIdx.x; i < n; i += blockDim.x) keys[i] = (KT)ck[i];
     __syncthreads();
     uint32_t kr[KPT];
-    keys_to_regs<false, KPT>(keys, n, kr);
+    keys_to_regs<KPT>(keys, kr);
+    raise_keys<false, KPT>(n, kr);
     // Each chunk holds k keys >= its smallest candidate key (a chunk with
     // fewer valid keys is padded with key 0), so the row's k-th largest key is
     // at least the largest of these minima: keys below it cannot be selected.
@@ -366,7 +584,8 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_merge_kernel(const int32_t*
     // selected positions go to LDS first, so that the index lookups below
     // are issued together rather than one dependent load after another
     __shared__ int32_t spos[MAX_K];
-    select_top<BF16 ? 16 : 32, KPT>(kr, n, kk, [&](int r, int i) { spos[r] = i; }, lo);
+    BlockScan bs;
+    select_top<BF16 ? 16 : 32, KPT>(kr, n, kk, bs, [&](int r, int i, uint32_t) { spos[r] = i; }, lo);
     __syncthreads();
     int32_t* o = out + (size_t)row * k;
     for (int r = threadIdx.x; r < k; r += blockDim.x) o[r] = r < kk ? ci[spos[r]] : -1;
