@@ -389,6 +389,7 @@ static int attention_common(void* stream, const csa_layer_desc* layer, const csa
     a.ws = (float*)ws;
     a.n_tokens = n_tokens;
     a.rows_max = rows;
+    a.one_per_req = batch->max_new <= 1 && n_tokens == batch->n_req;
     return hip_status(csa::launch_attention((hipStream_t)stream, a), "attention launch");
 }
 

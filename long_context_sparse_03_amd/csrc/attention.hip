@@ -557,6 +557,400 @@ __global__ __launch_bounds__((AttnCfg<KVF, C, R, HT>::NT)) void attn_kernel(Attn
     }
 }
 
+// FP8 entry records with bf16 queries (the serving shapes): two waves per
+// head tile.  Waves w and w + HT own heads 16w .. 16w+15 of the group: each
+// contracts every channel of the tile for those heads (S^T = K . Q^T) and
+// runs their online softmax in registers (the pair computes the same
+// values), and each accumulates the output of one half of the channels
+// (O^T = V^T . P^T), so the waves never exchange logits or weights.  Tiles
+// are double-buffered in LDS: the rows of tile n+1 are loaded into
+// registers while tile n computes and stored into the other buffer, and one
+// barrier per tile publishes them.  Each lane keeps the output of its head
+// for 4 channels of every 16-channel group of its half (C/8 fp32
+// accumulators), so two workgroups fit on a compute unit.
+template <int C, int R, int HT>
+__global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
+{
+    constexpr int NWV = 2 * HT;                                // waves
+    constexpr int NF = C - R, KP = C + 8, NT = 64 * NWV, RPW = 32 / NWV;
+    constexpr int KS = C / 32;                                 // 16x16x32 steps over the channels
+    constexpr int KSN = NF / 32;                               // ... of them over FP8 channels
+    constexpr int DT = C / 16;                                 // 16-channel output tiles
+    constexpr int DTN = NF / 16;                               // ... of them FP8 value channels
+    constexpr int DTH = DT / 2;                                // ... per wave (its half of the channels)
+    constexpr int WB = 2 * C;                                  // bytes of a window row (bf16)
+    constexpr int EB = NF + 2 * R;                             // bytes of an FP8 entry record
+    constexpr int NCH = NF / 16;                               // 16-byte chunks of FP8 codes
+    constexpr int DESC = NT;                                   // rows described at a time
+    static_assert(NF % 32 == 0 && R % 32 == 0 && WB <= 1024 && 32 % NWV == 0 && DESC % NT == 0 && DT % 2 == 0,
+                  "shape");
+
+    __shared__ __attribute__((aligned(16))) uint16_t Kt[2][32 * KP];
+    __shared__ float tscl[2][32];                              // per buffer: row scales ...
+    __shared__ int tval[2][32];                                // ... and valid rows
+    __shared__ const char* rptr[DESC];                         // row start (null: masked row)
+    __shared__ const char* rblk[DESC];                         // FP8 entry rows: their block (scale at byte 0)
+    __shared__ float rcs[R / 2], rsn[R / 2];
+    __shared__ int cu_sh[257];
+    __shared__ __attribute__((aligned(16))) float gam[C];      // query norm gains
+
+    const int lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ht = wave % HT, half = wave / HT;               // head tile, channel half
+    for (int j = threadIdx.x; j < C; j += NT) gam[j] = a.q_gamma[j];
+    const int gq = blockIdx.x;
+    const int head = blockIdx.y * 16 * HT + 16 * ht + li;     // this lane's head
+    const bool hvalid = head < a.nh;
+    const int split = blockIdx.z;
+    const bool dense = a.sel == nullptr;
+
+    // query fragments (B operand of S^T): channels 32s + 8g .. +7 of `head`,
+    // loaded first so that their latency overlaps the lookups below
+    uint4 QB[KS];
+    {
+        const char* qp = (const char*)a.q + ((size_t)gq * a.nh + (hvalid ? head : 0)) * C * 2;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) QB[s] = ld16(qp + (size_t)(32 * s + 8 * g) * 2);
+    }
+    // selected entries of this workgroup's first rows (independent of the
+    // position, so these loads overlap its lookup)
+    const int tile0 = split * a.tiles_per_split;
+    int esel[DESC / NT];
+#pragma unroll
+    for (int u = 0; u < DESC / NT; ++u) {
+        const int slot = tile0 * 32 + (int)threadIdx.x + u * NT;
+        esel[u] = (!dense && slot < a.k) ? a.sel[(size_t)gq * a.k + slot] : -1;
+    }
+    int req, tok;
+    if (a.one_per_req) {
+        req = gq;
+        tok = 0;
+    } else {
+        req = find_request_block(a.cu_new, a.n_req, gq, cu_sh, 256);
+        tok = gq - (a.n_req < 256 ? cu_sh[req] : a.cu_new[req]);
+    }
+    const int t = a.start_pos[req] + tok;
+    const int V = (t + 1) / a.m;
+    const int K0 = dense ? V : a.k;                            // entry slots before the window
+    const int nwr = min(a.n_win, t + 1);
+    const int w0 = t - nwr + 1;
+    const int n_slots = K0 + a.n_win;
+    const int n_tiles = (n_slots + 31) / 32;
+    const int tile1 = min(n_tiles, tile0 + a.tiles_per_split);
+    const char* ring = (const char*)a.state + (size_t)req * a.state_stride;
+
+    // ---- row descriptors of DESC consecutive slots (e: the entry of a
+    //      slot < K0, already loaded for the first window of a sparse query)
+    auto describe = [&](int first_slot, bool have_e) {
+#pragma unroll
+        for (int u = 0; u < DESC / NT; ++u) {
+            const int j = (int)threadIdx.x + u * NT;
+            const int slot = first_slot + j;
+            const char* p = nullptr;
+            const char* blk = nullptr;
+            if (slot < K0) {
+                const int e = dense ? slot : (have_e ? esel[u] : a.sel[(size_t)gq * a.k + slot]);
+                if (e >= 0 && e < V) {
+                    const int phys = a.block_table[(size_t)req * a.max_blocks + (e >> a.epb_log2)];
+                    const char* b = (const char*)a.kv + (size_t)phys * a.kv_block_bytes;
+                    p = b + 64 + (size_t)(e & (a.epb - 1)) * EB;
+                    blk = b;
+                }
+            } else if (slot < n_slots && slot - K0 < nwr) {
+                p = ring + (size_t)((w0 + slot - K0) % a.win_cap) * WB;
+            }
+            rptr[j] = p;
+            rblk[j] = blk;
+        }
+    };
+    // ---- one tile into registers: wave w loads rows w, w+NWV, .., one row
+    //      per instruction, lane l the row's bytes 16l..16l+15 (clamped to
+    //      the row; masked rows read a valid dummy row), the block scale of
+    //      each entry row and (bit j of rok) whether row j is valid
+    const char* dummy = (const char*)a.kv;
+    auto load_tile = [&](int tile, int drow0, uint4 (&raw)[RPW], float (&rsr)[RPW], int& rok) {
+        const int slot0 = tile * 32;
+        rok = 0;
+#pragma unroll
+        for (int j = 0; j < RPW; ++j) {
+            const int row = wave + NWV * j;
+            const char* p = rptr[drow0 + row];
+            const int bytes = (slot0 + row < K0) ? EB : WB;
+            raw[j] = ld16((p != nullptr ? p : dummy) + min(lane * 16, bytes - 16));
+            const char* b = rblk[drow0 + row];
+            rsr[j] = *(const CSA_GLOBAL float*)(b != nullptr ? b : dummy);
+            rok |= (p != nullptr) << j;
+        }
+    };
+    // ---- expand a loaded tile into Kt[buf] (masked rows become zeros) with
+    //      its row flags and scales
+    auto store_tile = [&](int tile, int buf, const uint4 (&raw)[RPW], const float (&rsr)[RPW], int rok) {
+        const int slot0 = tile * 32;
+#pragma unroll
+        for (int j = 0; j < RPW; ++j) {
+            const int row = wave + NWV * j;
+            const bool ok = (rok >> j) & 1;
+            const bool entry = slot0 + row < K0;
+            if (lane == 0) {
+                tval[buf][row] = ok;
+                tscl[buf][row] = (ok && entry) ? rsr[j] : 1.0f;
+            }
+            const uint4 v = sel16(ok, raw[j]);
+            uint16_t* kr = &Kt[buf][row * KP];
+            if (entry) {
+                if (lane < NCH) {                              // 16 FP8 codes per lane
+                    const uint2 b0 = e4m3x4_to_bf16x4(v.x), b1 = e4m3x4_to_bf16x4(v.y);
+                    const uint2 b2 = e4m3x4_to_bf16x4(v.z), b3 = e4m3x4_to_bf16x4(v.w);
+                    *(uint4*)(kr + 16 * lane) = make_uint4(b0.x, b0.y, b1.x, b1.y);
+                    *(uint4*)(kr + 16 * lane + 8) = make_uint4(b2.x, b2.y, b3.x, b3.y);
+                } else if (lane < NCH + R / 8) {               // the bf16 rotary channels
+                    *(uint4*)(kr + NF + 8 * (lane - NCH)) = v;
+                }
+            } else if (lane * 16 < WB) {
+                *(uint4*)(kr + 8 * lane) = v;                  // 8 bf16 channels of a window row
+            }
+        }
+    };
+
+    // ---- prologue: RoPE table at +t and the first descriptors
+    for (int j = threadIdx.x; j < R / 2; j += NT) rope_cs_f((double)t, a.inv_freq[j], &rcs[j], &rsn[j]);
+    if (tile0 < tile1) describe(tile0 * 32, true);
+    __syncthreads();
+    // two tiles in flight: the rows of tiles n+1 and n+2 load while tile n
+    // computes (slot k of raw / rsr / rok and LDS buffer k serve tiles
+    // tile0 + k, tile0 + k + 2, ..)
+    static_assert(DESC >= 64, "two tiles per descriptor window");
+    uint4 raw[2][RPW];
+    float rsr[2][RPW];
+    int rok[2];
+    if (tile0 < tile1) load_tile(tile0, 0, raw[0], rsr[0], rok[0]);
+    if (tile0 + 1 < tile1) load_tile(tile0 + 1, 32, raw[1], rsr[1], rok[1]);
+
+    // normalised, rotated, scaled query fragments of this lane's head
+    uint4 QF[KS];
+    {
+        float ss = 0.f;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const uint32_t w4[4] = {QB[s].x, QB[s].y, QB[s].z, QB[s].w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const float x0 = bf16_to_f32(w4[h] & 0xFFFF), x1 = bf16_to_f32(w4[h] >> 16);
+                ss += x0 * x0 + x1 * x1;
+            }
+        }
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        const float inv = hvalid ? 1.0f / sqrtf(ss / (float)C + a.eps) : 0.f;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const int d0 = 32 * s + 8 * g;
+            const float4 ga = *(const float4*)(gam + d0), gb = *(const float4*)(gam + d0 + 4);
+            const float gm[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+            const uint32_t w4[4] = {QB[s].x, QB[s].y, QB[s].z, QB[s].w};
+            float x[8];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                x[2 * h] = gm[2 * h] * (bf16_to_f32(w4[h] & 0xFFFF) * inv);
+                x[2 * h + 1] = gm[2 * h + 1] * (bf16_to_f32(w4[h] >> 16) * inv);
+            }
+            if (s >= KSN) {
+#pragma unroll
+                for (int j = 0; j < 8; j += 2) {
+                    const int pr = (d0 + j - NF) >> 1;
+                    const float u0 = x[j], u1 = x[j + 1];
+                    x[j] = u0 * rcs[pr] - u1 * rsn[pr];
+                    x[j + 1] = u0 * rsn[pr] + u1 * rcs[pr];
+                }
+            }
+            QF[s] = make_uint4(pack_bf16x2(x[0] * a.scale_log2, x[1] * a.scale_log2),
+                               pack_bf16x2(x[2] * a.scale_log2, x[3] * a.scale_log2),
+                               pack_bf16x2(x[4] * a.scale_log2, x[5] * a.scale_log2),
+                               pack_bf16x2(x[6] * a.scale_log2, x[7] * a.scale_log2));
+        }
+    }
+
+    // lane (g, li): O^T[16 (DTH half + j) + 4g + i][head li]
+    f32x4_t O[DTH];
+#pragma unroll
+    for (int j = 0; j < DTH; ++j) O[j] = zero4();
+    float m_run = -INFINITY, l_run = 0.f;
+
+    auto tile_step = [&](int tile, auto slot) {
+        constexpr int buf = decltype(slot)::value;
+        // Kt[buf] was last read by tile-2, which every wave finished before
+        // the barrier of tile-1
+        store_tile(tile, buf, raw[buf], rsr[buf], rok[buf]);
+        __syncthreads();                                       // tile in Kt[buf]
+        if (tile + 2 < tile1) {
+            const int drow = ((tile + 2 - tile0) * 32) % DESC;
+            if (drow == 0) {                                   // the next DESC rows (the loads of tile+1
+                describe((tile + 2) * 32, false);              // are issued, stores read no descriptors)
+                __syncthreads();
+            }
+            load_tile(tile + 2, drow, raw[buf], rsr[buf], rok[buf]);
+        }
+        const uint16_t* kt = Kt[buf];
+
+        // ---- S^T (rows 16 rt + 4g + i, head li); FP8 and rotary channels apart
+        // K fragments read QC steps ahead of the MFMAs that use them
+        constexpr int QC = 2;
+        static_assert(KS % QC == 0, "whole chunks");
+        f32x4_t an[2] = {zero4(), zero4()}, ar[2] = {zero4(), zero4()};
+        uint4 kf[2][QC][2];
+        auto read_k = [&](int c, uint4 (&f)[QC][2]) {
+#pragma unroll
+            for (int u = 0; u < QC; ++u) {
+                const int s = QC * c + u;
+                f[u][0] = *(const uint4*)(kt + li * KP + 32 * s + 8 * g);
+                f[u][1] = *(const uint4*)(kt + (16 + li) * KP + 32 * s + 8 * g);
+            }
+        };
+        read_k(0, kf[0]);
+#pragma unroll
+        for (int c = 0; c < KS / QC; ++c) {
+            if (c + 1 < KS / QC) read_k(c + 1, kf[(c + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < QC; ++u) {
+                const int s = QC * c + u;
+                if (s < KSN) {
+                    an[0] = MmaBF16::step(kf[c & 1][u][0], QF[s], an[0]);
+                    an[1] = MmaBF16::step(kf[c & 1][u][1], QF[s], an[1]);
+                } else {
+                    ar[0] = MmaBF16::step(kf[c & 1][u][0], QF[s], ar[0]);
+                    ar[1] = MmaBF16::step(kf[c & 1][u][1], QF[s], ar[1]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // ---- online softmax of head li over the 32 rows, in base 2
+        float sv[8], rsc[8];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * rt + 4 * g + i;
+                rsc[4 * rt + i] = tscl[buf][row];
+                const float v = rsc[4 * rt + i] * an[rt][i] + ar[rt][i];
+                sv[4 * rt + i] = tval[buf][row] != 0 ? v : -INFINITY;
+            }
+        float mx = sv[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        // the reference max moves only when a logit exceeds it by more than
+        // 2^8 (base 2), so weights stay <= 256 and rescales are rare
+        const bool raise = mx > m_run + 8.0f;
+        const bool rescale = raise && m_run != -INFINITY;
+        const float m_new = raise ? mx : m_run;
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.0f;
+        float p[8], ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            p[i] = __builtin_amdgcn_exp2f(sv[i] - m_use);
+            ps += p[i];
+        }
+        ps += __shfl_xor(ps, 16, 64);
+        ps += __shfl_xor(ps, 32, 64);
+        l_run = l_run * alpha + ps;
+        m_run = m_new;
+        if (__any(rescale)) {
+#pragma unroll
+            for (int j = 0; j < DTH; ++j) O[j] *= alpha;
+        }
+        // P^T: plain weights for the rotary (bf16) channels, weights times the
+        // row's block scale for the FP8 value channels
+        const uint4 pp = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                                    pack_bf16x2(p[6], p[7]));
+        const uint4 psc = make_uint4(pack_bf16x2(p[0] * rsc[0], p[1] * rsc[1]), pack_bf16x2(p[2] * rsc[2], p[3] * rsc[3]),
+                                     pack_bf16x2(p[4] * rsc[4], p[5] * rsc[5]), pack_bf16x2(p[6] * rsc[6], p[7] * rsc[7]));
+        // ---- O^T += V^T . P^T: lane m of a 16-lane group points at 4
+        //      channels of one row (row 4g + m/4, +16 for the second read), so
+        //      the transpose reads give lane (g, li) channel c0 + li of rows
+        //      4g..4g+3 and 16+4g..16+4g+3, the order of P^T's contraction
+        // V^T fragments read VC tiles ahead of their MFMAs
+        constexpr int VC = 2;
+        static_assert(DTH % VC == 0, "whole chunks");
+        uint4 vf[2][VC];
+        auto read_v = [&](int c, uint4 (&f)[VC]) {
+#pragma unroll
+            for (int u = 0; u < VC; ++u) {
+                const int dt = DTH * half + VC * c + u;
+                const uint16_t* base = kt + (4 * g + (li >> 2)) * KP + 16 * dt + 4 * (li & 3);
+                const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS s16x4_t*)base);
+                const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS s16x4_t*)(base + 16 * KP));
+                const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+                f[u] = make_uint4(l2.x, l2.y, h2.x, h2.y);
+            }
+        };
+        read_v(0, vf[0]);
+#pragma unroll
+        for (int c = 0; c < DTH / VC; ++c) {
+            if (c + 1 < DTH / VC) read_v(c + 1, vf[(c + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < VC; ++u) {
+                const int j = VC * c + u;
+                const int dt = DTH * half + j;
+                O[j] = MmaBF16::step(vf[c & 1][u], dt < DTN ? psc : pp, O[j]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    for (int tile = tile0; tile < tile1; tile += 2) {
+        tile_step(tile, std::integral_constant<int, 0>());
+        if (tile + 1 < tile1) tile_step(tile + 1, std::integral_constant<int, 1>());
+    }
+
+    // ---- output: the normalised result (one split) or the split partial
+    //      (max, sum at bytes 0 and 4, the C channels from byte 16)
+    if (!hvalid) return;
+    if (a.n_splits == 1) {
+        const float zs = a.sinks[head] * LOG2E;
+        const float M = fmaxf(m_run, zs);
+        const float sc = exp2f(m_run - M);
+        const float inv = sc / (l_run * sc + exp2f(zs - M));
+#pragma unroll
+        for (int j = 0; j < DTH; ++j) {
+            const int d = 16 * (DTH * half + j) + 4 * g;
+            float o[4] = {O[j][0] * inv, O[j][1] * inv, O[j][2] * inv, O[j][3] * inv};
+            if (d >= NF) {
+#pragma unroll
+                for (int j = 0; j < 4; j += 2) {               // rotate back at -t
+                    const int pj = (d + j - NF) >> 1;
+                    const float u0 = o[j], u1 = o[j + 1];
+                    o[j] = u0 * rcs[pj] + u1 * rsn[pj];
+                    o[j + 1] = -u0 * rsn[pj] + u1 * rcs[pj];
+                }
+            }
+            if (a.out_bf16)
+                *(uint2*)((uint16_t*)a.out + ((size_t)gq * a.nh + head) * C + d) =
+                    make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+            else
+                *(float4*)((float*)a.out + ((size_t)gq * a.nh + head) * C + d) = make_float4(o[0], o[1], o[2], o[3]);
+        }
+    } else {
+        const size_t pstride = a.out_bf16 ? 2 * (size_t)C + 16 : 4 * (size_t)C + 16;
+        char* pp = (char*)a.ws + (((size_t)gq * a.nh + head) * a.n_splits + split) * pstride;
+        if (g == 0 && half == 0) {
+            ((float*)pp)[0] = m_run;
+            ((float*)pp)[1] = l_run;
+        }
+#pragma unroll
+        for (int j = 0; j < DTH; ++j) {
+            const int d = 16 * (DTH * half + j) + 4 * g;
+            if (a.out_bf16)
+                *(uint2*)(pp + 16 + 2 * (size_t)d) = make_uint2(pack_bf16x2(O[j][0], O[j][1]),
+                                                                pack_bf16x2(O[j][2], O[j][3]));
+            else
+                *(float4*)(pp + 16 + 4 * (size_t)d) = make_float4(O[j][0], O[j][1], O[j][2], O[j][3]);
+        }
+    }
+}
+
 // Merge the split partials of one (query, head) in split order, add the sink,
 // normalise, rotate back at -t and store.  One workgroup of 128 threads per
 // (query, head); each thread owns 4 consecutive channels.
@@ -679,7 +1073,9 @@ hipError_t launch_attention(hipStream_t st, AttnArgs a)
     a.tiles_per_split = (tiles + a.n_splits - 1) / a.n_splits;
     for (int j = 0; j < a.r / 2 && j < 32; ++j) a.inv_freq[j] = rope_inv_freq(j, a.r, (double)a.theta);
     const dim3 grid(a.n_tokens, hg, a.n_splits);
-    if (ht == 4) launch_ht<4>(st, a, grid);
+    if (ht == 4 && a.kv_fmt == 2 && a.c == 512 && a.r == 64 && a.q_bf16 && a.win_bf16)
+        attn_ht_kernel<512, 64, 4><<<grid, 512, 0, st>>>(a);     // FP8 serving shapes: two waves per head tile
+    else if (ht == 4) launch_ht<4>(st, a, grid);
     else launch_ht<1>(st, a, grid);
     if (a.n_splits > 1) attn_combine_kernel<<<dim3(a.n_tokens, a.nh), 128, 0, st>>>(a);
     return hipGetLastError();

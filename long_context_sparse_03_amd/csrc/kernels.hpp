@@ -106,6 +106,7 @@ struct AttnArgs {
     int rows_max;              // rows per query (slots): k + n_win, or max entries + n_win
     int n_splits;
     int tiles_per_split;
+    int one_per_req;           // every request has exactly one new token (query gq is request gq's)
     double inv_freq[32];       // RoPE frequencies theta^(-2j/r), j < r/2 (filled by launch_attention)
 };
 
