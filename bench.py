@@ -6,7 +6,8 @@ sparse_mqa per CSA layer; compress_kv, cache_append and hca_attention per HCA
 layer.  Inputs (caches, window rings, compressor tails, weights, queries) are
 synthetic, resident in HBM before timing starts, and the cache is rotated
 over several replicas so that the 256 MB last-level cache cannot hold a
-step's working set.  Each replica's step is captured once in a HIP graph and
+step's working set.  One HIP graph holds one step of every replica in
+rotation order (single-replica graphs time a remainder), and the graphs are
 replayed.  Prints one JSON line.
 
 Workloads:
@@ -157,30 +158,44 @@ def time_decode(name, steps, warmup, replicas=0, graph=True):
             wls[i % reps].step()
         stream.synchronize()
 
-    graphs = []
+    # One graph holds one decode step of every replica, in rotation order, so
+    # a replay is `reps` consecutive steps (the launch of the graph is shared
+    # by them, as a serving loop that captures several steps would share it).
+    # Single-step graphs of each replica time the remainder when the step
+    # count is not a multiple of the replica count.
+    gph, gph_one = None, []
     if graph:
-        for wl in wls:
-            gph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gph, stream=stream):
+        gph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gph, stream=stream):
+            for wl in wls:
                 wl.step()
-            graphs.append(gph)
+        for wl in wls:
+            g1 = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g1, stream=stream):
+                wl.step()
+            gph_one.append(g1)
         torch.cuda.synchronize()
 
-    def run(i):
-        if graphs:
-            graphs[i % reps].replay()
-        else:
-            wls[i % reps].step()
+    def run_steps(n):
+        for _ in range(n // reps):
+            if gph is not None:
+                gph.replay()
+            else:
+                for wl in wls:
+                    wl.step()
+        for j in range(n % reps):
+            if gph is not None:
+                gph_one[j].replay()
+            else:
+                wls[j].step()
 
     with torch.cuda.stream(stream):
-        for i in range(warmup):
-            run(i)
+        run_steps(warmup)
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         t0.record(stream)
-        for i in range(steps):
-            run(i)
+        run_steps(steps)
         t1.record(stream)
         torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
@@ -213,7 +228,7 @@ def time_decode(name, steps, warmup, replicas=0, graph=True):
                 "traffic": profiled_traffic(kname, name),
                 "launch_ms": round(idx_avg_ms, 5), "algorithmic_bytes_per_launch": ab["index_launch"]}
     step_gbs = ab["total"] / (ms * 1e-3) / 1e9
-    del wls, graphs
+    del wls, gph, gph_one
     torch.cuda.empty_cache()
     return {"workload": name, "tokens_per_s": round(wd["n_req"] / (ms * 1e-3), 1), "ms_per_step": round(ms, 5),
             "requests": wd["n_req"], "ctx": wd["ctx"], "layers": len(wd["descs"]), "d": wd["d"],

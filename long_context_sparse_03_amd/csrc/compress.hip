@@ -76,38 +76,37 @@ __global__ __launch_bounds__(256) void proj_large(const T* __restrict__ X, const
         }
 }
 
-// Few rows (decode): a 16 x 16 output tile per workgroup, the four waves
-// split K into contiguous quarters and are summed in wave order.
-template <class T, class MMA>
-__global__ __launch_bounds__(256) void proj_small(const T* __restrict__ X, const T* __restrict__ W,
-                                                  const T* __restrict__ Wi, int n_main, int N, int M, int K,
-                                                  float* __restrict__ P)
+// Few rows (decode): a 16 x 16 output tile per workgroup; the NW waves
+// split K into contiguous parts (K / NW a multiple of the MMA step), summed
+// in wave order.  Sixteen waves keep a whole 16-column slice of the weights
+// in flight at once for the decode widths.
+template <class T, class MMA, int NW>
+__global__ __launch_bounds__(64 * NW) void proj_small(const T* __restrict__ X, const T* __restrict__ W,
+                                                      const T* __restrict__ Wi, int n_main, int N, int M, int K,
+                                                      float* __restrict__ P)
 {
     constexpr int EPF = 16 / sizeof(T);
-    __shared__ float red[4][64][4];
+    __shared__ float red[NW][64][4];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
     const int m = blockIdx.y * 16 + li, n = blockIdx.x * 16 + li;
     const bool av = m < M, bv = n < N;
-    const int kq = K / 4, kb = wave * kq;
+    const int kq = K / NW, kb = wave * kq;
     const T* ap = X + (size_t)(av ? m : 0) * K + kb + g * EPF;
     int nn = bv ? n : 0;
     const T* bp = (nn < n_main ? W + (size_t)nn * K : Wi + (size_t)(nn - n_main) * K) + kb + g * EPF;
     f32x4_t acc[4] = {zero4(), zero4(), zero4(), zero4()};
-    int k0 = 0;
-    for (; k0 + 8 * MMA::K <= kq; k0 += 8 * MMA::K) {      // eight fragment pairs in flight
+    for (int k0 = 0; k0 < kq; k0 += 8 * MMA::K) {          // up to eight fragment pairs in flight
+        const int nb = min(8, (kq - k0) / MMA::K);
         uint4 a8[8], b8[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            a8[u] = ld16(ap + k0 + u * MMA::K);   // clamped rows: only dropped outputs see them
-            b8[u] = ld16(bp + k0 + u * MMA::K);
+            const int ku = k0 + min(u, nb - 1) * MMA::K;    // clamped: steps past nb are not used
+            a8[u] = ld16(ap + ku);                          // clamped rows: only dropped outputs see them
+            b8[u] = ld16(bp + ku);
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) acc[u & 3] = MMA::step(a8[u], b8[u], acc[u & 3]);
-    }
-    for (; k0 < kq; k0 += MMA::K) {
-        uint4 a0 = ld16(ap + k0);
-        uint4 b0 = ld16(bp + k0);
-        acc[0] = MMA::step(a0, b0, acc[0]);
+        for (int u = 0; u < 8; ++u)
+            if (u < nb) acc[u & 3] = MMA::step(a8[u], b8[u], acc[u & 3]);
     }
     const f32x4_t acc0 = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     const f32x4_t acc1 = zero4();
@@ -118,7 +117,9 @@ __global__ __launch_bounds__(256) void proj_small(const T* __restrict__ X, const
         const int col = blockIdx.x * 16 + li;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            float v = red[0][lane][q] + red[1][lane][q] + red[2][lane][q] + red[3][lane][q];
+            float v = red[0][lane][q];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) v += red[w][lane][q];
             int row = blockIdx.y * 16 + 4 * g + q;
             if (row < M && col < N) P[(size_t)row * N + col] = v;
         }
@@ -297,12 +298,15 @@ hipError_t launch_compress(hipStream_t st, const CompressArgs& a, const void* H,
     if (M > 0) {
         if (M <= 64) {
             dim3 grid((N + 15) / 16, (M + 15) / 16);
-            if (bf16)
-                proj_small<uint16_t, MmaBF16><<<grid, 256, 0, st>>>((const uint16_t*)H, (const uint16_t*)W,
-                                                                    (const uint16_t*)Wi, n_main, N, M, d, a.P);
+            if (bf16 && d % (16 * MmaBF16::K) == 0)              // 16 waves of whole steps
+                proj_small<uint16_t, MmaBF16, 16><<<grid, 1024, 0, st>>>((const uint16_t*)H, (const uint16_t*)W,
+                                                                         (const uint16_t*)Wi, n_main, N, M, d, a.P);
+            else if (bf16)
+                proj_small<uint16_t, MmaBF16, 4><<<grid, 256, 0, st>>>((const uint16_t*)H, (const uint16_t*)W,
+                                                                       (const uint16_t*)Wi, n_main, N, M, d, a.P);
             else
-                proj_small<float, MmaF32><<<grid, 256, 0, st>>>((const float*)H, (const float*)W, (const float*)Wi,
-                                                                n_main, N, M, d, a.P);
+                proj_small<float, MmaF32, 4><<<grid, 256, 0, st>>>((const float*)H, (const float*)W, (const float*)Wi,
+                                                                   n_main, N, M, d, a.P);
         } else {
             dim3 grid((N + 127) / 128, (M + 127) / 128);
             if (bf16)

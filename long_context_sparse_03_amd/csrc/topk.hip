@@ -6,10 +6,11 @@
 // +0 map to the same key), so selection is integer work and bit-exact.  The
 // order is (key descending, index ascending).  A workgroup holds its keys in
 // registers, each thread a run of consecutive positions.  The k-th key is
-// found by an MSB-first radix select with 4-bit digits whose counts come from
-// wave ballots (one barrier per digit), and the selected set is emitted in
-// index order from one block-wide scan, which also breaks ties at the
-// threshold toward lower indices.  Before the radix select, a lower bound
+// found with histograms over the range [smallest, largest] of the keys in
+// play (at most 2048 bins, narrowed to the selected bin until bins are single
+// keys: one pass when the range spans at most 2048 keys), and the selected
+// set is emitted in index order from one block-wide scan, which also breaks
+// ties at the threshold toward lower indices.  Before that, a lower bound
 // from the per-thread maxima usually leaves only a few per cent of the keys
 // in play.
 //
@@ -31,6 +32,7 @@ constexpr int CAP32 = 20480;                  // fp32 keys per workgroup
 constexpr int KPT16 = CAP16 / TOPK_THREADS;   // keys per thread at the capacity
 constexpr int KPT32 = CAP32 / TOPK_THREADS;
 constexpr int SMALL_NT = 256, SMALL_KPT = 32; // workgroups of up to 8192 keys
+constexpr int MID_KPT = 40;                   // 256 threads for up to 10240 keys
 constexpr int SURV_CAP = 4096;                // keys kept after the lower bound (1024-thread workgroups)
 
 // Order-preserving key of a score: sign-magnitude flip; -0 and +0 share the key.
@@ -94,71 +96,6 @@ __shared__ uint32_t topk_digit[2];                  // chosen bin, remaining ran
 // positions tid*KPT .. tid*KPT+KPT-1, so a thread's positions are
 // consecutive; positions >= n hold key 0, and every real key is >= 1 (see
 // raise_keys), so kk <= n keeps them out of the selection.
-
-// Threshold of the top kk (at least kk keys >= lo): T = the kk-th largest
-// key, rem = how many keys equal to T belong to the top kk.  BITS = key width
-// (16 or 32).  Digits of 4 bits from the top.  Each wave counts its keys per
-// digit value into its own 16 LDS counters (LDS atomics for a few keys per
-// thread; per-thread 6-bit counters summed over the wave for many), the
-// waves' counts are summed after one barrier, and every wave takes the same
-// decision with lane-parallel arithmetic (a scan over the 16 digit totals and
-// one ballot).  The counters alternate between two buffers, as in BlockScan.
-// Keys below lo are known to lie under the threshold and are not counted.
-template <int BITS, int KPT>
-CSA_DEV void find_threshold(const uint32_t (&kr)[KPT], int kk, uint32_t lo, uint32_t& T, uint32_t& rem_out)
-{
-    __shared__ uint32_t cnt[2][16][16];          // [buffer][wave][digit value]
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    uint32_t prefix = 0, mask = 0, rem = (uint32_t)kk;
-#pragma unroll 1
-    for (int r = 0; r < BITS / 4; ++r) {
-        const int shift = BITS - 4 * (r + 1);
-        auto digit = [&](uint32_t k) { return (k >= lo && (k & mask) == prefix) ? (k >> shift) & 15u : 16u; };
-        uint32_t* my = cnt[r & 1][w];
-        if constexpr (KPT <= 4) {
-            // a wave's LDS operations run in order: clear, then count
-            if (lane < 16) my[lane] = 0u;
-#pragma unroll
-            for (int j = 0; j < KPT; ++j) {
-                const uint32_t d = digit(kr[j]);
-                if (d < 16u) atomicAdd(&my[d], 1u);
-            }
-        } else {
-            // per-thread counts in 6-bit fields (digit values 0-9 in c0,
-            // 10-15 in c1; KPT <= 63), then one wave sum per digit value
-            static_assert(KPT <= 63, "6-bit counters");
-            uint64_t c0 = 0, c1 = 0;
-#pragma unroll
-            for (int j = 0; j < KPT; ++j) {
-                const uint32_t d = digit(kr[j]);
-                c0 += d < 10u ? 1ull << (6 * d) : 0ull;
-                c1 += d - 10u < 6u ? 1ull << (6 * (d - 10u)) : 0ull;
-            }
-#pragma unroll 1
-            for (int v = 0; v < 16; ++v) {
-                const uint32_t x = (uint32_t)((v < 10 ? c0 >> (6 * v) : c1 >> (6 * (v - 10))) & 63u);
-                const uint32_t sum = wave_incl_scan(x);
-                if (lane == 63) my[v] = sum;
-            }
-        }
-        __syncthreads();
-        uint32_t bin = 0;                        // lane v < 16: the workgroup's count of digit v
-        if (lane < 16)
-            for (int i = 0; i < nw; ++i) bin += cnt[r & 1][i][lane];
-        // keys in digits above v: total - inclusive prefix up to v; the digit
-        // holding the rem-th largest key is the one lane where rem falls
-        const uint32_t incl = wave_incl_scan(bin);
-        const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 15);
-        const uint32_t above = total - incl;
-        const uint64_t hit = __ballot(lane < 16 && above < rem && rem <= above + bin);
-        const int d = (int)__builtin_ctzll(hit);
-        prefix |= (uint32_t)d << shift;
-        rem -= (uint32_t)__builtin_amdgcn_readlane((int)above, d);
-        mask |= 15u << shift;
-    }
-    T = prefix;
-    rem_out = rem;
-}
 
 // Running maximum / minimum over the lanes of a wave, in DPP steps as in
 // wave_incl_scan (lanes without a source see the identity); lane 63 ends
@@ -328,12 +265,22 @@ CSA_DEV void emit_selected(const uint32_t (&kr)[KPT], int kk, uint32_t T, uint32
 }
 
 // Select the top kk of n keys and emit the selected positions in ascending
-// order through emit(rank, position, key).
-template <int BITS, int KPT, class EmitF>
-CSA_DEV void select_top(const uint32_t (&kr)[KPT], int n, int kk, BlockScan& bs, EmitF emit, uint32_t lo = 0u)
+// order through emit(rank, position, key): the threshold by range
+// histograms over [smallest, largest] real key.
+template <int KPT, class EmitF>
+CSA_DEV void select_top(const uint32_t (&kr)[KPT], int n, int kk, BlockScan& bs, EmitF emit)
 {
     uint32_t T = 0, rem = 0;
-    if (kk < n) find_threshold<BITS, KPT>(kr, kk, lo, T, rem);
+    if (kk < n) {
+        uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            kmax = max(kmax, kr[j]);
+            kmin = min(kmin, kr[j] > 0u ? kr[j] : 0xFFFFFFFFu);
+        }
+        block_max_min(kmax, kmin, bs);
+        range_threshold<KPT>(kr, kmin, kmax, (uint32_t)kk, bs, T, rem);
+    }
     emit_selected<KPT>(kr, kk, T, rem, bs, emit);
 }
 
@@ -459,7 +406,6 @@ __global__ __launch_bounds__(NT) void topk_chunk_kernel(const void* scores, int 
                                                         int32_t* cand_idx)
 {
     using KT = typename std::conditional<BF16, uint16_t, uint32_t>::type;
-    constexpr int BITS = BF16 ? 16 : 32;
     constexpr int EPL = BF16 ? 8 : 4;
     const int row = blockIdx.y, ch = blockIdx.x;
     const int V = n_valid[row];
@@ -538,7 +484,7 @@ __global__ __launch_bounds__(NT) void topk_chunk_kernel(const void* scores, int 
             }
         }
     }
-    if (!done) select_top<BITS, KPT>(kr, n, kk, bs, emit);
+    if (!done) select_top<KPT>(kr, n, kk, bs, emit);
     for (int r = kk + threadIdx.x; r < k; r += blockDim.x) {
         o[r] = -1;
         if (!single) ck[r] = 0u;
@@ -564,7 +510,31 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_merge_kernel(const int32_t*
     const int32_t* ci = cand_idx + (size_t)row * n;
     __shared__ uint32_t floor_sh;
     if (threadIdx.x == 0) floor_sh = 0u;
-    for (int i = threadIdx.x; i < n; i += blockDim.x) keys[i] = (KT)ck[i];
+    {
+        // candidates into LDS: 16-byte loads, four in flight per thread,
+        // after a scalar prologue up to 16-byte alignment
+        const int head = (int)min((size_t)n, ((16 - (uintptr_t)ck % 16) % 16) / 4);
+        for (int i = threadIdx.x; i < head; i += TOPK_THREADS) keys[i] = (KT)ck[i];
+        const int nvec = (n - head) / 4;
+        const uint32_t* vb = ck + head;
+        for (int v0 = threadIdx.x; v0 < nvec; v0 += 4 * TOPK_THREADS) {
+            uint4 q[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) q[u] = ld16(vb + 4 * (size_t)min(v0 + u * TOPK_THREADS, nvec - 1));
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int v = v0 + u * TOPK_THREADS;
+                if (v < nvec) {
+                    KT* dst = keys + head + 4 * v;
+                    dst[0] = (KT)q[u].x;
+                    dst[1] = (KT)q[u].y;
+                    dst[2] = (KT)q[u].z;
+                    dst[3] = (KT)q[u].w;
+                }
+            }
+        }
+        for (int i = head + 4 * nvec + threadIdx.x; i < n; i += TOPK_THREADS) keys[i] = (KT)ck[i];
+    }
     __syncthreads();
     uint32_t kr[KPT];
     keys_to_regs<KPT>(keys, kr);
@@ -585,7 +555,15 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_merge_kernel(const int32_t*
     // are issued together rather than one dependent load after another
     __shared__ int32_t spos[MAX_K];
     BlockScan bs;
-    select_top<BF16 ? 16 : 32, KPT>(kr, n, kk, bs, [&](int r, int i, uint32_t) { spos[r] = i; }, lo);
+    // the threshold by range histograms over [lo, the largest key] (one pass
+    // when the candidates above the floor span at most 2048 keys)
+    uint32_t kmax = 0u, dummy_min = 0xFFFFFFFFu;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) kmax = max(kmax, kr[j]);
+    block_max_min(kmax, dummy_min, bs);
+    uint32_t T = 0, rem = 0;
+    if (kk < n) range_threshold<KPT>(kr, lo, kmax, (uint32_t)kk, bs, T, rem);
+    emit_selected<KPT>(kr, kk, T, rem, bs, [&](int r, int i, uint32_t) { spos[r] = i; });
     __syncthreads();
     int32_t* o = out + (size_t)row * k;
     for (int r = threadIdx.x; r < k; r += blockDim.x) o[r] = r < kk ? ci[spos[r]] : -1;
@@ -629,6 +607,9 @@ static void launch_chunks(hipStream_t st, dim3 grid, int chunk, const void* scor
     if (chunk <= SMALL_NT * SMALL_KPT)
         topk_chunk_kernel<BF16, SMALL_NT, SMALL_KPT><<<grid, SMALL_NT, 0, st>>>(scores, ld, n_valid, k, chunk,
                                                                                 n_chunks, out, ck, ci);
+    else if (BF16 && chunk <= SMALL_NT * MID_KPT)
+        topk_chunk_kernel<BF16, SMALL_NT, MID_KPT><<<grid, SMALL_NT, 0, st>>>(scores, ld, n_valid, k, chunk,
+                                                                              n_chunks, out, ck, ci);
     else
         topk_chunk_kernel<BF16, TOPK_THREADS, BF16 ? KPT16 : KPT32><<<grid, TOPK_THREADS, 0, st>>>(
             scores, ld, n_valid, k, chunk, n_chunks, out, ck, ci);
