@@ -363,62 +363,77 @@ __global__ __launch_bounds__(512) void index_prefill_kernel(IndexArgs a, int gro
 // fed straight into the scaled FP4 MFMA (one instruction per 16 keys and 16
 // heads covers the whole 128-wide key).
 template <int HT>
-__global__ __launch_bounds__(256) void index_decode_fp4_kernel(IndexArgs a)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void index_decode_fp4_kernel(IndexArgs a)
 {
+    static_assert(HT <= 4, "one wave quantises each head tile");
     __shared__ int bt[IDX_EPW + 1];
     __shared__ int cu_sh[1025];
+    __shared__ uint4 qc_sh[HT][64];              // quantised query: E2M1 codes ...
+    __shared__ int qs_sh[HT][64];                // ... and E8M0 scales per (head tile, lane)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
     const int gq = blockIdx.y;
-    int req, t;
+    const int wg0 = blockIdx.x * IDX_EPW;
+    const int cI = a.cI, nh = a.nh;                // cI == 128: lane group g holds MX block g
+    int req, tok;
     if (a.one_per_req) {                         // token gq is request gq's only new token
         req = gq;
-        t = a.start_pos[gq];
+        tok = 0;
     } else {
         req = find_request_block(a.cu_new, a.n_req, gq, cu_sh);
-        t = a.start_pos[req] + (gq - cu_sh[req]);
+        tok = gq - cu_sh[req];
     }
-    const int V = (t + 1) / a.m;
-    if (blockIdx.x == 0 && threadIdx.x == 0) a.n_valid[gq] = V;
-    const int wg0 = blockIdx.x * IDX_EPW;
-    if (wg0 >= V) return;
-    const int cI = a.cI, nh = a.nh;                // cI == 128: lane group g holds MX block g
+    // position, block-table slice (every block the workgroup can touch,
+    // clamped to the row), query block of this wave's head tile and head
+    // weights: all loads issued together
     const int blk0 = wg0 >> a.epb_log2;
-    const int nblk = ((min(V, wg0 + IDX_EPW) - 1) >> a.epb_log2) - blk0 + 1;
+    const int nbw = ((wg0 + IDX_EPW - 1) >> a.epb_log2) - blk0 + 1;
+    const int sp = a.start_pos[req];
     int btv[(IDX_EPW + 255) / 256];
 #pragma unroll
     for (int i = 0; i < (IDX_EPW + 255) / 256; ++i) {
-        const int j = min((int)threadIdx.x + 256 * i, nblk - 1);
-        btv[i] = a.block_table[(size_t)req * a.max_blocks + blk0 + j];
+        const int j = min(blk0 + min((int)threadIdx.x + 256 * i, nbw - 1), a.max_blocks - 1);
+        btv[i] = a.block_table[(size_t)req * a.max_blocks + j];
     }
-    uint4 Aq[HT];
-    int sa[HT];
-    float wv[HT][4];
-#pragma unroll 1
-    for (int ht = 0; ht < HT; ++ht) {
-        const int head = min(16 * ht + li, nh - 1);
+    uint4 f[4];
+    if (wave < HT) {
+        const int head = min(16 * wave + li, nh - 1);
         const char* qp = (const char*)a.q + ((size_t)gq * nh + head) * cI * 2 + (size_t)g * 64;
-        uint4 f[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) f[s] = ld16(qp + 16 * s);
+    }
+    float wv[HT][4];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wv[ht][i] = a.w[(size_t)gq * nh + min(16 * ht + 4 * g + i, nh - 1)];
+    const int t = sp + tok;
+    const int V = (t + 1) / a.m;
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.n_valid[gq] = V;
+    if (wg0 >= V) return;                        // workgroup-uniform
+#pragma unroll
+    for (int i = 0; i < (IDX_EPW + 255) / 256; ++i)
+        if ((int)threadIdx.x + 256 * i < nbw) bt[threadIdx.x + 256 * i] = btv[i];
+    if (wave < HT) {
         uint4 codes;
         const int sc = mx_quant_codes(f, codes);
-        const bool hv = 16 * ht + li < nh;
-#pragma unroll
-        for (int h = 0; h < HT; ++h)
-            if (h == ht) { Aq[h] = sel16(hv, codes); sa[h] = sc; }
+        qc_sh[wave][lane] = sel16(16 * wave + li < nh, codes);
+        qs_sh[wave][lane] = sc;
     }
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int hh = 16 * ht + 4 * g + i;
-            wv[ht][i] = hh < nh ? a.w[(size_t)gq * nh + hh] : 0.f;
-        }
-#pragma unroll
-    for (int i = 0; i < (IDX_EPW + 255) / 256; ++i)
-        if ((int)threadIdx.x + 256 * i < nblk) bt[threadIdx.x + 256 * i] = btv[i];
+        for (int i = 0; i < 4; ++i) wv[ht][i] = 16 * ht + 4 * g + i < nh ? wv[ht][i] : 0.f;
     __syncthreads();
+    uint4 Aq[HT];
+    int sa[HT];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        Aq[ht] = qc_sh[ht][lane];
+        sa[ht] = qs_sh[ht][lane];
+    }
 
+    // loads are unconditional (entries past V are clamped to V-1, whose
+    // scores are not stored), so the wait counts stay exact
     const size_t codes_off = (size_t)a.epb * (cI / 2);
     auto load = [&](int e0, uint4 (&B)[4], uint32_t (&SC)[4]) {
 #pragma unroll
@@ -430,33 +445,41 @@ __global__ __launch_bounds__(256) void index_decode_fp4_kernel(IndexArgs a)
             SC[tile] = (uint8_t)kb[codes_off + (size_t)slot * (cI / 32) + g];
         }
     };
-    uint4 B[2][4];
-    uint32_t SC[2][4];
-    load(wg0 + wave * 64, B[0], SC[0]);
+    // NB buffers: NB-1 iterations of keys in flight while one is multiplied
+    constexpr int NB = 2;
+    uint4 B[NB][4];
+    uint32_t SC[NB][4];
+#pragma unroll
+    for (int j = 0; j < NB - 1; ++j) {
+        if (j < IDX_ITERS) load(wg0 + 256 * j + wave * 64, B[j], SC[j]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int it = 0; it < IDX_ITERS; ++it) {
-        const int cur = it & 1;
+        const int cur = it % NB;
         const int e_base = wg0 + it * 256 + wave * 64;
-        if (it + 1 < IDX_ITERS && e_base + 256 < V) load(e_base + 256, B[cur ^ 1], SC[cur ^ 1]);
+        if (it + NB - 1 < IDX_ITERS) load(e_base + 256 * (NB - 1), B[(it + NB - 1) % NB], SC[(it + NB - 1) % NB]);
         __builtin_amdgcn_sched_barrier(0);
-        if (e_base >= V) break;
+        if (e_base >= V) break;                  // wave-uniform
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int tile = 0; tile < 4; ++tile) {
-            if (e_base + 16 * tile >= V) break;
-            const int e = e_base + 16 * tile + li;
-            float v = 0.f;
+        for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-            for (int ht = 0; ht < HT; ++ht) {
+            for (int tile = 0; tile < 4; ++tile) {
                 const f32x4_t acc = mfma_fp4(Aq[ht], sa[ht], B[cur][tile], (int)SC[cur][tile]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) v += wv[ht][i] * fmaxf(acc[i], 0.f);
+                for (int i = 0; i < 4; ++i) v[tile] += wv[ht][i] * fmaxf(acc[i], 0.f);
             }
-            v += __shfl_xor(v, 16, 64);
-            v += __shfl_xor(v, 32, 64);
+#pragma unroll
+        for (int tile = 0; tile < 4; ++tile) {
+            const int e = e_base + 16 * tile + li;
+            float x = v[tile];
+            x += __shfl_xor(x, 16, 64);
+            x += __shfl_xor(x, 32, 64);
             if (g == 0 && e < V) {
-                if (v == 0.0f) v = 0.0f;
-                if (a.score_bf16) ((uint16_t*)a.scores)[(size_t)gq * a.ld + e] = f32_to_bf16(v);
-                else ((float*)a.scores)[(size_t)gq * a.ld + e] = v;
+                if (x == 0.0f) x = 0.0f;
+                if (a.score_bf16) ((uint16_t*)a.scores)[(size_t)gq * a.ld + e] = f32_to_bf16(x);
+                else ((float*)a.scores)[(size_t)gq * a.ld + e] = x;
             }
         }
     }
