@@ -558,16 +558,16 @@ __global__ __launch_bounds__((AttnCfg<KVF, C, R, HT>::NT)) void attn_kernel(Attn
 }
 
 // FP8 entry records with bf16 queries (the serving shapes): two waves per
-// head tile.  Waves w and w + HT own heads 16w .. 16w+15 of the group: each
-// contracts every channel of the tile for those heads (S^T = K . Q^T) and
-// runs their online softmax in registers (the pair computes the same
-// values), and each accumulates the output of one half of the channels
-// (O^T = V^T . P^T), so the waves never exchange logits or weights.  Tiles
-// are double-buffered in LDS: the rows of tile n+1 are loaded into
-// registers while tile n computes and stored into the other buffer, and one
-// barrier per tile publishes them.  Each lane keeps the output of its head
-// for 4 channels of every 16-channel group of its half (C/8 fp32
-// accumulators), so two workgroups fit on a compute unit.
+// head tile.  Waves w and w + HT own heads 16w .. 16w+15 of the group and one
+// half of the channels each: each contracts its half of the tile for those
+// heads (S^T = K . Q^T), the two partial logits meet in LDS and are summed
+// in the same order by both waves, both run the same online softmax in
+// registers, and each accumulates the output of its half of the channels
+// (O^T = V^T . P^T).  Tiles are double-buffered in LDS: the rows of the next
+// two tiles are loaded into registers while one computes, and two barriers
+// per tile publish a stored tile and the partial logits.  Each lane keeps
+// the output of its head for 4 channels of every 16-channel group of its
+// half (C/8 fp32 accumulators).
 template <int C, int R, int HT>
 __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
 {
@@ -575,6 +575,7 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
     constexpr int NF = C - R, KP = C + 8, NT = 64 * NWV, RPW = 32 / NWV;
     constexpr int KS = C / 32;                                 // 16x16x32 steps over the channels
     constexpr int KSN = NF / 32;                               // ... of them over FP8 channels
+    constexpr int KSH = KS / 2;                                // ... per wave (its half of the channels)
     constexpr int DT = C / 16;                                 // 16-channel output tiles
     constexpr int DTN = NF / 16;                               // ... of them FP8 value channels
     constexpr int DTH = DT / 2;                                // ... per wave (its half of the channels)
@@ -593,6 +594,8 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
     __shared__ float rcs[R / 2], rsn[R / 2];
     __shared__ int cu_sh[257];
     __shared__ __attribute__((aligned(16))) float gam[C];      // query norm gains
+    __shared__ __attribute__((aligned(16))) f32x4_t Sx[2][HT][2][2][64];  // partial logits per half
+    __shared__ float ssx[HT][2][16];                           // partial sums of squares of the query
 
     const int lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -606,11 +609,11 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
 
     // query fragments (B operand of S^T): channels 32s + 8g .. +7 of `head`,
     // loaded first so that their latency overlaps the lookups below
-    uint4 QB[KS];
+    uint4 QB[KSH];                                             // this wave's half: steps KSH*half + j
     {
         const char* qp = (const char*)a.q + ((size_t)gq * a.nh + (hvalid ? head : 0)) * C * 2;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) QB[s] = ld16(qp + (size_t)(32 * s + 8 * g) * 2);
+        for (int j = 0; j < KSH; ++j) QB[j] = ld16(qp + (size_t)(32 * (KSH * half + j) + 8 * g) * 2);
     }
     // selected entries of this workgroup's first rows (independent of the
     // position, so these loads overlap its lookup)
@@ -712,9 +715,25 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
         }
     };
 
-    // ---- prologue: RoPE table at +t and the first descriptors
+    // ---- prologue: RoPE table at +t, the first descriptors and the partial
+    //      sums of squares of the query heads over this wave's half
     for (int j = threadIdx.x; j < R / 2; j += NT) rope_cs_f((double)t, a.inv_freq[j], &rcs[j], &rsn[j]);
     if (tile0 < tile1) describe(tile0 * 32, true);
+    {
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < KSH; ++j) {
+            const uint32_t w4[4] = {QB[j].x, QB[j].y, QB[j].z, QB[j].w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const float x0 = bf16_to_f32(w4[h] & 0xFFFF), x1 = bf16_to_f32(w4[h] >> 16);
+                ss += x0 * x0 + x1 * x1;
+            }
+        }
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        if (g == 0) ssx[ht][half][li] = ss;
+    }
     __syncthreads();
     // two tiles in flight: the rows of tiles n+1 and n+2 load while tile n
     // computes (slot k of raw / rsr / rok and LDS buffer k serve tiles
@@ -727,27 +746,17 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
     if (tile0 + 1 < tile1) load_tile(tile0 + 1, 32, raw[1], rsr[1], rok[1]);
 
     // normalised, rotated, scaled query fragments of this lane's head
-    uint4 QF[KS];
+    uint4 QF[KSH];
     {
-        float ss = 0.f;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const uint32_t w4[4] = {QB[s].x, QB[s].y, QB[s].z, QB[s].w};
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                const float x0 = bf16_to_f32(w4[h] & 0xFFFF), x1 = bf16_to_f32(w4[h] >> 16);
-                ss += x0 * x0 + x1 * x1;
-            }
-        }
-        ss += __shfl_xor(ss, 16, 64);
-        ss += __shfl_xor(ss, 32, 64);
+        const float ss = ssx[ht][0][li] + ssx[ht][1][li];     // the same order in both waves
         const float inv = hvalid ? 1.0f / sqrtf(ss / (float)C + a.eps) : 0.f;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
+        for (int j = 0; j < KSH; ++j) {
+            const int s = KSH * half + j;
             const int d0 = 32 * s + 8 * g;
             const float4 ga = *(const float4*)(gam + d0), gb = *(const float4*)(gam + d0 + 4);
             const float gm[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
-            const uint32_t w4[4] = {QB[s].x, QB[s].y, QB[s].z, QB[s].w};
+            const uint32_t w4[4] = {QB[j].x, QB[j].y, QB[j].z, QB[j].w};
             float x[8];
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
@@ -763,7 +772,7 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
                     x[j + 1] = u0 * rsn[pr] + u1 * rcs[pr];
                 }
             }
-            QF[s] = make_uint4(pack_bf16x2(x[0] * a.scale_log2, x[1] * a.scale_log2),
+            QF[j] = make_uint4(pack_bf16x2(x[0] * a.scale_log2, x[1] * a.scale_log2),
                                pack_bf16x2(x[2] * a.scale_log2, x[3] * a.scale_log2),
                                pack_bf16x2(x[4] * a.scale_log2, x[5] * a.scale_log2),
                                pack_bf16x2(x[6] * a.scale_log2, x[7] * a.scale_log2));
@@ -793,48 +802,62 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
         const uint16_t* kt = Kt[buf];
 
         // ---- S^T (rows 16 rt + 4g + i, head li); FP8 and rotary channels apart
-        // K fragments read QC steps ahead of the MFMAs that use them
+        // K fragments of this wave's half, read QC steps ahead of the MFMAs
         constexpr int QC = 2;
-        static_assert(KS % QC == 0, "whole chunks");
+        static_assert(KSH % QC == 0, "whole chunks");
         f32x4_t an[2] = {zero4(), zero4()}, ar[2] = {zero4(), zero4()};
         uint4 kf[2][QC][2];
         auto read_k = [&](int c, uint4 (&f)[QC][2]) {
 #pragma unroll
             for (int u = 0; u < QC; ++u) {
-                const int s = QC * c + u;
+                const int s = KSH * half + QC * c + u;
                 f[u][0] = *(const uint4*)(kt + li * KP + 32 * s + 8 * g);
                 f[u][1] = *(const uint4*)(kt + (16 + li) * KP + 32 * s + 8 * g);
             }
         };
         read_k(0, kf[0]);
 #pragma unroll
-        for (int c = 0; c < KS / QC; ++c) {
-            if (c + 1 < KS / QC) read_k(c + 1, kf[(c + 1) & 1]);
+        for (int c = 0; c < KSH / QC; ++c) {
+            if (c + 1 < KSH / QC) read_k(c + 1, kf[(c + 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < QC; ++u) {
-                const int s = QC * c + u;
-                if (s < KSN) {
-                    an[0] = MmaBF16::step(kf[c & 1][u][0], QF[s], an[0]);
-                    an[1] = MmaBF16::step(kf[c & 1][u][1], QF[s], an[1]);
+                const int j = QC * c + u;
+                if (KSH * half + j < KSN) {                     // wave-uniform
+                    an[0] = MmaBF16::step(kf[c & 1][u][0], QF[j], an[0]);
+                    an[1] = MmaBF16::step(kf[c & 1][u][1], QF[j], an[1]);
                 } else {
-                    ar[0] = MmaBF16::step(kf[c & 1][u][0], QF[s], ar[0]);
-                    ar[1] = MmaBF16::step(kf[c & 1][u][1], QF[s], ar[1]);
+                    ar[0] = MmaBF16::step(kf[c & 1][u][0], QF[j], ar[0]);
+                    ar[1] = MmaBF16::step(kf[c & 1][u][1], QF[j], ar[1]);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        // ---- online softmax of head li over the 32 rows, in base 2
-        float sv[8], rsc[8];
+        // ---- the two halves' partial logits (FP8 channels scaled by the
+        //      row's block scale) meet in LDS; both waves add them in half order
+        float rsc[8];
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+        for (int rt = 0; rt < 2; ++rt) {
+            f32x4_t part;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                rsc[4 * rt + i] = tscl[buf][16 * rt + 4 * g + i];
+                part[i] = rsc[4 * rt + i] * an[rt][i] + ar[rt][i];
+            }
+            Sx[buf][ht][half][rt][lane] = part;
+        }
+        __syncthreads();                                       // partial logits of both halves in LDS
+        // ---- online softmax of head li over the 32 rows, in base 2
+        float sv[8];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const f32x4_t s0 = Sx[buf][ht][0][rt][lane], s1 = Sx[buf][ht][1][rt][lane];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * rt + 4 * g + i;
-                rsc[4 * rt + i] = tscl[buf][row];
-                const float v = rsc[4 * rt + i] * an[rt][i] + ar[rt][i];
-                sv[4 * rt + i] = tval[buf][row] != 0 ? v : -INFINITY;
+                sv[4 * rt + i] = tval[buf][row] != 0 ? s0[i] + s1[i] : -INFINITY;
             }
+        }
         float mx = sv[0];
 #pragma unroll
         for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
