@@ -976,55 +976,102 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
 
 // Merge the split partials of one (query, head) in split order, add the sink,
 // normalise, rotate back at -t and store.  One workgroup of 128 threads per
-// (query, head); each thread owns 4 consecutive channels.
+// (query, head); each thread owns 4 consecutive channels.  The partials'
+// (max, sum) pairs and (up to CB splits) the thread's channels of every
+// partial are loaded at once; the weights and the denominator come from
+// fixed-order reductions, so the result does not depend on scheduling.
+constexpr int CB = 16;                                         // splits whose channels load in one batch
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a)
 {
-    __shared__ float w_sh[256];
+    __shared__ float red[2][2];
     __shared__ float o_sh[512];
     __shared__ float rc[32], rs[32];
-    __shared__ float m_sh, inv_sh;
     const int gq = blockIdx.x, head = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int C = a.c, S = a.n_splits, nf = C - a.r;
-    const int req = find_request(a.cu_new, a.n_req, gq);
-    const int t = a.start_pos[req] + (gq - a.cu_new[req]);
     const size_t pstride = a.out_bf16 ? 2 * (size_t)C + 16 : 4 * (size_t)C + 16;
     const char* pp = (const char*)a.ws + ((size_t)gq * a.nh + head) * S * pstride;
+    const int d4 = threadIdx.x;                                // channels 4 d4 .. 4 d4 + 3
+    const bool dv = d4 < C / 4;
+    // loads first: position, (max, sum) of splits tid and tid + 128, and the
+    // thread's channels of the first CB splits
+    int req, tok;
+    if (a.one_per_req) {
+        req = gq;
+        tok = 0;
+    } else {
+        req = find_request(a.cu_new, a.n_req, gq);
+        tok = gq - a.cu_new[req];
+    }
+    float2 ml[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int sidx = threadIdx.x + 128 * u;
+        ml[u] = sidx < S ? *(const float2*)(pp + sidx * pstride) : make_float2(-INFINITY, 0.f);
+    }
+    uint4 ov[CB];
+#pragma unroll
+    for (int sb = 0; sb < CB; ++sb) {
+        const char* src = pp + (size_t)min(sb, S - 1) * pstride + 16;
+        if (a.out_bf16) {
+            const uint2 u = dv ? *(const uint2*)(src + 8 * (size_t)d4) : make_uint2(0u, 0u);
+            ov[sb] = make_uint4(u.x, u.y, 0u, 0u);
+        } else {
+            ov[sb] = dv ? *(const uint4*)(src + 16 * (size_t)d4) : make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+    const int t = a.start_pos[req] + tok;
     const float zs = a.sinks[head] * LOG2E;
     for (int j = threadIdx.x; j < a.r / 2; j += blockDim.x) rope_cs_f((double)t, a.inv_freq[j], &rc[j], &rs[j]);
-    if (threadIdx.x < 64) {                                    // one wave: the common reference max
-        float M = zs;
-        for (int s = threadIdx.x; s < S; s += 64) M = fmaxf(M, *(const float*)(pp + s * pstride));
-        for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-        if (threadIdx.x == 0) m_sh = M;
-    }
+    // the common reference max (with the sink)
+    float M = fmaxf(ml[0].x, ml[1].x);
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    if (lane == 0) red[0][wave] = M;
     __syncthreads();
-    const float M = m_sh;
-    for (int s = threadIdx.x; s < S; s += blockDim.x) w_sh[s] = exp2f(*(const float*)(pp + s * pstride) - M);
+    M = fmaxf(fmaxf(red[0][0], red[0][1]), zs);
+    // the denominator: sum of l_s * 2^(m_s - M) over splits in a fixed tree order
+    float w0 = ml[0].x == -INFINITY ? 0.f : exp2f(ml[0].x - M);
+    float w1 = ml[1].x == -INFINITY ? 0.f : exp2f(ml[1].x - M);
+    float Lp = ml[0].y * w0 + ml[1].y * w1;
+    for (int o = 32; o > 0; o >>= 1) Lp += __shfl_xor(Lp, o, 64);
+    if (lane == 0) red[1][wave] = Lp;
     __syncthreads();
-    if (threadIdx.x == 0) {                                    // the denominator, in split order
-        float L = exp2f(zs - M);
-        for (int s = 0; s < S; ++s) L += *(const float*)(pp + s * pstride + 4) * w_sh[s];
-        inv_sh = 1.0f / L;
-    }
-    __syncthreads();
-    const float inv = inv_sh;
-    for (int d4 = threadIdx.x; d4 < C / 4; d4 += blockDim.x) {
-        float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-        for (int s = 0; s < S; ++s) {
-            const char* src = pp + s * pstride + 16;
-            float v0, v1, v2, v3;
-            if (a.out_bf16) {
-                const uint2 u = *(const uint2*)(src + 8 * (size_t)d4);
-                v0 = bf16_to_f32(u.x & 0xFFFF); v1 = bf16_to_f32(u.x >> 16);
-                v2 = bf16_to_f32(u.y & 0xFFFF); v3 = bf16_to_f32(u.y >> 16);
-            } else {
-                const float4 u = *(const float4*)(src + 16 * (size_t)d4);
-                v0 = u.x; v1 = u.y; v2 = u.z; v3 = u.w;
-            }
-            const float w = w_sh[s];
-            o0 += v0 * w; o1 += v1 * w; o2 += v2 * w; o3 += v3 * w;
+    const float inv = 1.0f / (exp2f(zs - M) + (red[1][0] + red[1][1]));
+    // weighted sum of the partial outputs in split order
+    float o4[4] = {0.f, 0.f, 0.f, 0.f};
+    auto accum = [&](int sidx, uint4 u) {
+        const float ms = *(const float*)(pp + sidx * pstride);    // the split's max (cached)
+        const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
+        float v[4];
+        if (a.out_bf16) {
+            v[0] = bf16_to_f32(u.x & 0xFFFF); v[1] = bf16_to_f32(u.x >> 16);
+            v[2] = bf16_to_f32(u.y & 0xFFFF); v[3] = bf16_to_f32(u.y >> 16);
+        } else {
+            v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y);
+            v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
         }
-        o_sh[4 * d4] = o0 * inv; o_sh[4 * d4 + 1] = o1 * inv; o_sh[4 * d4 + 2] = o2 * inv; o_sh[4 * d4 + 3] = o3 * inv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o4[i] += v[i] * w;
+    };
+#pragma unroll
+    for (int sb = 0; sb < CB; ++sb)
+        if (sb < S) accum(sb, ov[sb]);
+    for (int sidx = CB; sidx < S; ++sidx) {
+        const char* src = pp + (size_t)sidx * pstride + 16;
+        uint4 u = make_uint4(0u, 0u, 0u, 0u);
+        if (dv) {
+            if (a.out_bf16) {
+                const uint2 h = *(const uint2*)(src + 8 * (size_t)d4);
+                u = make_uint4(h.x, h.y, 0u, 0u);
+            } else {
+                u = *(const uint4*)(src + 16 * (size_t)d4);
+            }
+        }
+        accum(sidx, u);
+    }
+    if (dv) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o_sh[4 * d4 + i] = o4[i] * inv;
     }
     __syncthreads();
     for (int d = threadIdx.x; d < C; d += blockDim.x) {
