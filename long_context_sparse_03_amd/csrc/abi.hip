@@ -262,6 +262,7 @@ int csa_cache_append(void* stream, const csa_layer_desc* layer, const csa_batch*
     a.max_entries = max_entries;
     a.win = win;
     a.n_tokens = n_tokens;
+    a.one_per_req = batch->max_new <= 1 && n_tokens == batch->n_req;
     a.cu_new = batch->cu_new;
     a.start_pos = batch->start_pos;
     a.block_table = batch->block_table;

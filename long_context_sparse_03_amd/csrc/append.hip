@@ -103,8 +103,8 @@ CSA_DEV void append_entry(const AppendArgs& a, int e, float* red, float* s_sh)
 
 CSA_DEV void append_window_row(const AppendArgs& a, int gtok)
 {
-    const int req = find_request(a.cu_new, a.n_req, gtok);
-    const int pos = a.start_pos[req] + (gtok - a.cu_new[req]);
+    const int req = a.one_per_req ? gtok : find_request(a.cu_new, a.n_req, gtok);
+    const int pos = a.start_pos[req] + (a.one_per_req ? 0 : gtok - a.cu_new[req]);
     const int slot = pos % a.win_cap;
     const float* src = a.win + (size_t)gtok * a.c;
     char* ring = (char*)a.state + (size_t)req * a.state_stride;

@@ -158,14 +158,41 @@ CSA_DEV void norm_rope_store(float* xs, float* red, int c, int r, const float* g
 
 CSA_DEV void merge_entry(const CompressArgs& a, int e, float* xs, float* red)
 {
-    // locate the entry: requests in order, entries of a request in index order
-    int total = 0, req = -1, ent = 0;
-    for (int rr = 0; rr < a.n_req; ++rr) {
-        int s = a.start_pos[rr], n = a.cu_new[rr + 1] - a.cu_new[rr];
-        int cnt = (s + n) / a.m - s / a.m;
-        if (req < 0 && e < total + cnt) { req = rr; ent = s / a.m + (e - total); }
-        total += cnt;
+    // locate the entry: requests in order, entries of a request in index
+    // order.  The threads take one request each (256 at a time): the entries
+    // a request completes, an exclusive scan over the requests, and the
+    // thread whose range holds e records (request, entry index).
+    __shared__ int wsum[4], loc[2];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (threadIdx.x == 0) loc[0] = -1;
+    int total = 0;
+    for (int base = 0; base < a.n_req; base += 256) {
+        const int rr = base + (int)threadIdx.x;
+        int cnt = 0, s = 0;
+        if (rr < a.n_req) {
+            s = a.start_pos[rr];
+            cnt = (s + a.cu_new[rr + 1] - a.cu_new[rr]) / a.m - s / a.m;
+        }
+        int inc = cnt;                                          // inclusive scan within the wave
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += y;
+        }
+        if (lane == 63) wsum[w] = inc;
+        __syncthreads();
+        int before = total;
+        for (int i = 0; i < 4; ++i) {
+            before += i < w ? wsum[i] : 0;
+            total += wsum[i];
+        }
+        before += inc - cnt;
+        if (cnt > 0 && e >= before && e < before + cnt) {
+            loc[0] = rr;
+            loc[1] = s / a.m + (e - before);
+        }
+        __syncthreads();
     }
+    const int req = loc[0], ent = loc[1];
     if (e == 0 && threadIdx.x == 0) *a.out_count = total;
     if (req < 0 || e >= a.max_entries) return;
 
@@ -278,8 +305,8 @@ __global__ __launch_bounds__(256) void post_decode_kernel(CompressArgs a, int nm
         return;
     }
     const int gtok = blockIdx.x - nm;
-    const int req = find_request(a.cu_new, a.n_req, gtok);
-    const int pos = a.start_pos[req] + (gtok - a.cu_new[req]);
+    const int req = a.one_per_req ? gtok : find_request(a.cu_new, a.n_req, gtok);
+    const int pos = a.start_pos[req] + (a.one_per_req ? 0 : gtok - a.cu_new[req]);
     window_row(a, gtok, pos, xs, red);
     float* tail = (float*)((char*)a.state + (size_t)req * a.state_stride + a.tail_off);
     const float* src = a.P + (size_t)gtok * a.ncols;
@@ -319,7 +346,9 @@ hipError_t launch_compress(hipStream_t st, const CompressArgs& a, const void* H,
     }
     const int nm = a.max_entries > 0 ? a.max_entries : 1;
     if (a.max_new <= 1) {
-        post_decode_kernel<<<nm + M, 256, 0, st>>>(a, nm);
+        CompressArgs b = a;
+        b.one_per_req = M == a.n_req;                           // at most one each, n_req of them
+        post_decode_kernel<<<nm + M, 256, 0, st>>>(b, nm);
     } else {
         merge_kernel<<<nm, 256, 0, st>>>(a);
         if (M > 0) {

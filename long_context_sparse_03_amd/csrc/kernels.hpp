@@ -27,6 +27,7 @@ struct CompressArgs {
     int max_entries;
     float* out_win;
     int max_new;               // largest number of new tokens of one request
+    int one_per_req;           // set by launch_compress: every request has exactly one new token
 };
 
 hipError_t launch_compress(hipStream_t st, const CompressArgs& a, const void* H, const void* W, const void* Wi,
@@ -53,6 +54,7 @@ struct AppendArgs {
     void* state;
     size_t state_stride;
     int win_cap;
+    int one_per_req;           // every request has exactly one new token (token g is request g's)
 };
 
 hipError_t launch_append(hipStream_t st, const AppendArgs& a);
