@@ -90,11 +90,12 @@ CSA_DEV f32x4_t mfma_fp4(uint4 a, int sa, uint4 b, int sb)
 // HT = head tiles (<= 4), S = fragments per lane group.
 constexpr int IDX_EPW = 1024;                 // entries per workgroup (MXFP4 kernel)
 constexpr int IDXD_EPW = 1024;                // entries per workgroup (fp32 / bf16 kernel)
-constexpr int IDXD_ITERS = IDXD_EPW / 256;    // iterations of 256 entries (64 per wave)
+constexpr int IDXD_TPI = 4;                   // 16-key tiles per wave and iteration (fp32 / bf16 kernel)
+constexpr int IDXD_ITERS = IDXD_EPW / (64 * IDXD_TPI);   // iterations of 64 * TPI entries
 constexpr int IDX_ITERS = IDX_EPW / 256;      // the same for the MXFP4 kernel
 
-template <int IDXF, int S>
-CSA_DEV void load_keys(const IndexArgs& a, const int* bt, int blk0, int e0, int V, int g, int li, uint4 (&B)[4][S])
+template <int IDXF, int S, int TPI>
+CSA_DEV void load_keys(const IndexArgs& a, const int* bt, int blk0, int e0, int V, int g, int li, uint4 (&B)[TPI][S])
 {
     // Loads are unconditional (entries past V are clamped to V-1): an MFMA
     // column only feeds the score of its own entry, and scores of entries
@@ -102,7 +103,7 @@ CSA_DEV void load_keys(const IndexArgs& a, const int* bt, int blk0, int e0, int 
     const int cI = a.cI, quarter = cI / 4;
     const size_t kbytes = IDXF == 0 ? (size_t)cI * 4 : (size_t)cI * 2;
 #pragma unroll
-    for (int tile = 0; tile < 4; ++tile) {
+    for (int tile = 0; tile < TPI; ++tile) {
         const int e = min(e0 + 16 * tile + li, V - 1);
         const int phys = bt[(e >> a.epb_log2) - blk0];
         const int slot = (e & (a.epb - 1));
@@ -187,33 +188,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S <= 4 ? 2 
     // ---- main loop: 256 entries per iteration (64 per wave); the next
     //      iterations' key loads are issued before this one's arithmetic
     constexpr int NB = 2;                       // key buffers (NB-1 iterations in flight)
-    uint4 B[NB][4][S];
+    constexpr int TPI = IDXD_TPI, EPI = 64 * TPI;           // tiles per wave, entries per iteration
+    uint4 B[NB][TPI][S];
     // The loads are unconditional (clamped to the last visible entry): loads
     // under a branch would make the wait counts below pessimistic.
 #pragma unroll
     for (int j = 0; j < NB - 1; ++j) {
-        if (j < IDXD_ITERS) load_keys<IDXF, S>(a, bt, blk0, wg0 + 256 * j + wave * 64, V, g, li, B[j]);
+        if (j < IDXD_ITERS) load_keys<IDXF, S, TPI>(a, bt, blk0, wg0 + EPI * j + wave * 16 * TPI, V, g, li, B[j]);
         __builtin_amdgcn_sched_barrier(0);            // keep the loads in iteration order
     }
 #pragma unroll
     for (int it = 0; it < IDXD_ITERS; ++it) {
         const int cur = it % NB;
-        const int e_base = wg0 + it * 256 + wave * 64;
+        const int e_base = wg0 + it * EPI + wave * 16 * TPI;
         if (it + NB - 1 < IDXD_ITERS)
-            load_keys<IDXF, S>(a, bt, blk0, e_base + 256 * (NB - 1), V, g, li, B[(it + NB - 1) % NB]);
+            load_keys<IDXF, S, TPI>(a, bt, blk0, e_base + EPI * (NB - 1), V, g, li, B[(it + NB - 1) % NB]);
         __builtin_amdgcn_sched_barrier(0);
         if (e_base >= V) break;                  // wave-uniform
         // head tiles outermost: each query fragment is read from LDS once
         // per iteration and serves the four key tiles; every tile's score
         // still sums the head tiles in order
-        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        float v[TPI];
+#pragma unroll
+        for (int tile = 0; tile < TPI; ++tile) v[tile] = 0.f;
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
             uint4 qf[S];
 #pragma unroll
             for (int s = 0; s < S; ++s) qf[s] = qfrag[ht][s][lane];
 #pragma unroll
-            for (int tile = 0; tile < 4; ++tile) {
+            for (int tile = 0; tile < TPI; ++tile) {
                 f32x4_t acc = zero4();
 #pragma unroll
                 for (int s = 0; s < S; ++s) acc = MMA::step(qf[s], B[cur][tile][s], acc);
@@ -222,7 +226,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S <= 4 ? 2 
             }
         }
 #pragma unroll
-        for (int tile = 0; tile < 4; ++tile) {
+        for (int tile = 0; tile < TPI; ++tile) {
             const int e = e_base + 16 * tile + li;
             float x = v[tile];
             x += __shfl_xor(x, 16, 64);
