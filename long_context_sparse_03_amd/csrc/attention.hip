@@ -75,7 +75,6 @@ struct AttnCfg {
 };
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
-#define CSA_LDS __attribute__((address_space(3)))
 
 template <int KVF, int C, int R, int HT>
 __global__ __launch_bounds__((AttnCfg<KVF, C, R, HT>::NT)) void attn_kernel(AttnArgs a)

@@ -145,6 +145,7 @@ CSA_DEV f32x4_t zero4() { f32x4_t z = {0.f, 0.f, 0.f, 0.f}; return z; }
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 #define CSA_GLOBAL __attribute__((address_space(1)))
+#define CSA_LDS __attribute__((address_space(3)))
 
 // 16-byte load as one dwordx4 (the address must be 16-byte aligned).
 CSA_DEV uint4 ld16(const void* p)

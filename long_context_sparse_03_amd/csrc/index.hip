@@ -23,6 +23,11 @@
 
 namespace csa {
 
+// ReLU as one clamp to [0, FLT_MAX]: the same value as max(x, 0) for every
+// finite x, without the canonicalising copy an IEEE-mode max of an MFMA
+// result costs
+CSA_DEV float relu_clamp(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, 3.40282347e38f); }
+
 // Load EPF elements of a row (f32 or bf16 storage) as one 16-byte fragment of
 // the MMA element type (T_MMA_BF16 = bf16 fragments).
 template <bool MMA_BF16>
@@ -240,22 +245,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S <= 4 ? 2 
     }
 }
 
-// Prefill-shaped launch (bf16 keys): eight queries of one request per
-// workgroup, one per wave, share every 128-key tile staged in LDS, so a key
-// is read from memory once per eight queries.  Tiles are double-buffered:
-// the next tile's loads are in flight while the current one is multiplied.
+// Prefill-shaped launch (bf16 keys, 128 channels): eight queries of one
+// request per workgroup, one per wave, share every 128-key tile staged in
+// LDS, so a key is read from memory once per eight queries.  Tiles are
+// double-buffered and go from memory straight into LDS (no register
+// staging): the next tile's loads are in flight while the current one is
+// multiplied.  A tile row is the key's 16 chunks of 16 bytes, chunk c at
+// slot c ^ (row mod 16), so the 16 lanes that read one chunk of 16
+// consecutive keys hit 16 different slots (all 64 banks).
 constexpr int PF_QPW = 8;                     // queries (waves) per workgroup
 constexpr int PF_TILE = 128;                  // keys per LDS tile
 constexpr int PF_ECH = 8192;                  // keys per workgroup
+constexpr int PF_CI = 128;                    // key channels (16 chunks of 16 bytes)
 
-template <int HT, int S>
-__global__ __launch_bounds__(512) void index_prefill_kernel(IndexArgs a, int groups_per_req)
+template <int HT, int S, bool BF16OUT>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void index_prefill_kernel(IndexArgs a, int groups_per_req)
 {
-    constexpr int KSTR = 136;                 // LDS key stride in bf16 (272 bytes: spreads banks)
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][PF_TILE * KSTR];
+    static_assert(S * 8 * 4 == PF_CI, "S steps of eight channels in each of four lane groups cover a key");
+    static_assert(PF_TILE == 8 * 4 * 4, "each wave brings four 1 KB pieces (four rows each) of a tile");
+    // two tile buffers as separate objects, so that reads of one need not
+    // wait for the loads in flight into the other
+    __shared__ __attribute__((aligned(16))) uint16_t Ks0[PF_TILE * PF_CI];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks1[PF_TILE * PF_CI];
     __shared__ int bt[PF_ECH / 32 + 2];
     __shared__ int cu_sh[1025];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
+    const int lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int req = blockIdx.y / groups_per_req, grp = blockIdx.y % groups_per_req;
     if (a.n_req >= 1024) return;                                    // host dispatch keeps n_req small here
     for (int i = threadIdx.x; i <= a.n_req; i += blockDim.x) cu_sh[i] = a.cu_new[i];
@@ -272,8 +287,8 @@ __global__ __launch_bounds__(512) void index_prefill_kernel(IndexArgs a, int gro
     const int e0 = blockIdx.x * PF_ECH;
     if (e0 >= Vmax) return;                                         // whole workgroup
     const int e1 = min(Vmax, e0 + PF_ECH);
-    const int cI = a.cI, nh = a.nh, quarter = cI / 4;
-    const size_t kbytes = (size_t)cI * 2;
+    const int nh = a.nh;
+    constexpr int quarter = PF_CI / 4;
 
     const int blk0 = e0 >> a.epb_log2;
     const int nblk = ((e1 - 1) >> a.epb_log2) - blk0 + 1;
@@ -285,7 +300,7 @@ __global__ __launch_bounds__(512) void index_prefill_kernel(IndexArgs a, int gro
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
         const int head = min(16 * ht + li, nh - 1);
-        const char* qp = (const char*)a.q + ((size_t)gq * nh + head) * cI * 2 + (size_t)g * quarter * 2;
+        const char* qp = (const char*)a.q + ((size_t)gq * nh + head) * PF_CI * 2 + (size_t)g * quarter * 2;
 #pragma unroll
         for (int s = 0; s < S; ++s) A[ht][s] = ld16(qp + 16 * s);
 #pragma unroll
@@ -301,66 +316,102 @@ __global__ __launch_bounds__(512) void index_prefill_kernel(IndexArgs a, int gro
     }
     __syncthreads();                                                // bt ready
 
-    // tile staging: 16-byte chunks, chunk c of key e at idx = e * CPK + c
-    const int CPK = cI / 8;                                         // chunks per key
-    const int chunks = PF_TILE * CPK;
-    constexpr int LPT = 4;                                          // chunk loads per thread (PF_TILE*16/512)
-    auto load_tile = [&](int t0, uint4 (&r)[LPT]) {
+    // one tile into a buffer: wave w fills bytes 1024 (4w + u) .. +1023 for
+    // u < 4, i.e. rows 16w + 4u .. +3; lane l brings chunk (l mod 16) ^ (row
+    // mod 16) of row 16w + 4u + l/16 (rows past the range repeat the last key)
+    auto issue_tile = [&](int t0, uint16_t* buf) {
 #pragma unroll
-        for (int u = 0; u < LPT; ++u) {
-            const int idx = threadIdx.x + u * 512;
-            const int e = min(t0 + idx / CPK, e1 - 1);
-            const int c = idx % CPK;
-            const char* kb = (const char*)a.keys + (size_t)bt[(e >> a.epb_log2) - blk0] * a.key_block_bytes;
-            r[u] = idx < chunks ? ld16(kb + (size_t)((e & (a.epb - 1))) * kbytes + 16 * c) : make_uint4(0, 0, 0, 0);
+        for (int u = 0; u < 4; ++u) {
+            const int row = 16 * wave + 4 * u + (lane >> 4);
+            const int e = min(t0 + row, e1 - 1);
+            const int c = (lane & 15) ^ (row & 15);
+            const char* src = (const char*)a.keys + (size_t)bt[(e >> a.epb_log2) - blk0] * a.key_block_bytes +
+                              (size_t)(e & (a.epb - 1)) * (PF_CI * 2) + 16 * c;
+            __builtin_amdgcn_global_load_lds((const CSA_GLOBAL void*)src,
+                                             (CSA_LDS void*)(buf + (16 * wave + 4 * u) * PF_CI), 16, 0, 0);
         }
     };
-    auto store_tile = [&](int buf, const uint4 (&r)[LPT]) {
+    // scores of the last tile, stored at the start of the next one (a
+    // store issued right before the end-of-tile wait would hold it up)
+    float xs[PF_TILE / 64];
+    int es = -1;                                                    // first key of those scores (-1: none)
+    auto store_scores = [&]() {
+        if (es < 0) return;
 #pragma unroll
-        for (int u = 0; u < LPT; ++u) {
-            const int idx = threadIdx.x + u * 512;
-            if (idx < chunks) *(uint4*)&Ks[buf][(idx / CPK) * KSTR + (idx % CPK) * 8] = r[u];
-        }
-    };
-
-    uint4 R[LPT];
-    load_tile(e0, R);
-    store_tile(0, R);
-    __syncthreads();
-    const int n_tiles = (e1 - e0 + PF_TILE - 1) / PF_TILE;
-    for (int it = 0; it < n_tiles; ++it) {
-        const int t0 = e0 + it * PF_TILE;
-        const bool more = it + 1 < n_tiles;
-        if (more) load_tile(t0 + PF_TILE, R);
-        const uint16_t* K = Ks[it & 1];
-        if (qvalid && t0 < V) {
-#pragma unroll 2
-            for (int et = 0; et < PF_TILE / 16; ++et) {
-                const int e = t0 + et * 16 + li;
-                uint4 B[S];
-#pragma unroll
-                for (int s = 0; s < S; ++s) B[s] = *(const uint4*)&K[(et * 16 + li) * KSTR + g * quarter + s * 8];
-                float v = 0.f;
-#pragma unroll
-                for (int ht = 0; ht < HT; ++ht) {
-                    f32x4_t acc = zero4();
-#pragma unroll
-                    for (int s = 0; s < S; ++s) acc = MmaBF16::step(A[ht][s], B[s], acc);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) v += wv[ht][i] * fmaxf(acc[i], 0.f);
-                }
-                v += __shfl_xor(v, 16, 64);
-                v += __shfl_xor(v, 32, 64);
-                if (g == 0 && e < V) {
-                    if (v == 0.0f) v = 0.0f;            // -0 is stored as +0
-                    if (a.score_bf16) ((uint16_t*)a.scores)[(size_t)gq * a.ld + e] = f32_to_bf16(v);
-                    else ((float*)a.scores)[(size_t)gq * a.ld + e] = v;
-                }
+        for (int eb = 0; eb < PF_TILE / 64; ++eb) {
+            const int e = es + eb * 64 + 16 * (2 * (g & 1) + (g >> 1)) + li;
+            if (e < V) {
+                float x = xs[eb];
+                if (x == 0.0f) x = 0.0f;                            // -0 is stored as +0
+                if constexpr (BF16OUT) ((uint16_t*)a.scores)[(size_t)gq * a.ld + e] = f32_to_bf16(x);
+                else ((float*)a.scores)[(size_t)gq * a.ld + e] = x;
             }
         }
-        if (more) store_tile((it + 1) & 1, R);
+        es = -1;
+    };
+    auto compute = [&](int t0, const uint16_t* K) {
+        if (!(qvalid && t0 < V)) return;
+#pragma unroll
+        for (int eb = 0; eb < PF_TILE / 64; ++eb) {                 // 64-key blocks
+            // v[j]: this lane's partial score of key 64 eb + 16 j + li over
+            // heads 4g .. 4g+3 of every head tile
+            float v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = eb * 64 + j * 16 + li;              // row mod 16 == li
+                uint4 B[S];
+#pragma unroll
+                for (int s = 0; s < S; ++s) B[s] = *(const uint4*)&K[row * PF_CI + 8 * ((g * S + s) ^ li)];
+                f32x4_t acc[HT];
+#pragma unroll
+                for (int ht = 0; ht < HT; ++ht) acc[ht] = zero4();
+#pragma unroll
+                for (int s = 0; s < S; ++s)
+#pragma unroll
+                    for (int ht = 0; ht < HT; ++ht) acc[ht] = MmaBF16::step(A[ht][s], B[s], acc[ht]);
+                float vj = 0.f;
+#pragma unroll
+                for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) vj += wv[ht][i] * relu_clamp(acc[ht][i]);
+                v[j] = vj;
+            }
+            // sum over the four lane groups, transposed: after the exchange
+            // with group g^1 a lane keeps two keys, after the one with g^2
+            // one key, (v_g + v_g^1) + (v_g^2 + v_g^3) in every case
+            const bool o1 = g & 1, o2 = g & 2;
+            float k0 = o1 ? v[2] : v[0], k1 = o1 ? v[3] : v[1];
+            k0 += __shfl_xor(o1 ? v[0] : v[2], 16, 64);
+            k1 += __shfl_xor(o1 ? v[1] : v[3], 16, 64);
+            float x = o2 ? k1 : k0;
+            x += __shfl_xor(o2 ? k0 : k1, 32, 64);
+            xs[eb] = x;
+        }
+        es = t0;
+    };
+    // every wave's loads of a tile have landed before the barrier after it
+    auto tile_done = [&]() {
+        __builtin_amdgcn_s_waitcnt(0x0F70);                         // vmcnt(0)
         __syncthreads();
+    };
+
+    const int n_tiles = (e1 - e0 + PF_TILE - 1) / PF_TILE;
+    issue_tile(e0, Ks0);
+    tile_done();
+    for (int it = 0; it < n_tiles; it += 2) {
+        const int t0 = e0 + it * PF_TILE;
+        // Ks1 was last read in the previous pass, finished before its barrier
+        if (it + 1 < n_tiles) issue_tile(t0 + PF_TILE, Ks1);
+        store_scores();
+        compute(t0, Ks0);
+        tile_done();
+        if (it + 1 >= n_tiles) break;
+        if (it + 2 < n_tiles) issue_tile(t0 + 2 * PF_TILE, Ks0);
+        store_scores();
+        compute(t0 + PF_TILE, Ks1);
+        tile_done();
     }
+    store_scores();
 }
 
 // MXFP4 decode launch: as the bf16 decode kernel, with the stored key bytes
@@ -519,6 +570,16 @@ static void launch_fmt(hipStream_t st, const IndexArgs& a, dim3 grid)
     }
 }
 
+template <bool BF16OUT>
+static void launch_prefill(hipStream_t st, const IndexArgs& a, dim3 grid, int groups)
+{
+    const int HT = (a.nh + 15) / 16;
+    if (HT == 4) index_prefill_kernel<4, 4, BF16OUT><<<grid, 512, 0, st>>>(a, groups);
+    else if (HT == 3) index_prefill_kernel<3, 4, BF16OUT><<<grid, 512, 0, st>>>(a, groups);
+    else if (HT == 2) index_prefill_kernel<2, 4, BF16OUT><<<grid, 512, 0, st>>>(a, groups);
+    else index_prefill_kernel<1, 4, BF16OUT><<<grid, 512, 0, st>>>(a, groups);
+}
+
 hipError_t launch_index(hipStream_t st, const IndexArgs& args, int max_visible, int max_new)
 {
     if (args.n_tokens <= 0) return hipSuccess;
@@ -529,10 +590,8 @@ hipError_t launch_index(hipStream_t st, const IndexArgs& args, int max_visible, 
         const int groups = (max_new + PF_QPW - 1) / PF_QPW;
         dim3 grid(max_visible > 0 ? (max_visible + PF_ECH - 1) / PF_ECH : 1, a.n_req * groups);
         const int HT = (a.nh + 15) / 16;
-        if (HT == 4) index_prefill_kernel<4, 4><<<grid, 512, 0, st>>>(a, groups);
-        else if (HT == 3) index_prefill_kernel<3, 4><<<grid, 512, 0, st>>>(a, groups);
-        else if (HT == 2) index_prefill_kernel<2, 4><<<grid, 512, 0, st>>>(a, groups);
-        else index_prefill_kernel<1, 4><<<grid, 512, 0, st>>>(a, groups);
+        if (a.score_bf16) launch_prefill<true>(st, a, grid, groups);
+        else launch_prefill<false>(st, a, grid, groups);
         return hipGetLastError();
     }
     const int epw = a.idx_fmt == 2 ? IDX_EPW : IDXD_EPW;
