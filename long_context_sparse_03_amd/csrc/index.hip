@@ -325,8 +325,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void i
             const int row = 16 * wave + 4 * u + (lane >> 4);
             const int e = min(t0 + row, e1 - 1);
             const int c = (lane & 15) ^ (row & 15);
-            const char* src = (const char*)a.keys + (size_t)bt[(e >> a.epb_log2) - blk0] * a.key_block_bytes +
-                              (size_t)(e & (a.epb - 1)) * (PF_CI * 2) + 16 * c;
+            const uint32_t in_blk = (uint32_t)(e & (a.epb - 1)) * (PF_CI * 2) + 16u * (uint32_t)c;
+            const char* src = (const char*)a.keys + (size_t)bt[(e >> a.epb_log2) - blk0] * a.key_block_bytes + in_blk;
             __builtin_amdgcn_global_load_lds((const CSA_GLOBAL void*)src,
                                              (CSA_LDS void*)(buf + (16 * wave + 4 * u) * PF_CI), 16, 0, 0);
         }
