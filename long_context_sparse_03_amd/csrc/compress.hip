@@ -212,34 +212,43 @@ CSA_DEV void merge_entry(const CompressArgs& a, int e, float* xs, float* red)
         const int colCb = base + w + cc;
         const int colZa = base + (a.overlap ? 2 * w : w) + cc;
         const int colZb = base + 3 * w + cc;
-        float mx = -INFINITY;
-        for (int r = 0; r < m; ++r) {
-            int p = m * ent + r;
-            const float* row = (p >= s0) ? a.P + (size_t)(cu + p - s0) * a.ncols : tail + (size_t)(p % a.R) * a.ncols;
-            mx = fmaxf(mx, row[colZa] + Ba[r * w + cc]);
-        }
-        if (has_b)
-            for (int r = 0; r < m; ++r) {
-                int p = m * (ent - 1) + r;
+        // softmax over the entry's m rows (and the previous entry's m rows
+        // with overlap) of Z + B, weights on C; rows go in batches of MB
+        // whose loads are all issued before use, with a running maximum
+        // across batches
+        constexpr int MB = 8;
+        const int nrows = has_b ? 2 * m : m;
+        float mx = -INFINITY, den = 0.f, acc = 0.f;
+        for (int r0 = 0; r0 < nrows; r0 += MB) {
+            float z[MB], cv[MB];
+#pragma unroll
+            for (int u = 0; u < MB; ++u) {
+                const int rr = min(r0 + u, nrows - 1);
+                const bool second = rr >= m;                    // a row of the previous entry (overlap)
+                const int r = second ? rr - m : rr;
+                const int p = m * (second ? ent - 1 : ent) + r;
                 const float* row = (p >= s0) ? a.P + (size_t)(cu + p - s0) * a.ncols : tail + (size_t)(p % a.R) * a.ncols;
-                mx = fmaxf(mx, row[colZb] + Bb[r * w + cc]);
+                z[u] = row[second ? colZb : colZa] + (second ? Bb : Ba)[r * w + cc];
+                cv[u] = row[second ? colCb : colCa];
             }
-        float den = 0.f, acc = 0.f;
-        for (int r = 0; r < m; ++r) {
-            int p = m * ent + r;
-            const float* row = (p >= s0) ? a.P + (size_t)(cu + p - s0) * a.ncols : tail + (size_t)(p % a.R) * a.ncols;
-            float wgt = expf(row[colZa] + Ba[r * w + cc] - mx);
-            den += wgt;
-            acc += wgt * row[colCa];
+            float cm = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < MB; ++u)
+                if (r0 + u < nrows) cm = fmaxf(cm, z[u]);
+            const float nm = fmaxf(mx, cm);
+            const float sc = mx == -INFINITY ? 0.f : expf(mx - nm);
+            den *= sc;
+            acc *= sc;
+#pragma unroll
+            for (int u = 0; u < MB; ++u) {
+                if (r0 + u < nrows) {
+                    const float wgt = expf(z[u] - nm);
+                    den += wgt;
+                    acc += wgt * cv[u];
+                }
+            }
+            mx = nm;
         }
-        if (has_b)
-            for (int r = 0; r < m; ++r) {
-                int p = m * (ent - 1) + r;
-                const float* row = (p >= s0) ? a.P + (size_t)(cu + p - s0) * a.ncols : tail + (size_t)(p % a.R) * a.ncols;
-                float wgt = expf(row[colZb] + Bb[r * w + cc] - mx);
-                den += wgt;
-                acc += wgt * row[colCb];
-            }
         float v = acc / den;
         if (ix) a.out_keys[(size_t)e * cI + cc] = v;
         else xs[cc] = v;
