@@ -126,6 +126,47 @@ __global__ __launch_bounds__(64 * NW) void proj_small(const T* __restrict__ X, c
     }
 }
 
+// Copy n floats from src to dst (and the first n2 of them also to dst2) with
+// the threads of the block: 16-byte pieces when every pointer is 16-byte
+// aligned and n, n2 are multiples of 4, each thread's pieces of a batch all
+// loaded before any is stored (one memory latency per batch).
+CSA_DEV void copy_row(float* __restrict__ dst, const float* __restrict__ src, int n, float* dst2 = nullptr, int n2 = 0)
+{
+    constexpr int U = 4;
+    if (((n | n2) & 3) == 0 && (((uintptr_t)dst | (uintptr_t)src | (uintptr_t)dst2) & 15) == 0) {
+        const int n4 = n >> 2;
+        for (int b = threadIdx.x; b < n4; b += U * blockDim.x) {
+            float4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = b + u * blockDim.x;
+                if (i < n4) v[u] = ((const float4*)src)[i];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = b + u * blockDim.x;
+                if (i < n4) ((float4*)dst)[i] = v[u];
+                if (4 * i < n2) ((float4*)dst2)[i] = v[u];
+            }
+        }
+    } else {
+        for (int b = threadIdx.x; b < n; b += U * blockDim.x) {
+            float v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = b + u * blockDim.x;
+                if (i < n) v[u] = src[i];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = b + u * blockDim.x;
+                if (i < n) dst[i] = v[u];
+                if (i < n2) dst2[i] = v[u];
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // RMSNorm + RoPE of one row held in LDS (xs[0..c)), written to out.
 // ---------------------------------------------------------------------------
@@ -263,7 +304,7 @@ CSA_DEV void merge_entry(const CompressArgs& a, int e, float* xs, float* red)
 
 __global__ __launch_bounds__(256) void merge_kernel(CompressArgs a)
 {
-    __shared__ float xs[512];
+    __shared__ __attribute__((aligned(16))) float xs[512];
     __shared__ float red[16];
     merge_entry(a, blockIdx.x, xs, red);
 }
@@ -272,15 +313,14 @@ __global__ __launch_bounds__(256) void merge_kernel(CompressArgs a)
 // rotated at its position
 CSA_DEV void window_row(const CompressArgs& a, int gtok, int pos, float* xs, float* red)
 {
-    const float* row = a.P + (size_t)gtok * a.ncols;       // C^a (CSA) or C (HCA) at column 0
-    for (int ch = threadIdx.x; ch < a.c; ch += blockDim.x) xs[ch] = row[ch];
+    copy_row(xs, a.P + (size_t)gtok * a.ncols, a.c);       // C^a (CSA) or C (HCA) at column 0
     __syncthreads();
     norm_rope_store(xs, red, a.c, a.r, a.gamma, a.eps, (double)pos, a.theta, a.out_win + (size_t)gtok * a.c);
 }
 
 __global__ __launch_bounds__(256) void window_rows_kernel(CompressArgs a)
 {
-    __shared__ float xs[512];
+    __shared__ __attribute__((aligned(16))) float xs[512];
     __shared__ float red[16];
     const int gtok = blockIdx.x;
     const int req = find_request(a.cu_new, a.n_req, gtok);
@@ -295,9 +335,7 @@ __global__ __launch_bounds__(256) void tail_update_kernel(CompressArgs a)
     if (j >= keep) return;
     const int p = s0 + n - keep + j;
     float* tail = (float*)((char*)a.state + (size_t)req * a.state_stride + a.tail_off);
-    const float* src = a.P + (size_t)(cu + n - keep + j) * a.ncols;
-    float* dst = tail + (size_t)(p % a.R) * a.ncols;
-    for (int ch = threadIdx.x; ch < a.ncols; ch += blockDim.x) dst[ch] = src[ch];
+    copy_row(tail + (size_t)(p % a.R) * a.ncols, a.P + (size_t)(cu + n - keep + j) * a.ncols, a.ncols);
 }
 
 // At most one new token per request: the merges, the window rows and the
@@ -307,7 +345,7 @@ __global__ __launch_bounds__(256) void tail_update_kernel(CompressArgs a)
 // an entry completed by the token at p reads positions p-R+1 .. p only.
 __global__ __launch_bounds__(256) void post_decode_kernel(CompressArgs a, int nm)
 {
-    __shared__ float xs[512];
+    __shared__ __attribute__((aligned(16))) float xs[512];
     __shared__ float red[16];
     if ((int)blockIdx.x < nm) {
         merge_entry(a, blockIdx.x, xs, red);
@@ -316,11 +354,12 @@ __global__ __launch_bounds__(256) void post_decode_kernel(CompressArgs a, int nm
     const int gtok = blockIdx.x - nm;
     const int req = a.one_per_req ? gtok : find_request(a.cu_new, a.n_req, gtok);
     const int pos = a.start_pos[req] + (a.one_per_req ? 0 : gtok - a.cu_new[req]);
-    window_row(a, gtok, pos, xs, red);
+    // one pass over the projected row: into the tail ring, and its first c
+    // channels (C^a, HCA: C) into LDS for the window row
     float* tail = (float*)((char*)a.state + (size_t)req * a.state_stride + a.tail_off);
-    const float* src = a.P + (size_t)gtok * a.ncols;
-    float* dst = tail + (size_t)(pos % a.R) * a.ncols;
-    for (int ch = threadIdx.x; ch < a.ncols; ch += blockDim.x) dst[ch] = src[ch];
+    copy_row(tail + (size_t)(pos % a.R) * a.ncols, a.P + (size_t)gtok * a.ncols, a.ncols, xs, a.c);
+    __syncthreads();
+    norm_rope_store(xs, red, a.c, a.r, a.gamma, a.eps, (double)pos, a.theta, a.out_win + (size_t)gtok * a.c);
 }
 
 // ---------------------------------------------------------------------------
