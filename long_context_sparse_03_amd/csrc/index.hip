@@ -528,19 +528,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
             for (int tile = 0; tile < 4; ++tile) {
                 const f32x4_t acc = mfma_fp4(Aq[ht], sa[ht], B[cur][tile], (int)SC[cur][tile]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) v[tile] += wv[ht][i] * fmaxf(acc[i], 0.f);
+                for (int i = 0; i < 4; ++i) v[tile] += wv[ht][i] * relu_clamp(acc[i]);
             }
-#pragma unroll
-        for (int tile = 0; tile < 4; ++tile) {
-            const int e = e_base + 16 * tile + li;
-            float x = v[tile];
-            x += __shfl_xor(x, 16, 64);
-            x += __shfl_xor(x, 32, 64);
-            if (g == 0 && e < V) {
-                if (x == 0.0f) x = 0.0f;
-                if (a.score_bf16) ((uint16_t*)a.scores)[(size_t)gq * a.ld + e] = f32_to_bf16(x);
-                else ((float*)a.scores)[(size_t)gq * a.ld + e] = x;
-            }
+        // transposed sum over the four lane groups (as the bf16 kernel):
+        // lane (g, li) ends with the entry of tile 2 (g & 1) + (g >> 1)
+        const bool o1 = g & 1, o2 = g & 2;
+        float k0 = o1 ? v[2] : v[0], k1 = o1 ? v[3] : v[1];
+        k0 += __shfl_xor(o1 ? v[0] : v[2], 16, 64);
+        k1 += __shfl_xor(o1 ? v[1] : v[3], 16, 64);
+        float x = o2 ? k1 : k0;
+        x += __shfl_xor(o2 ? k0 : k1, 32, 64);
+        const int e = e_base + 16 * (2 * (g & 1) + (g >> 1)) + li;
+        if (e < V) {
+            if (x == 0.0f) x = 0.0f;                    // -0 is stored as +0
+            if (a.score_bf16) ((uint16_t*)a.scores)[(size_t)gq * a.ld + e] = f32_to_bf16(x);
+            else ((float*)a.scores)[(size_t)gq * a.ld + e] = x;
         }
     }
 }
