@@ -295,6 +295,7 @@ int csa_index_scores(void* stream, const csa_layer_desc* layer, const csa_batch*
     REQUIRE(n_tokens >= 0, CSA_EINVAL, "n_tokens=%d", n_tokens);
     const int max_vis = batch->max_ctx / layer->m;
     REQUIRE(ld >= max_vis && ld >= 1, CSA_EINVAL, "ld=%d < largest visible count %d", ld, max_vis);
+    REQUIRE(max_vis / 1024 < 65535, CSA_EUNSUPPORTED, "max_ctx / m = %d entries exceeds the decode grid", max_vis);
     REQUIRE(n_tokens == 0 || (q_idx != nullptr && w != nullptr && idx_cache != nullptr && scores != nullptr &&
                               n_valid != nullptr),
             CSA_EINVAL, "NULL pointer argument");

@@ -132,8 +132,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S <= 4 ? 2 
     // key bytes are in flight)
     __shared__ uint4 qfrag[HT][S][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
-    const int gq = blockIdx.y;
-    const int wg0 = blockIdx.x * IDXD_EPW;
+    // query fastest in the dispatch order: every query's near-empty last
+    // key chunk comes after all full chunks, not among them
+    const int gq = blockIdx.x;
+    const int wg0 = blockIdx.y * IDXD_EPW;
     const int cI = a.cI, nh = a.nh;
     constexpr int QES = IDXF == 0 ? 4 : 2;      // query element size
     __shared__ int cu_sh[1025];
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S <= 4 ? 2 
         for (int i = 0; i < 4; ++i) wv[ht][i] = a.w[(size_t)gq * nh + min(16 * ht + 4 * g + i, nh - 1)];
     const int t = sp + tok;
     const int V = (t + 1) / a.m;
-    if (blockIdx.x == 0 && threadIdx.x == 0) a.n_valid[gq] = V;
+    if (blockIdx.y == 0 && threadIdx.x == 0) a.n_valid[gq] = V;
     if (wg0 >= V) return;                        // workgroup-uniform
 #pragma unroll
     for (int i = 0; i < (IDXD_EPW + 255) / 256; ++i)
@@ -431,8 +433,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
     __shared__ uint4 qc_sh[HT][64];              // quantised query: E2M1 codes ...
     __shared__ int qs_sh[HT][64];                // ... and E8M0 scales per (head tile, lane)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
-    const int gq = blockIdx.y;
-    const int wg0 = blockIdx.x * IDX_EPW;
+    const int gq = blockIdx.x;                   // query fastest (as the bf16 kernel)
+    const int wg0 = blockIdx.y * IDX_EPW;
     const int cI = a.cI, nh = a.nh;                // cI == 128: lane group g holds MX block g
     int req, tok;
     if (a.one_per_req) {                         // token gq is request gq's only new token
@@ -468,7 +470,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
         for (int i = 0; i < 4; ++i) wv[ht][i] = a.w[(size_t)gq * nh + min(16 * ht + 4 * g + i, nh - 1)];
     const int t = sp + tok;
     const int V = (t + 1) / a.m;
-    if (blockIdx.x == 0 && threadIdx.x == 0) a.n_valid[gq] = V;
+    if (blockIdx.y == 0 && threadIdx.x == 0) a.n_valid[gq] = V;
     if (wg0 >= V) return;                        // workgroup-uniform
 #pragma unroll
     for (int i = 0; i < (IDX_EPW + 255) / 256; ++i)
@@ -602,7 +604,7 @@ hipError_t launch_index(hipStream_t st, const IndexArgs& args, int max_visible, 
         return hipGetLastError();
     }
     const int epw = a.idx_fmt == 2 ? IDX_EPW : IDXD_EPW;
-    dim3 grid(max_visible > 0 ? (max_visible + epw - 1) / epw : 1, a.n_tokens);
+    dim3 grid(a.n_tokens, max_visible > 0 ? (max_visible + epw - 1) / epw : 1);
     if (a.idx_fmt == 0) launch_fmt<0>(st, a, grid);
     else if (a.idx_fmt == 1) launch_fmt<1>(st, a, grid);
     else {
