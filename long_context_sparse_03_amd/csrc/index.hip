@@ -295,7 +295,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void i
     if (e0 >= Vmax) return;                                         // whole workgroup
     const int e1 = min(Vmax, e0 + PF_ECH);
     const int nh = a.nh;
-    constexpr int quarter = PF_CI / 4;
 
     const int blk0 = e0 >> a.epb_log2;
     const int nblk = ((e1 - 1) >> a.epb_log2) - blk0 + 1;
@@ -307,9 +306,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void i
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
         const int head = min(16 * ht + li, nh - 1);
-        const char* qp = (const char*)a.q + ((size_t)gq * nh + head) * PF_CI * 2 + (size_t)g * quarter * 2;
+        // step s, lane group g: channels 32s + 8g .. +7, the decode kernel's
+        // split of the channels into MFMA steps, so both kernels sum in the
+        // same order and give identical scores
+        const char* qp = (const char*)a.q + ((size_t)gq * nh + head) * PF_CI * 2 + (size_t)g * 16;
 #pragma unroll
-        for (int s = 0; s < S; ++s) A[ht][s] = ld16(qp + 16 * s);
+        for (int s = 0; s < S; ++s) A[ht][s] = ld16(qp + 64 * s);
 #pragma unroll
         for (int i = 0; i < 4; ++i) wv[ht][i] = a.w[(size_t)gq * nh + min(16 * ht + 4 * g + i, nh - 1)];
     }
@@ -368,7 +370,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void i
                 const int row = eb * 64 + j * 16 + li;              // row mod 16 == li
                 uint4 B[S];
 #pragma unroll
-                for (int s = 0; s < S; ++s) B[s] = *(const uint4*)&K[row * PF_CI + 8 * ((g * S + s) ^ li)];
+                for (int s = 0; s < S; ++s) B[s] = *(const uint4*)&K[row * PF_CI + 8 * ((4 * s + g) ^ li)];
                 f32x4_t acc[HT];
 #pragma unroll
                 for (int ht = 0; ht < HT; ++ht) acc[ht] = zero4();

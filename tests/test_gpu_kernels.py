@@ -262,6 +262,38 @@ def test_index_scores(name):
         row += n_new[r]
 
 
+def test_index_prefill_matches_decode():
+    """The prefill-shaped launch (eight queries per workgroup) and the decode
+    launch split the channels into the same MFMA steps and sum in the same
+    order: a query's scores are bit-identical whichever launch scores it."""
+    desc = presets.csa_flash_decode(win_cap=256)
+    _flush("index prefill vs decode")
+    g = synth.rng(107)
+    E = 4096
+    epb = desc.block_tokens // desc.m
+    bt = synth.block_table(g, 1, (E + epb - 1) // epb)
+    st = LayerState(desc, 1, bt.size)
+    _fill_keys(st, desc, bt, [E], g)
+    T, s0 = 40, 4 * E - 40
+    qd = synth.queries(g, T, 1, 1, desc.n_idx_heads, desc.c_idx)
+    qI = to_dev(synth.to_bf16_values(qd["qI"]), torch.bfloat16)
+    w = to_dev(qd["w"])
+    ld = E + 8
+    one = torch.full((T, ld), float("nan"), dtype=torch.bfloat16, device="cuda")
+    nv = torch.zeros(T, dtype=torch.int32, device="cuda")
+    st.index(batch([s0], [T], bt), T, qI, w, one, ld, nv)             # one call, 40 new tokens
+    each = torch.full((T, ld), float("nan"), dtype=torch.bfloat16, device="cuda")
+    nv1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for j in range(T):                                                 # one call per token
+        st.index(batch([s0 + j], [1], bt), 1, qI[j:j + 1], w[j:j + 1], each[j:j + 1], ld, nv1)
+    torch.cuda.synchronize()
+    a = one.view(torch.int16).cpu().numpy()
+    b = each.view(torch.int16).cpu().numpy()
+    for j in range(T):
+        V = (s0 + j + 1) // desc.m
+        assert np.array_equal(a[j, :V], b[j, :V]), f"token {j}: prefill and decode scores differ"
+
+
 # ---------------------------------------------------------------------------
 # a5 / a6: attention with window and sink, on shared inputs
 # ---------------------------------------------------------------------------
