@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 1
+#define CSA_ABI_VERSION 2
 
 typedef enum {
     CSA_OK = 0,
@@ -109,7 +109,23 @@ typedef struct {
     int32_t out_fmt;       /* CSA_FMT_*: attention output */
     float rope_theta;      /* RoPE base (10000) */
     float norm_eps;        /* RMSNorm epsilon (1e-6) */
+    int32_t flags;         /* CSA_FLAG_* (0: none) */
 } csa_layer_desc;
+
+/* Batch invariance ([YP] "批无关性 & 计算确定性"; [DD] §6.3): every output of a
+ * request (entries, keys, window rows, scores, selection, attention output)
+ * is bit-identical whatever other requests share its calls.  The projection
+ * is computed by the same kernel whatever the number of rows (each row's sums
+ * do not depend on the other rows), and the attention always splits a
+ * query's rows at the same boundaries (CSA_INVARIANT_SPLIT_ROWS rows per
+ * split) and merges the splits in split order, also when a query has a
+ * single split.  A request's own chunking (how its tokens are spread over
+ * calls) still decides its FP8 block scales (see csa_cache_append).  The
+ * indexer and the top-k are batch-invariant in every mode.  Costs: the
+ * projection of many rows and the attention of many queries are slower, and
+ * the attention workspace grows with the split count. */
+#define CSA_FLAG_BATCH_INVARIANT 1
+#define CSA_INVARIANT_SPLIT_ROWS 128
 
 /* The requests of one call.  The struct itself is [host]. */
 typedef struct {

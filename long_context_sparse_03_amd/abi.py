@@ -14,6 +14,7 @@ KV_F32, KV_BF16, KV_FP8 = 0, 1, 2
 IDX_F32, IDX_BF16, IDX_MXFP4 = 0, 1, 2
 ACT_F32, ACT_BF16 = 0, 1
 OP_COMPRESS, OP_TOPK, OP_ATTENTION = 0, 1, 2
+FLAG_BATCH_INVARIANT = 1
 
 
 class CSAError(RuntimeError):
@@ -26,7 +27,7 @@ class LayerDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "kind", "m", "c", "rope_dim", "n_heads", "n_idx_heads", "c_idx", "top_k", "n_win", "win_cap",
         "block_tokens", "kv_fmt", "idx_fmt", "score_fmt", "act_fmt", "out_fmt")] + [
-        ("rope_theta", ctypes.c_float), ("norm_eps", ctypes.c_float)]
+        ("rope_theta", ctypes.c_float), ("norm_eps", ctypes.c_float), ("flags", ctypes.c_int32)]
 
     @property
     def epb(self) -> int:

@@ -36,6 +36,7 @@ bool is_csa(const csa_layer_desc* L) { return L->kind == CSA_KIND_CSA; }
 int tail_rows(const csa_layer_desc* L) { return is_csa(L) ? 2 * L->m : L->m; }
 
 int proj_cols(const csa_layer_desc* L) { return is_csa(L) ? 4 * L->c + 4 * L->c_idx : 2 * L->c; }
+bool invariant(const csa_layer_desc* L) { return (L->flags & CSA_FLAG_BATCH_INVARIANT) != 0; }
 
 size_t kv_record(const csa_layer_desc* L)
 {
@@ -99,6 +100,7 @@ int check_layer(const csa_layer_desc* L)
     REQUIRE(L->kv_fmt != CSA_KV_FP8 || (L->c - L->rope_dim) % 32 == 0, CSA_EUNSUPPORTED,
             "fp8 KV needs c - rope_dim to be a multiple of 32");
     REQUIRE(L->norm_eps >= 0.0f && L->rope_theta > 0.0f, CSA_EINVAL, "norm_eps / rope_theta");
+    REQUIRE((L->flags & ~CSA_FLAG_BATCH_INVARIANT) == 0, CSA_EINVAL, "flags=%d", L->flags);
     if (is_csa(L)) {
         REQUIRE(L->n_idx_heads >= 1 && L->n_idx_heads <= 64, CSA_EUNSUPPORTED, "n_idx_heads=%d (1..64)",
                 L->n_idx_heads);
@@ -174,7 +176,9 @@ int csa_workspace_size(const csa_layer_desc* layer, int op, int n_rows, int max_
         REQUIRE(top_k >= 1, CSA_EINVAL, "top_k=%d", top_k);
         *bytes = csa::topk_workspace(n_rows, max_cols, top_k, layer->score_fmt == CSA_FMT_BF16);
         return CSA_OK;
-    case CSA_OP_ATTENTION: *bytes = csa::attention_workspace(n_rows, layer->n_heads, layer->c, max_cols); return CSA_OK;
+    case CSA_OP_ATTENTION:
+        *bytes = csa::attention_workspace(n_rows, layer->n_heads, layer->c, max_cols, invariant(layer));
+        return CSA_OK;
     default: return fail(CSA_EINVAL, "op=%d", op);
     }
 }
@@ -206,6 +210,7 @@ int csa_compress_kv(void* stream, const csa_layer_desc* layer, const csa_batch* 
             need);
     csa::CompressArgs a;
     memset(&a, 0, sizeof(a));
+    a.invariant = invariant(layer);
     a.P = (float*)ws;
     a.ncols = proj_cols(layer);
     a.state = state;
@@ -353,11 +358,12 @@ static int attention_common(void* stream, const csa_layer_desc* layer, const csa
                               sinks != nullptr && out != nullptr),
             CSA_EINVAL, "NULL pointer argument");
     const int rows = (sel ? layer->top_k : batch->max_ctx / layer->m) + layer->n_win;
-    const size_t need = csa::attention_workspace(n_tokens, layer->n_heads, layer->c, rows);
+    const size_t need = csa::attention_workspace(n_tokens, layer->n_heads, layer->c, rows, invariant(layer));
     REQUIRE(ws_bytes >= need && (need == 0 || ws != nullptr), CSA_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes,
             need);
     csa::AttnArgs a;
     memset(&a, 0, sizeof(a));
+    a.invariant = invariant(layer);
     a.q = q;
     a.q_gamma = q_gamma;
     a.sel = sel;

@@ -33,6 +33,7 @@
 // split order, so the output does not depend on scheduling.
 #include <type_traits>
 
+#include "csa.h"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -515,7 +516,7 @@ __global__ __launch_bounds__((AttnCfg<KVF, C, R, HT>::NT)) void attn_kernel(Attn
         if (head >= a.nh) continue;
         const float mh = HT == 1 ? m_run : Mbuf[ht][li];
         const float lh = HT == 1 ? l_run : Lbuf[ht][li];
-        if (a.n_splits == 1) {
+        if (a.n_splits == 1 && !a.invariant) {
             const float zs = a.sinks[head] * LOG2E;
             const float M = fmaxf(mh, zs);
             const float sc = exp2f(mh - M);
@@ -930,7 +931,7 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
     // ---- output: the normalised result (one split) or the split partial
     //      (max, sum at bytes 0 and 4, the C channels from byte 16)
     if (!hvalid) return;
-    if (a.n_splits == 1) {
+    if (a.n_splits == 1 && !a.invariant) {
         const float zs = a.sinks[head] * LOG2E;
         const float M = fmaxf(m_run, zs);
         const float sc = exp2f(m_run - M);
@@ -1041,6 +1042,7 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a)
     auto accum = [&](int sidx, uint4 u) {
         const float ms = *(const float*)(pp + sidx * pstride);    // the split's max (cached)
         const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
+        if (w == 0.f) return;                                  // empty splits add nothing, not even +0
         float v[4];
         if (a.out_bf16) {
             v[0] = bf16_to_f32(u.x & 0xFFFF); v[1] = bf16_to_f32(u.x >> 16);
@@ -1102,11 +1104,18 @@ int attention_splits(int n_tokens, int n_heads, int rows_max)
     return splits;
 }
 
-// Bytes of split partials (fp32 layout, the larger of the two).
-size_t attention_workspace(int n_tokens, int n_heads, int c, int rows_max)
+// Splits of a batch-invariant layer: fixed boundaries every
+// CSA_INVARIANT_SPLIT_ROWS rows of a query.
+static int invariant_splits(int rows_max)
 {
-    const int s = attention_splits(n_tokens, n_heads, rows_max);
-    if (s <= 1) return 0;
+    return max(1, (rows_max + CSA_INVARIANT_SPLIT_ROWS - 1) / CSA_INVARIANT_SPLIT_ROWS);
+}
+
+// Bytes of split partials (fp32 layout, the larger of the two).
+size_t attention_workspace(int n_tokens, int n_heads, int c, int rows_max, bool invariant)
+{
+    const int s = invariant ? invariant_splits(rows_max) : attention_splits(n_tokens, n_heads, rows_max);
+    if (s <= 1 && !invariant) return 0;
     return (size_t)n_tokens * n_heads * s * (4 * (size_t)c + 16);
 }
 
@@ -1138,15 +1147,20 @@ hipError_t launch_attention(hipStream_t st, AttnArgs a)
     const int ht = head_tiles(a.nh);
     const int hg = (a.nh + 16 * ht - 1) / (16 * ht);
     const int tiles = (a.rows_max + 31) / 32;
-    a.n_splits = attention_splits(a.n_tokens, a.nh, a.rows_max);
-    a.tiles_per_split = (tiles + a.n_splits - 1) / a.n_splits;
+    if (a.invariant) {                       // the same boundaries in every batch
+        a.tiles_per_split = CSA_INVARIANT_SPLIT_ROWS / 32;
+        a.n_splits = invariant_splits(a.rows_max);
+    } else {
+        a.n_splits = attention_splits(a.n_tokens, a.nh, a.rows_max);
+        a.tiles_per_split = (tiles + a.n_splits - 1) / a.n_splits;
+    }
     for (int j = 0; j < a.r / 2 && j < 32; ++j) a.inv_freq[j] = rope_inv_freq(j, a.r, (double)a.theta);
     const dim3 grid(a.n_tokens, hg, a.n_splits);
     if (ht == 4 && a.kv_fmt == 2 && a.c == 512 && a.r == 64 && a.q_bf16 && a.win_bf16)
         attn_ht_kernel<512, 64, 4><<<grid, 512, 0, st>>>(a);     // FP8 serving shapes: two waves per head tile
     else if (ht == 4) launch_ht<4>(st, a, grid);
     else launch_ht<1>(st, a, grid);
-    if (a.n_splits > 1) attn_combine_kernel<<<dim3(a.n_tokens, a.nh), 128, 0, st>>>(a);
+    if (a.n_splits > 1 || a.invariant) attn_combine_kernel<<<dim3(a.n_tokens, a.nh), 128, 0, st>>>(a);
     return hipGetLastError();
 }
 

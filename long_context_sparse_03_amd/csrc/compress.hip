@@ -371,7 +371,9 @@ hipError_t launch_compress(hipStream_t st, const CompressArgs& a, const void* H,
 {
     const int N = a.ncols, M = n_tokens;
     if (M > 0) {
-        if (M <= 64) {
+        // batch-invariant layers: one kernel whatever the row count (its sums
+        // for a row do not depend on the other rows)
+        if (M <= 64 || a.invariant) {
             dim3 grid((N + 15) / 16, (M + 15) / 16);
             if (bf16 && d % (16 * MmaBF16::K) == 0)              // 16 waves of whole steps
                 proj_small<uint16_t, MmaBF16, 16><<<grid, 1024, 0, st>>>((const uint16_t*)H, (const uint16_t*)W,

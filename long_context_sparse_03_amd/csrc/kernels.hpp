@@ -28,6 +28,7 @@ struct CompressArgs {
     float* out_win;
     int max_new;               // largest number of new tokens of one request
     int one_per_req;           // set by launch_compress: every request has exactly one new token
+    int invariant;             // batch-invariant layer: the projection kernel does not depend on the row count
 };
 
 hipError_t launch_compress(hipStream_t st, const CompressArgs& a, const void* H, const void* W, const void* Wi,
@@ -109,11 +110,12 @@ struct AttnArgs {
     int n_splits;
     int tiles_per_split;
     int one_per_req;           // every request has exactly one new token (query gq is request gq's)
+    int invariant;             // batch-invariant layer: fixed split boundaries, always split partials + combine
     double inv_freq[32];       // RoPE frequencies theta^(-2j/r), j < r/2 (filled by launch_attention)
 };
 
 int attention_splits(int n_tokens, int n_heads, int rows_max);
-size_t attention_workspace(int n_tokens, int n_heads, int c, int rows_max);
+size_t attention_workspace(int n_tokens, int n_heads, int c, int rows_max, bool invariant);
 hipError_t launch_attention(hipStream_t st, AttnArgs a);
 
 }  // namespace csa

@@ -13,11 +13,11 @@ from .abi import (ACT_BF16, ACT_F32, IDX_BF16, IDX_F32, IDX_MXFP4, KIND_CSA, KIN
 
 def layer(kind, m, c, r, n_heads, n_idx_heads=0, c_idx=0, top_k=0, n_win=128, win_cap=128, block_tokens=128,
           kv_fmt=KV_F32, idx_fmt=IDX_F32, score_fmt=ACT_F32, act_fmt=ACT_F32, out_fmt=ACT_F32,
-          rope_theta=10000.0, norm_eps=1e-6) -> LayerDesc:
+          rope_theta=10000.0, norm_eps=1e-6, flags=0) -> LayerDesc:
     return LayerDesc(kind=kind, m=m, c=c, rope_dim=r, n_heads=n_heads, n_idx_heads=n_idx_heads, c_idx=c_idx,
                      top_k=top_k, n_win=n_win, win_cap=win_cap, block_tokens=block_tokens, kv_fmt=kv_fmt,
                      idx_fmt=idx_fmt, score_fmt=score_fmt, act_fmt=act_fmt, out_fmt=out_fmt,
-                     rope_theta=rope_theta, norm_eps=norm_eps)
+                     rope_theta=rope_theta, norm_eps=norm_eps, flags=flags)
 
 
 def tiny_csa_fp32(win_cap=128) -> LayerDesc:

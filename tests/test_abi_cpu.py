@@ -24,7 +24,7 @@ def test_header_symbols_exported():
     L = P.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert P.abi_version() == 1
+    assert P.abi_version() == 2
 
 
 def test_sizes_follow_layouts():
