@@ -45,7 +45,7 @@ def test_sizes_follow_layouts():
 
 @pytest.mark.parametrize("field,value,code", [("c", 96, -2), ("m", 3, -1), ("rope_dim", 7, -1), ("n_heads", 200, -2),
                                               ("kv_fmt", 9, -1), ("top_k", 0, -2), ("c_idx", 96, -2),
-                                              ("win_cap", 64, -1)])
+                                              ("win_cap", 64, -1), ("flags", 2, -1)])
 def test_layer_validation(field, value, code):
     d = presets.csa_flash_decode()
     setattr(d, field, value)
@@ -115,3 +115,8 @@ def test_workspace_sizes():
     assert P.workspace_size(d, abi.OP_TOPK, 4, 262144, 1024) == 4 * 26 * 1024 * 8  # 26 chunks of 10240
     assert P.workspace_size(d, abi.OP_ATTENTION, 16, 640) > 0               # few queries: split-KV partials
     assert P.workspace_size(d, abi.OP_ATTENTION, 4096, 640) == 0
+    # batch-invariant layer: partials of splits every 128 rows, whatever the
+    # number of queries (640 rows: 5 splits of 512 fp32 channels + 16 bytes)
+    d.flags = abi.FLAG_BATCH_INVARIANT
+    assert P.workspace_size(d, abi.OP_ATTENTION, 4096, 640) == 4096 * 64 * 5 * (4 * 512 + 16)
+    assert P.workspace_size(d, abi.OP_ATTENTION, 1, 100) == 64 * 1 * (4 * 512 + 16)
