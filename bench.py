@@ -320,6 +320,38 @@ def time_prefill(steps, warmup):
             "attention_tflops": round(attn_flop / (parts[3] * 1e-3) / 1e12, 1)}
 
 
+def time_prefix(reps=3):
+    """Prefix reuse, host-memory tier: the blocks of a 1,048,576-token CSA
+    prefix (Pro shape, 8192 blocks of KV and indexer keys) to and from pinned
+    host memory, one launch each way."""
+    import torch
+    from long_context_sparse_03_amd import abi, presets
+    from long_context_sparse_03_amd.layer import LayerState
+
+    desc = presets.csa_pro()
+    n_blocks = (1 << 20) // desc.block_tokens
+    st = LayerState(desc, 1, n_blocks)
+    ids = torch.arange(n_blocks, dtype=torch.int32, device="cuda")
+    host = torch.empty(abi.prefix_bytes(desc, n_blocks), dtype=torch.uint8, pin_memory=True)
+    nbytes = host.numel()
+    res = {}
+    for name, direction in (("save", abi.TO_HOST), ("restore", abi.FROM_HOST)):
+        abi.prefix_blocks(desc, n_blocks, ids, st.kv, st.idx, host, direction)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            abi.prefix_blocks(desc, n_blocks, ids, st.kv, st.idx, host, direction)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[name] = {"ms": round(ms, 3), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    del st, host
+    torch.cuda.empty_cache()
+    return {"workload": "csa_prefix_1m_host", "blocks": n_blocks, "bytes": nbytes, **res,
+            "note": "kernel reads / writes pinned host memory over PCIe"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -351,6 +383,7 @@ def main():
         other = "hybrid_decode_1m" if args.workload == "csa_decode_128k" else "csa_decode_128k"
         extras[other] = time_decode(other, max(20, args.steps // 2), args.warmup, 0, not args.no_graph)
         extras["csa_prefill_1m"] = time_prefill(max(2, min(5, args.steps // 40)), 1)
+        extras["csa_prefix_1m_host"] = time_prefix()
         # warm: one cache replica, whose step working set stays in the 256 MB
         # last-level cache between steps (the primary number rotates
         # replicas so that it does not)

@@ -216,6 +216,37 @@ int csa_cache_append(void* stream, const csa_layer_desc* layer, const csa_batch*
                      void* kv_cache, void* idx_cache, void* state);
 
 /*
+ * Prefix reuse, host-memory tier ([DD] §7: the compressed entries of a shared
+ * prefix are stored whole; the sliding window by one of three strategies, one
+ * of them a checkpoint every p tokens).  Copies between a layer's caches and
+ * PINNED host memory (hipHostMalloc, or a torch tensor with pin_memory=True);
+ * any other host pointer is rejected with CSA_EINVAL before anything runs.
+ *
+ * csa_prefix_blocks: the n_blocks physical blocks block_ids[0..n_blocks)
+ *   (device int32; negative ids are skipped) of kv_cache and, for CSA, of
+ *   idx_cache, to (CSA_TO_HOST) or from (CSA_FROM_HOST) host, packed as
+ *   n_blocks x kv_block_bytes followed (CSA) by n_blocks x idx_block_bytes
+ *   (csa_prefix_bytes).  One kernel reads or writes the host buffer directly.
+ * csa_prefix_state: one state slot (window ring and compressor tail ring,
+ *   state_bytes) to or from host, stream-ordered.
+ *
+ * A request resumes bit-identically (every later output equal to the
+ * uninterrupted run's) from its blocks and its state slot saved together
+ * after a call that ended at position P.  A block holding only entries
+ * below P is final once complete (its FP8 scale changes only when entries
+ * are appended to it), so with P a multiple of block_tokens the blocks of a
+ * shared prefix can be saved once and the window state checkpointed every p
+ * tokens (p a multiple of block_tokens).  Calls sharing buffers must be
+ * ordered by the caller; host buffers must not be reused before the stream
+ * has reached the copy.
+ */
+enum { CSA_TO_HOST = 0, CSA_FROM_HOST = 1 };
+int csa_prefix_bytes(const csa_layer_desc* layer, int n_blocks, size_t* bytes);
+int csa_prefix_blocks(void* stream, const csa_layer_desc* layer, int n_blocks, const int32_t* block_ids,
+                      void* kv_cache, void* idx_cache, void* host, int dir);
+int csa_prefix_state(void* stream, const csa_layer_desc* layer, void* state_slot, void* host, int dir);
+
+/*
  * a3: Lightning Indexer scores ([DD] §1.2 Step 2; [YP] eq. (8); [DD] §6.2).
  * For every new token t of the batch (query row g = its global row) and every
  * visible entry s < V_t:

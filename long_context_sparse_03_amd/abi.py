@@ -15,6 +15,7 @@ IDX_F32, IDX_BF16, IDX_MXFP4 = 0, 1, 2
 ACT_F32, ACT_BF16 = 0, 1
 OP_COMPRESS, OP_TOPK, OP_ATTENTION = 0, 1, 2
 FLAG_BATCH_INVARIANT = 1
+TO_HOST, FROM_HOST = 0, 1
 
 
 class CSAError(RuntimeError):
@@ -70,6 +71,9 @@ def lib():
             "csa_topk_select": (I, [P, I, I, P, I, P, I, P, P, Z]),
             "csa_sparse_mqa": (I, [P, LP, BP, I, P, P, P, P, P, P, P, P, Z]),
             "csa_hca_attention": (I, [P, LP, BP, I, P, P, P, P, P, P, P, Z]),
+            "csa_prefix_bytes": (I, [LP, I, ctypes.POINTER(ctypes.c_size_t)]),
+            "csa_prefix_blocks": (I, [P, LP, I, P, P, P, P, I]),
+            "csa_prefix_state": (I, [P, LP, P, P, I]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -153,3 +157,23 @@ def hca_attention(desc, batch, n_tokens, q, q_gamma, kv_cache, state, sinks, out
         _stream(stream), ctypes.byref(desc), ctypes.byref(batch), n_tokens, _ptr(q), _ptr(q_gamma),
         _ptr(kv_cache), _ptr(state), _ptr(sinks), _ptr(out), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size()))
+
+
+def prefix_bytes(desc, n_blocks: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check("csa_prefix_bytes", lib().csa_prefix_bytes(ctypes.byref(desc), n_blocks, ctypes.byref(out)))
+    return out.value
+
+
+def prefix_blocks(desc, n_blocks, block_ids, kv_cache, idx_cache, host, direction, stream=None):
+    """Blocks block_ids (device int32) of the caches to (TO_HOST) or from
+    (FROM_HOST) the pinned host tensor `host`."""
+    _check("csa_prefix_blocks", lib().csa_prefix_blocks(
+        _stream(stream), ctypes.byref(desc), n_blocks, _ptr(block_ids), _ptr(kv_cache), _ptr(idx_cache), _ptr(host),
+        direction))
+
+
+def prefix_state(desc, state_slot_ptr: int, host, direction, stream=None):
+    """One state slot (device address) to or from the pinned host tensor `host`."""
+    _check("csa_prefix_state", lib().csa_prefix_state(
+        _stream(stream), ctypes.byref(desc), state_slot_ptr, _ptr(host), direction))

@@ -420,4 +420,65 @@ int csa_hca_attention(void* stream, const csa_layer_desc* layer, const csa_batch
                             ws_bytes);
 }
 
+// ---- prefix reuse (host-memory tier) --------------------------------------
+
+// Device address of a host buffer the device may read and write (pinned host
+// memory, or device memory), or null.
+static void* device_visible(void* host)
+{
+    if (host == nullptr) return nullptr;
+    hipPointerAttribute_t at;
+    const hipError_t e = hipPointerGetAttributes(&at, host);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();                  // pageable memory: clear the error it leaves
+        return nullptr;
+    }
+    if (at.type != hipMemoryTypeHost && at.type != hipMemoryTypeDevice) return nullptr;
+    return at.devicePointer != nullptr ? at.devicePointer : host;
+}
+
+int csa_prefix_bytes(const csa_layer_desc* layer, int n_blocks, size_t* bytes)
+{
+    CHECK(check_layer(layer));
+    REQUIRE(n_blocks >= 0 && bytes != nullptr, CSA_EINVAL, "n_blocks=%d / bytes", n_blocks);
+    *bytes = (size_t)n_blocks * (kv_block(layer) + idx_block(layer));
+    return CSA_OK;
+}
+
+int csa_prefix_blocks(void* stream, const csa_layer_desc* layer, int n_blocks, const int32_t* block_ids,
+                      void* kv_cache, void* idx_cache, void* host, int dir)
+{
+    CHECK(check_layer(layer));
+    const bool csa = is_csa(layer);
+    REQUIRE(dir == CSA_TO_HOST || dir == CSA_FROM_HOST, CSA_EINVAL, "dir=%d", dir);
+    REQUIRE(n_blocks >= 0, CSA_EINVAL, "n_blocks=%d", n_blocks);
+    if (n_blocks == 0) return CSA_OK;
+    REQUIRE(block_ids != nullptr && kv_cache != nullptr && (!csa || idx_cache != nullptr), CSA_EINVAL,
+            "block_ids / kv_cache / idx_cache is NULL");
+    REQUIRE(kv_block(layer) % 16 == 0 && idx_block(layer) % 16 == 0, CSA_EUNSUPPORTED, "block bytes not 16-aligned");
+    char* h = (char*)device_visible(host);
+    REQUIRE(h != nullptr && ((uintptr_t)h & 15) == 0, CSA_EINVAL,
+            "host buffer must be 16-byte aligned pinned host memory (hipHostMalloc / pin_memory)");
+    const hipStream_t st = (hipStream_t)stream;
+    hipError_t e = csa::launch_prefix_blocks(st, n_blocks, block_ids, kv_cache, kv_block(layer), h, dir);
+    if (e == hipSuccess && csa)
+        e = csa::launch_prefix_blocks(st, n_blocks, block_ids, idx_cache, idx_block(layer),
+                                      h + (size_t)n_blocks * kv_block(layer), dir);
+    return hip_status(e, "prefix_blocks launch");
+}
+
+int csa_prefix_state(void* stream, const csa_layer_desc* layer, void* state_slot, void* host, int dir)
+{
+    CHECK(check_layer(layer));
+    REQUIRE(dir == CSA_TO_HOST || dir == CSA_FROM_HOST, CSA_EINVAL, "dir=%d", dir);
+    REQUIRE(state_slot != nullptr, CSA_EINVAL, "state_slot is NULL");
+    REQUIRE(device_visible(host) != nullptr, CSA_EINVAL,
+            "host buffer must be pinned host memory (hipHostMalloc / pin_memory)");
+    const size_t n = state_bytes(layer);
+    const hipError_t e = dir == CSA_TO_HOST
+        ? hipMemcpyAsync(host, state_slot, n, hipMemcpyDeviceToHost, (hipStream_t)stream)
+        : hipMemcpyAsync(state_slot, host, n, hipMemcpyHostToDevice, (hipStream_t)stream);
+    return hip_status(e, "prefix_state copy");
+}
+
 }  // extern "C"

@@ -114,6 +114,10 @@ struct AttnArgs {
     double inv_freq[32];       // RoPE frequencies theta^(-2j/r), j < r/2 (filled by launch_attention)
 };
 
+// Prefix reuse: n_blocks blocks (ids, device) of a pool to / from host (dir 0 / 1).
+hipError_t launch_prefix_blocks(hipStream_t st, int n_blocks, const int32_t* ids, void* pool, size_t block_bytes,
+                                void* host, int dir);
+
 int attention_splits(int n_tokens, int n_heads, int rows_max);
 size_t attention_workspace(int n_tokens, int n_heads, int c, int rows_max, bool invariant);
 hipError_t launch_attention(hipStream_t st, AttnArgs a);

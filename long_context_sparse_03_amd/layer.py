@@ -103,3 +103,23 @@ class LayerState:
             abi.sparse_mqa(d, bi.batch, n_tokens, q, q_gamma, sel, self.kv, self.state, sinks, out, ws, stream=stream)
         else:
             abi.hca_attention(d, bi.batch, n_tokens, q, q_gamma, self.kv, self.state, sinks, out, ws, stream=stream)
+
+    # ---- prefix reuse (host-memory tier)
+    def save_prefix(self, block_ids: torch.Tensor, slot: int, stream=None):
+        """Blocks block_ids (device int32) and state slot `slot` into new
+        pinned host tensors (blocks, state)."""
+        n = int(block_ids.numel())
+        blocks = torch.empty(abi.prefix_bytes(self.desc, n), dtype=torch.uint8, pin_memory=True)
+        state = torch.empty(self.sizes.state_bytes, dtype=torch.uint8, pin_memory=True)
+        abi.prefix_blocks(self.desc, n, block_ids, self.kv, self.idx, blocks, abi.TO_HOST, stream=stream)
+        abi.prefix_state(self.desc, self.state.data_ptr() + slot * self.sizes.state_bytes, state, abi.TO_HOST,
+                         stream=stream)
+        return blocks, state
+
+    def load_prefix(self, block_ids: torch.Tensor, slot: int, blocks: torch.Tensor, state: torch.Tensor,
+                    stream=None):
+        """The reverse of save_prefix, into blocks block_ids and slot `slot`."""
+        abi.prefix_blocks(self.desc, int(block_ids.numel()), block_ids, self.kv, self.idx, blocks, abi.FROM_HOST,
+                          stream=stream)
+        abi.prefix_state(self.desc, self.state.data_ptr() + slot * self.sizes.state_bytes, state, abi.FROM_HOST,
+                         stream=stream)

@@ -120,3 +120,19 @@ def test_workspace_sizes():
     d.flags = abi.FLAG_BATCH_INVARIANT
     assert P.workspace_size(d, abi.OP_ATTENTION, 4096, 640) == 4096 * 64 * 5 * (4 * 512 + 16)
     assert P.workspace_size(d, abi.OP_ATTENTION, 1, 100) == 64 * 1 * (4 * 512 + 16)
+
+
+def test_prefix_argument_checks():
+    """Prefix copies validate direction and counts on the host before any
+    device call."""
+    d = presets.csa_flash_decode()
+    assert P.prefix_bytes(d, 23) == 23 * (18496 + 8192)
+    assert P.prefix_bytes(presets.hca_pro(), 4) == 4 * (64 + 576)
+    L = P.lib()
+    assert L.csa_prefix_blocks(None, ctypes.byref(d), 1, 8, 8, 8, 8, 7) == -1      # direction
+    assert L.csa_prefix_blocks(None, ctypes.byref(d), -1, 8, 8, 8, 8, 0) == -1     # block count
+    assert L.csa_prefix_blocks(None, ctypes.byref(d), 0, None, None, None, None, 0) == 0   # nothing to copy
+    assert L.csa_prefix_blocks(None, ctypes.byref(d), 2, None, 8, 8, 8, 0) == -1   # no block list
+    assert L.csa_prefix_state(None, ctypes.byref(d), 8, 8, 3) == -1               # direction
+    assert L.csa_prefix_state(None, ctypes.byref(d), None, 8, 0) == -1            # no slot
+

@@ -1,0 +1,65 @@
+"""Prefix reuse ([DD] §7, host-memory tier): a request saved to pinned host
+memory after a call that ended at a block boundary, and restored into other
+physical blocks of a fresh cache, continues bit-identically to the
+uninterrupted run (compressed entries, keys, window rows, index scores,
+selections and attention outputs of every later call)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from long_context_sparse_03_amd import abi, presets
+from long_context_sparse_03_amd.layer import LayerState
+from test_gpu_invariance import _desc, _rows, _same
+from test_gpu_layers import Params, gpu_layer_call
+
+pytestmark = pytest.mark.gpu
+
+
+def _outputs(desc, got, cnt):
+    o = {"entries": got["entries"][:got["count"]], "win": got["win"][:cnt], "out": got["out"][:cnt]}
+    if desc.kind == abi.KIND_CSA:
+        o.update(keys=got["keys"][:got["count"]], sel=got["sel"][:cnt])
+    return o
+
+
+@pytest.mark.parametrize("kind", ["csa", "hca"])
+def test_prefix_save_and_restore(kind):
+    desc = _desc(kind)
+    desc.flags = 0
+    d = presets.D_FLASH
+    g = synth.rng(301)
+    P = Params(g, desc, d)
+    P_len, steps = 23 * desc.block_tokens, 5          # checkpoint at a block boundary
+    x = _rows(d, P_len + steps, g, desc)
+    n_blocks = (P_len + steps + desc.block_tokens - 1) // desc.block_tokens + 1
+    csa = desc.kind == abi.KIND_CSA
+    print(f"prefix reuse {kind}: prefix {P_len} tokens, {steps} decode steps", flush=True)
+
+    def call(st, bt, s, n):
+        sl = slice(s, s + n)
+        return gpu_layer_call(st, desc, P, [s], [n], bt, x["H"][sl], x["q"][sl], x["qI"][sl] if csa else None,
+                              x["w"][sl] if csa else None)
+
+    # uninterrupted run; the prefix is saved after the call that ends at P_len
+    bt1 = np.arange(n_blocks, dtype=np.int32).reshape(1, -1)
+    st1 = LayerState(desc, 1, n_blocks)
+    call(st1, bt1, 0, P_len)
+    ids1 = torch.from_numpy(bt1[0, :P_len // desc.block_tokens].copy()).cuda()
+    blocks, state = st1.save_prefix(ids1, 0)
+    torch.cuda.synchronize()
+    ref = [_outputs(desc, call(st1, bt1, P_len + i, 1), 1) for i in range(steps)]
+
+    # restore into other physical blocks of a fresh, larger pool
+    pool = 3 * n_blocks
+    bt2 = (pool - 1 - 2 * np.arange(n_blocks, dtype=np.int32)).reshape(1, -1)
+    st2 = LayerState(desc, 1, pool)
+    ids2 = torch.from_numpy(bt2[0, :P_len // desc.block_tokens].copy()).cuda()
+    st2.load_prefix(ids2, 0, blocks, state)
+    got = [_outputs(desc, call(st2, bt2, P_len + i, 1), 1) for i in range(steps)]
+    for i, (a, b) in enumerate(zip(ref, got)):
+        for key in a:
+            _same(a[key], b[key], f"step {i} {key}")
+    # the host copy holds the blocks as the cache did at the checkpoint
+    assert blocks.numel() == abi.prefix_bytes(desc, P_len // desc.block_tokens)
+    print(f"  restored run bit-identical over {steps} steps", flush=True)
