@@ -352,6 +352,46 @@ def time_prefix(reps=3):
             "note": "kernel reads / writes pinned host memory over PCIe"}
 
 
+def time_projections(reps=20):
+    """The dense projections around the path at the Pro shape for one decode
+    step of 16 requests: the low-rank query path (d 7168 -> d_c 1024 -> 128
+    heads x 512 and 64 indexer heads x 128, plus the 64 head weights) and the
+    grouped output projection (16 groups of 8 heads -> 1024 each -> 7168).
+    Weight-streaming: bytes are the bf16 weights read once."""
+    import torch
+    from long_context_sparse_03_amd import abi
+    from long_context_sparse_03_amd.projections import output_projection, query_path
+
+    T, d, dc, nqc, nic, nhi, ng, dg = 16, 7168, 1024, 128 * 512, 64 * 128, 64, 16, 1024
+    gen = torch.Generator(device="cuda").manual_seed(7)
+
+    def w(*shape):
+        return (torch.randn(*shape, device="cuda", generator=gen) / shape[-1] ** 0.5).to(torch.bfloat16)
+
+    h, o = w(T, d), w(T, nqc)
+    W_DQ, W_UQ, W_UQI, W_w = w(dc, d), w(nqc, dc), w(nic, dc), w(nhi, d)
+    W_G, W_O = w(ng, dg, nqc // ng), w(d, ng * dg)
+    qb = 2 * (W_DQ.numel() + W_UQ.numel() + W_UQI.numel() + W_w.numel())
+    ob = 2 * (W_G.numel() + W_O.numel())
+    res = {}
+    for name, fn, nbytes in (("query_path", lambda: query_path(h, W_DQ, W_UQ, W_UQI, W_w), qb),
+                             ("output_projection", lambda: output_projection(o, W_G, W_O), ob)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1000
+        res[name] = {"us": round(us, 1), "weight_bytes": nbytes, "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+    return {"workload": "pro_projections_decode", "rows": T, **res,
+            "note": "the same weights in every repetition: the query path's 167 MB fit the 256 MB last-level "
+                    "cache, the output projection's 369 MB do not"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -384,6 +424,7 @@ def main():
         extras[other] = time_decode(other, max(20, args.steps // 2), args.warmup, 0, not args.no_graph)
         extras["csa_prefill_1m"] = time_prefill(max(2, min(5, args.steps // 40)), 1)
         extras["csa_prefix_1m_host"] = time_prefix()
+        extras["pro_projections_decode"] = time_projections()
         # warm: one cache replica, whose step working set stays in the 256 MB
         # last-level cache between steps (the primary number rotates
         # replicas so that it does not)

@@ -247,6 +247,26 @@ int csa_prefix_blocks(void* stream, const csa_layer_desc* layer, int n_blocks, c
 int csa_prefix_state(void* stream, const csa_layer_desc* layer, void* state_slot, void* host, int dir);
 
 /*
+ * The dense projections on either side of the path ([DD] §1.2 Step 2 query
+ * side: c^Q_t = h_t . W^DQ, then the indexer queries from c^Q; Step 3:
+ * grouped output projection, g groups of head outputs each projected to d_g,
+ * concatenated and projected to d; [AD]: d_c = 1024; [DD]: V4-Pro g = 16,
+ * d_g = 1024).  The caller composes them (see DESIGN): one GEMM per call,
+ * fp32 accumulation on the MFMA, no workspace.
+ *
+ * csa_linear:         Y[n_rows x N] = X[n_rows x K] . W^T,  W [N x K] (one row per output)
+ * csa_grouped_linear: for g < groups:
+ *                     Y[:, g*N .. g*N+N) = X[:, g*K .. g*K+K) . W[g]^T,  W [groups x N x K]
+ *   X, W in act_fmt (CSA_FMT_BF16 or CSA_FMT_F32), Y in out_fmt (bf16 rounds
+ *   to nearest even).  K must be a positive multiple of 128; all pointers
+ *   16-byte aligned.
+ */
+int csa_linear(void* stream, int act_fmt, int out_fmt, int n_rows, int K, int N, const void* X, const void* W,
+               void* Y);
+int csa_grouped_linear(void* stream, int act_fmt, int out_fmt, int n_rows, int groups, int K, int N, const void* X,
+                       const void* W, void* Y);
+
+/*
  * a3: Lightning Indexer scores ([DD] §1.2 Step 2; [YP] eq. (8); [DD] §6.2).
  * For every new token t of the batch (query row g = its global row) and every
  * visible entry s < V_t:

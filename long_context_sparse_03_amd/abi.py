@@ -71,6 +71,8 @@ def lib():
             "csa_topk_select": (I, [P, I, I, P, I, P, I, P, P, Z]),
             "csa_sparse_mqa": (I, [P, LP, BP, I, P, P, P, P, P, P, P, P, Z]),
             "csa_hca_attention": (I, [P, LP, BP, I, P, P, P, P, P, P, P, Z]),
+            "csa_linear": (I, [P, I, I, I, I, I, P, P, P]),
+            "csa_grouped_linear": (I, [P, I, I, I, I, I, I, P, P, P]),
             "csa_prefix_bytes": (I, [LP, I, ctypes.POINTER(ctypes.c_size_t)]),
             "csa_prefix_blocks": (I, [P, LP, I, P, P, P, P, I]),
             "csa_prefix_state": (I, [P, LP, P, P, I]),
@@ -177,3 +179,19 @@ def prefix_state(desc, state_slot_ptr: int, host, direction, stream=None):
     """One state slot (device address) to or from the pinned host tensor `host`."""
     _check("csa_prefix_state", lib().csa_prefix_state(
         _stream(stream), ctypes.byref(desc), state_slot_ptr, _ptr(host), direction))
+
+
+def grouped_linear(act_fmt, out_fmt, groups, X, W, Y, stream=None):
+    """Y[:, g*N:(g+1)*N] = X[:, g*K:(g+1)*K] . W[g]^T for every group g
+    (X [rows x groups*K], W [groups x N x K], Y [rows x groups*N])."""
+    K = X.shape[-1] // groups
+    N = W.shape[-2]
+    _check("csa_grouped_linear", lib().csa_grouped_linear(
+        _stream(stream), act_fmt, out_fmt, X.shape[0], groups, K, N, _ptr(X), _ptr(W), _ptr(Y)))
+
+
+def linear(act_fmt, out_fmt, X, W, Y, stream=None):
+    """Y = X . W^T (X [rows x K], W [N x K], Y [rows x N])."""
+    _check("csa_linear", lib().csa_linear(
+        _stream(stream), act_fmt, out_fmt, X.shape[0], X.shape[1], W.shape[0], _ptr(X), _ptr(W), _ptr(Y)))
+

@@ -420,6 +420,30 @@ int csa_hca_attention(void* stream, const csa_layer_desc* layer, const csa_batch
                             ws_bytes);
 }
 
+// ---- dense projections around the path ------------------------------------
+
+int csa_grouped_linear(void* stream, int act_fmt, int out_fmt, int n_rows, int groups, int K, int N, const void* X,
+                       const void* W, void* Y)
+{
+    REQUIRE(act_fmt == CSA_FMT_F32 || act_fmt == CSA_FMT_BF16, CSA_EINVAL, "act_fmt=%d", act_fmt);
+    REQUIRE(out_fmt == CSA_FMT_F32 || out_fmt == CSA_FMT_BF16, CSA_EINVAL, "out_fmt=%d", out_fmt);
+    REQUIRE(n_rows >= 0 && groups >= 1 && N >= 1, CSA_EINVAL, "n_rows=%d groups=%d N=%d", n_rows, groups, N);
+    REQUIRE(K >= 128 && K % 128 == 0, CSA_EUNSUPPORTED, "K=%d must be a positive multiple of 128", K);
+    REQUIRE(n_rows <= 65535 * 16 && groups <= 65535, CSA_EUNSUPPORTED, "n_rows=%d groups=%d", n_rows, groups);
+    if (n_rows == 0) return CSA_OK;
+    REQUIRE(X != nullptr && W != nullptr && Y != nullptr, CSA_EINVAL, "X / W / Y is NULL");
+    REQUIRE((((uintptr_t)X | (uintptr_t)W | (uintptr_t)Y) & 15) == 0, CSA_EINVAL, "pointers must be 16-byte aligned");
+    return hip_status(csa::launch_linear((hipStream_t)stream, act_fmt == CSA_FMT_BF16, n_rows, K, N, groups, X, W, Y,
+                                         out_fmt == CSA_FMT_BF16),
+                      "linear launch");
+}
+
+int csa_linear(void* stream, int act_fmt, int out_fmt, int n_rows, int K, int N, const void* X, const void* W,
+               void* Y)
+{
+    return csa_grouped_linear(stream, act_fmt, out_fmt, n_rows, 1, K, N, X, W, Y);
+}
+
 // ---- prefix reuse (host-memory tier) --------------------------------------
 
 // Device address of a host buffer the device may read and write (pinned host

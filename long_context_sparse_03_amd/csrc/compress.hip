@@ -20,15 +20,33 @@ namespace csa {
 
 // ---------------------------------------------------------------------------
 // projection: P[M x N] = X[M x K] . Wt[N x K]^T, Wt rows n < n_main from W,
-// the rest from Wi.  T is float or uint16_t (bf16).
+// the rest from Wi.  T is float or uint16_t (bf16).  Rows of X are ldx
+// elements apart and rows of P ldp apart; P is fp32 or (out_bf16) bf16;
+// grid z selects a group: X, W / Wi and P advance by gx, gw and gp elements
+// per group (the compressor: one group, ldx = K, ldp = N, fp32).
 // ---------------------------------------------------------------------------
+
+struct GemmShape {
+    int ldx, ldp, out_bf16;
+    size_t gx, gw, gp;
+};
+
+CSA_DEV void store_out(void* P, size_t i, int out_bf16, float v)
+{
+    if (out_bf16) ((uint16_t*)P)[i] = f32_to_bf16(v);
+    else ((float*)P)[i] = v;
+}
 
 template <class T, class MMA>
 __global__ __launch_bounds__(256) void proj_large(const T* __restrict__ X, const T* __restrict__ W,
                                                   const T* __restrict__ Wi, int n_main, int N, int M, int K,
-                                                  float* __restrict__ P)
+                                                  void* __restrict__ P, GemmShape sh)
 {
     constexpr int EPF = 16 / sizeof(T);
+    X += blockIdx.z * sh.gx;
+    W += blockIdx.z * sh.gw;
+    Wi += blockIdx.z * sh.gw;
+    const size_t p0 = blockIdx.z * sh.gp;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
     const int m0 = blockIdx.y * 128 + (wave >> 1) * 64;
     const int n0 = blockIdx.x * 128 + (wave & 1) * 64;
@@ -39,7 +57,7 @@ __global__ __launch_bounds__(256) void proj_large(const T* __restrict__ X, const
     for (int t = 0; t < 4; ++t) {
         int m = m0 + 16 * t + li;
         av[t] = m < M;
-        ap[t] = X + (size_t)(av[t] ? m : 0) * K + g * EPF;
+        ap[t] = X + (size_t)(av[t] ? m : 0) * sh.ldx + g * EPF;
         int n = n0 + 16 * t + li;
         bv[t] = n < N;
         int nn = bv[t] ? n : 0;
@@ -71,7 +89,7 @@ __global__ __launch_bounds__(256) void proj_large(const T* __restrict__ X, const
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 int m = m0 + 16 * i + 4 * g + q;
-                if (m < M) P[(size_t)m * N + n] = acc[i][j][q];
+                if (m < M) store_out(P, p0 + (size_t)m * sh.ldp + n, sh.out_bf16, acc[i][j][q]);
             }
         }
 }
@@ -83,15 +101,19 @@ __global__ __launch_bounds__(256) void proj_large(const T* __restrict__ X, const
 template <class T, class MMA, int NW>
 __global__ __launch_bounds__(64 * NW) void proj_small(const T* __restrict__ X, const T* __restrict__ W,
                                                       const T* __restrict__ Wi, int n_main, int N, int M, int K,
-                                                      float* __restrict__ P)
+                                                      void* __restrict__ P, GemmShape sh)
 {
     constexpr int EPF = 16 / sizeof(T);
     __shared__ float red[NW][64][4];
+    X += blockIdx.z * sh.gx;
+    W += blockIdx.z * sh.gw;
+    Wi += blockIdx.z * sh.gw;
+    const size_t p0 = blockIdx.z * sh.gp;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
     const int m = blockIdx.y * 16 + li, n = blockIdx.x * 16 + li;
     const bool av = m < M, bv = n < N;
     const int kq = K / NW, kb = wave * kq;
-    const T* ap = X + (size_t)(av ? m : 0) * K + kb + g * EPF;
+    const T* ap = X + (size_t)(av ? m : 0) * sh.ldx + kb + g * EPF;
     int nn = bv ? n : 0;
     const T* bp = (nn < n_main ? W + (size_t)nn * K : Wi + (size_t)(nn - n_main) * K) + kb + g * EPF;
     f32x4_t acc[4] = {zero4(), zero4(), zero4(), zero4()};
@@ -121,7 +143,7 @@ __global__ __launch_bounds__(64 * NW) void proj_small(const T* __restrict__ X, c
 #pragma unroll
             for (int w = 1; w < NW; ++w) v += red[w][lane][q];
             int row = blockIdx.y * 16 + 4 * g + q;
-            if (row < M && col < N) P[(size_t)row * N + col] = v;
+            if (row < M && col < N) store_out(P, p0 + (size_t)row * sh.ldp + col, sh.out_bf16, v);
         }
     }
 }
@@ -370,6 +392,7 @@ hipError_t launch_compress(hipStream_t st, const CompressArgs& a, const void* H,
                            int n_main, int d, bool bf16, int n_tokens)
 {
     const int N = a.ncols, M = n_tokens;
+    const GemmShape sh{d, N, 0, 0, 0, 0};
     if (M > 0) {
         // batch-invariant layers: one kernel whatever the row count (its sums
         // for a row do not depend on the other rows)
@@ -377,21 +400,21 @@ hipError_t launch_compress(hipStream_t st, const CompressArgs& a, const void* H,
             dim3 grid((N + 15) / 16, (M + 15) / 16);
             if (bf16 && d % (16 * MmaBF16::K) == 0)              // 16 waves of whole steps
                 proj_small<uint16_t, MmaBF16, 16><<<grid, 1024, 0, st>>>((const uint16_t*)H, (const uint16_t*)W,
-                                                                         (const uint16_t*)Wi, n_main, N, M, d, a.P);
+                                                                         (const uint16_t*)Wi, n_main, N, M, d, a.P, sh);
             else if (bf16)
                 proj_small<uint16_t, MmaBF16, 4><<<grid, 256, 0, st>>>((const uint16_t*)H, (const uint16_t*)W,
-                                                                       (const uint16_t*)Wi, n_main, N, M, d, a.P);
+                                                                       (const uint16_t*)Wi, n_main, N, M, d, a.P, sh);
             else
                 proj_small<float, MmaF32, 4><<<grid, 256, 0, st>>>((const float*)H, (const float*)W, (const float*)Wi,
-                                                                   n_main, N, M, d, a.P);
+                                                                   n_main, N, M, d, a.P, sh);
         } else {
             dim3 grid((N + 127) / 128, (M + 127) / 128);
             if (bf16)
                 proj_large<uint16_t, MmaBF16><<<grid, 256, 0, st>>>((const uint16_t*)H, (const uint16_t*)W,
-                                                                    (const uint16_t*)Wi, n_main, N, M, d, a.P);
+                                                                    (const uint16_t*)Wi, n_main, N, M, d, a.P, sh);
             else
                 proj_large<float, MmaF32><<<grid, 256, 0, st>>>((const float*)H, (const float*)W, (const float*)Wi,
-                                                                n_main, N, M, d, a.P);
+                                                                n_main, N, M, d, a.P, sh);
         }
     }
     const int nm = a.max_entries > 0 ? a.max_entries : 1;
@@ -405,6 +428,41 @@ hipError_t launch_compress(hipStream_t st, const CompressArgs& a, const void* H,
             window_rows_kernel<<<M, 256, 0, st>>>(a);
             tail_update_kernel<<<dim3(a.R, a.n_req), 256, 0, st>>>(a);
         }
+    }
+    return hipGetLastError();
+}
+
+}  // namespace csa
+
+namespace csa {
+
+// Y[M x N] = X[M x K] . W^T per group (grid z), W [groups x N x K].  Few rows:
+// the small-row kernel (16 waves when K allows), else the 128 x 128 tiles.
+hipError_t launch_linear(hipStream_t st, bool bf16, int M, int K, int N, int groups, const void* X, const void* W,
+                         void* Y, bool out_bf16)
+{
+    if (M <= 0 || N <= 0 || groups <= 0) return hipSuccess;
+    const GemmShape sh{K * groups, N * groups, out_bf16 ? 1 : 0, (size_t)K, (size_t)N * K, (size_t)N};
+    if (M <= 64) {
+        dim3 grid((N + 15) / 16, (M + 15) / 16, groups);
+        // sixteen waves per column tile only when each gets a long slice of K
+        if (bf16 && K % (16 * MmaBF16::K) == 0 && K >= 4096)
+            proj_small<uint16_t, MmaBF16, 16><<<grid, 1024, 0, st>>>((const uint16_t*)X, (const uint16_t*)W,
+                                                                     (const uint16_t*)W, N, N, M, K, Y, sh);
+        else if (bf16)
+            proj_small<uint16_t, MmaBF16, 4><<<grid, 256, 0, st>>>((const uint16_t*)X, (const uint16_t*)W,
+                                                                   (const uint16_t*)W, N, N, M, K, Y, sh);
+        else
+            proj_small<float, MmaF32, 4><<<grid, 256, 0, st>>>((const float*)X, (const float*)W, (const float*)W, N,
+                                                               N, M, K, Y, sh);
+    } else {
+        dim3 grid((N + 127) / 128, (M + 127) / 128, groups);
+        if (bf16)
+            proj_large<uint16_t, MmaBF16><<<grid, 256, 0, st>>>((const uint16_t*)X, (const uint16_t*)W,
+                                                                (const uint16_t*)W, N, N, M, K, Y, sh);
+        else
+            proj_large<float, MmaF32><<<grid, 256, 0, st>>>((const float*)X, (const float*)W, (const float*)W, N, N,
+                                                            M, K, Y, sh);
     }
     return hipGetLastError();
 }

@@ -31,6 +31,11 @@ struct CompressArgs {
     int invariant;             // batch-invariant layer: the projection kernel does not depend on the row count
 };
 
+// Y[M x groups*N] = per group g: X[:, g*K .. g*K+K) . W[g]^T, W [groups x N x K];
+// X, W bf16 (bf16) or fp32, Y fp32 or (out_bf16) bf16.
+hipError_t launch_linear(hipStream_t st, bool bf16, int M, int K, int N, int groups, const void* X, const void* W,
+                         void* Y, bool out_bf16);
+
 hipError_t launch_compress(hipStream_t st, const CompressArgs& a, const void* H, const void* W, const void* Wi,
                            int n_main, int d, bool bf16, int n_tokens);
 

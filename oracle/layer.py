@@ -78,6 +78,33 @@ def project(H, W):
     return np.asarray(H, np.float64) @ np.asarray(W, np.float64)
 
 
+def query_path(H, W_DQ, W_UQ, W_UQI, W_w, round_mid: bool = True):
+    """[DD] §1.2 Step 2 query side; [AD] d_c = 1024: c^Q = H W_DQ^T (stored in
+    bf16 unless round_mid is False), q = c^Q W_UQ^T, q^I = c^Q W_UQI^T, and
+    the indexer head weights w = H W_w^T (reading: a projection of the
+    token's hidden state).  Weights one row per output."""
+    H = np.asarray(H, np.float64)
+    cq = H @ np.asarray(W_DQ, np.float64).T
+    if round_mid:
+        cq = O.bf16_round(cq).astype(np.float64)
+    return (cq @ np.asarray(W_UQ, np.float64).T, cq @ np.asarray(W_UQI, np.float64).T,
+            H @ np.asarray(W_w, np.float64).T)
+
+
+def grouped_output(Oh, W_G, W_O, round_mid: bool = True):
+    """[DD] §1.2 Step 3: the head outputs (concatenated in head order, width
+    n_h*c) split into g equal groups; group j is projected by W_G[j]
+    (d_g x n_h*c/g) to d_g; the g results, concatenated in group order (bf16
+    unless round_mid is False), are projected by W_O (d x g*d_g) to d."""
+    Oh = np.asarray(Oh, np.float64)
+    g = W_G.shape[0]
+    K = Oh.shape[1] // g
+    z = np.concatenate([Oh[:, j * K:(j + 1) * K] @ np.asarray(W_G[j], np.float64).T for j in range(g)], axis=1)
+    if round_mid:
+        z = O.bf16_round(z).astype(np.float64)
+    return z @ np.asarray(W_O, np.float64).T
+
+
 def compress_layer(spec: Spec, H, W, Ba, Bb=None, gamma=None, W_I=None, BaI=None, BbI=None, pos0: int = 0):
     """Entries, indexer keys and window rows of one request's tokens 0..n-1
     (the sequence may start at position pos0, a multiple of m: entry i is then

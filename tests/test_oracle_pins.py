@@ -487,3 +487,41 @@ def test_fp8_block_scale_raise_requantises_earlier_slots():
     b1, _ = L.store_entries(spec, y[:4], [(0, 4)])
     b2, _ = L.store_entries(spec, y, [(0, 4), (4, 4)])
     assert np.array_equal(b1[0, :64 + 4 * 80], b2[0, :64 + 4 * 80])
+
+
+# ---------------------------------------------------------------------------
+# dense projections around the path
+# ---------------------------------------------------------------------------
+
+def test_grouped_output_is_a_block_diagonal_product():
+    """The grouped output projection equals one product with the explicit
+    block-diagonal matrix of the group projections, then W_O (a different
+    formulation: a group index or order mistake, or a transposed block,
+    breaks it)."""
+    from scipy.linalg import block_diag
+    g = np.random.default_rng(5)
+    T, n_groups, K, dg, d = 3, 4, 6, 5, 7
+    Oh = g.standard_normal((T, n_groups * K))
+    W_G = g.standard_normal((n_groups, dg, K))
+    W_O = g.standard_normal((d, n_groups * dg))
+    want = Oh @ block_diag(*[W_G[j].T for j in range(n_groups)]) @ W_O.T
+    got = L.grouped_output(Oh, W_G, W_O, round_mid=False)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_query_path_is_the_low_rank_product():
+    """q = (h W_DQ^T) W_UQ^T equals h (W_UQ W_DQ)^T (the low-rank factors
+    multiplied first); with c^Q stored in bf16 the difference stays within
+    the rounding bound 2^-8 |h W_DQ^T| |W_UQ|^T."""
+    g = np.random.default_rng(6)
+    T, d, dc, nq, ni, nh = 4, 24, 8, 10, 6, 3
+    H = g.standard_normal((T, d))
+    W_DQ, W_UQ, W_UQI, W_w = (g.standard_normal(s) for s in [(dc, d), (nq, dc), (ni, dc), (nh, d)])
+    q, qI, w = L.query_path(H, W_DQ, W_UQ, W_UQI, W_w, round_mid=False)
+    assert np.allclose(q, H @ (W_UQ @ W_DQ).T, rtol=1e-12, atol=1e-12)
+    assert np.allclose(qI, H @ (W_UQI @ W_DQ).T, rtol=1e-12, atol=1e-12)
+    assert np.allclose(w, np.einsum("td,hd->th", H, W_w), rtol=1e-12, atol=1e-12)
+    qr, _, _ = L.query_path(H, W_DQ, W_UQ, W_UQI, W_w, round_mid=True)
+    bound = 2.0 ** -8 * np.abs(H @ W_DQ.T) @ np.abs(W_UQ).T
+    assert np.all(np.abs(qr - q) <= bound + 1e-15)
+    assert np.any(qr != q)                       # the rounding is applied
