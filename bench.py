@@ -137,7 +137,7 @@ def profiled_traffic(kernel: str, workload: str):
     return int(float(vals["traffic_bytes_per_launch"]))
 
 
-def time_decode(name, steps, warmup, replicas=0, graph=True):
+def time_decode(name, steps, warmup, replicas=0, graph=True, fused_append=True):
     """Decode throughput of one workload; returns a dict of measurements."""
     import torch
     from long_context_sparse_03_amd import abi
@@ -148,7 +148,7 @@ def time_decode(name, steps, warmup, replicas=0, graph=True):
     total_steps = warmup + steps + 64
     t_build = time.time()
     wls = [DecodeWorkload(wd["descs"], wd["d"], wd["n_req"], wd["ctx"], max_steps=total_steps,
-                          rows=torch_rows(1000 + i), seed=i) for i in range(reps)]
+                          rows=torch_rows(1000 + i), seed=i, fused_append=fused_append) for i in range(reps)]
     torch.cuda.synchronize()
     build_s = time.time() - t_build
 
@@ -402,6 +402,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the 1M decode and 1M prefill sub-results")
     ap.add_argument("--cpu-tokens", type=int, default=640, help="decode tokens in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="decode steps call compress_kv and cache_append instead of compress_append")
     ap.add_argument("--copy-probe", action="store_true", help="also run a 1 GiB device copy (HBM counter scale)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -417,18 +419,19 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    prim = time_decode(args.workload, args.steps, args.warmup, args.replicas, not args.no_graph)
+    fused = not args.separate_append
+    prim = time_decode(args.workload, args.steps, args.warmup, args.replicas, not args.no_graph, fused)
     extras = {}
     if not args.no_extras:
         other = "hybrid_decode_1m" if args.workload == "csa_decode_128k" else "csa_decode_128k"
-        extras[other] = time_decode(other, max(20, args.steps // 2), args.warmup, 0, not args.no_graph)
+        extras[other] = time_decode(other, max(20, args.steps // 2), args.warmup, 0, not args.no_graph, fused)
         extras["csa_prefill_1m"] = time_prefill(max(2, min(5, args.steps // 40)), 1)
         extras["csa_prefix_1m_host"] = time_prefix()
         extras["pro_projections_decode"] = time_projections()
         # warm: one cache replica, whose step working set stays in the 256 MB
         # last-level cache between steps (the primary number rotates
         # replicas so that it does not)
-        w = time_decode(args.workload, max(20, args.steps // 2), args.warmup, 1, not args.no_graph)
+        w = time_decode(args.workload, max(20, args.steps // 2), args.warmup, 1, not args.no_graph, fused)
         extras[args.workload + "_warm"] = {
             "workload": args.workload, "replicas": 1, "tokens_per_s": w["tokens_per_s"],
             "ms_per_step": w["ms_per_step"], "index_launch_ms": w["roofline"]["launch_ms"],
@@ -442,7 +445,8 @@ def main():
         "ms_per_step": prim["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16/fp8 storage, fp32 accumulate", "data": "synthetic",
         "config": {"workload": args.workload, "requests": prim["requests"], "ctx": prim["ctx"],
-                   "layers": prim["layers"], "d": prim["d"], "replicas": prim["replicas"], "graph": prim["graph"]},
+                   "layers": prim["layers"], "d": prim["d"], "replicas": prim["replicas"], "graph": prim["graph"],
+                   "compress_append": fused},
         "step_hbm_gbs": prim["step_hbm_gbs"], "step_hbm_frac": prim["step_hbm_frac"],
         "step_algorithmic_bytes": prim["step_algorithmic_bytes"],
         "roofline": prim["roofline"],

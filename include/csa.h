@@ -216,6 +216,25 @@ int csa_cache_append(void* stream, const csa_layer_desc* layer, const csa_batch*
                      void* kv_cache, void* idx_cache, void* state);
 
 /*
+ * a1 then a2 in one call ([DD] §7: the new tokens' compressed entries and
+ * window rows go to the caches as they are produced).  Same arguments,
+ * outputs and errors as csa_compress_kv, plus the caches of
+ * csa_cache_append (batch->block_table required, max_new <= win_cap); the
+ * caches and state end as after csa_compress_kv followed by
+ * csa_cache_append on its outputs, byte for byte.  With batch->max_new <= 1
+ * (decode: at most one entry per request and call) the merge and window
+ * workgroups store what they produce themselves, in one kernel; otherwise the
+ * two calls' kernels run in order.
+ */
+int csa_compress_append(void* stream, const csa_layer_desc* layer, const csa_batch* batch,
+                        int n_tokens, int d, const void* H, const void* W, const void* W_idx,
+                        const float* B_a, const float* B_b, const float* B_a_idx, const float* B_b_idx,
+                        const float* gamma, void* state,
+                        float* out_entries, float* out_keys, int32_t* out_meta, int32_t* out_count,
+                        int max_entries, float* out_win, void* kv_cache, void* idx_cache,
+                        void* ws, size_t ws_bytes);
+
+/*
  * Prefix reuse, host-memory tier ([DD] §7: the compressed entries of a shared
  * prefix are stored whole; the sliding window by one of three strategies, one
  * of them a checkpoint every p tokens).  Copies between a layer's caches and

@@ -10,8 +10,8 @@ from __future__ import annotations
 
 from .abi import (  # noqa: F401
     ACT_BF16, ACT_F32, CSAError, IDX_BF16, IDX_F32, IDX_MXFP4, KIND_CSA, KIND_HCA, KV_BF16, KV_F32, KV_FP8,
-    OP_ATTENTION, OP_COMPRESS, OP_TOPK, Batch, LayerDesc, Sizes, abi_version, cache_append, compress_kv,
-    grouped_linear, hca_attention, index_scores, layer_sizes, lib, linear, prefix_blocks, prefix_bytes, prefix_state,
+    OP_ATTENTION, OP_COMPRESS, OP_TOPK, Batch, LayerDesc, Sizes, abi_version, cache_append, compress_append,
+    compress_kv, grouped_linear, hca_attention, index_scores, layer_sizes, lib, linear, prefix_blocks, prefix_bytes, prefix_state,
     sparse_mqa, topk_select, workspace_size,
 )
 from .layer import LayerState, make_batch  # noqa: F401

@@ -67,6 +67,7 @@ def lib():
             "csa_workspace_size": (I, [LP, I, I, I, I, ctypes.POINTER(ctypes.c_size_t)]),
             "csa_compress_kv": (I, [P, LP, BP, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, I, P, P, Z]),
             "csa_cache_append": (I, [P, LP, BP, I, P, P, P, P, I, P, P, P, P]),
+            "csa_compress_append": (I, [P, LP, BP, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, I, P, P, P, P, Z]),
             "csa_index_scores": (I, [P, LP, BP, I, P, P, P, P, I, P]),
             "csa_topk_select": (I, [P, I, I, P, I, P, I, P, P, Z]),
             "csa_sparse_mqa": (I, [P, LP, BP, I, P, P, P, P, P, P, P, P, Z]),
@@ -133,6 +134,17 @@ def cache_append(desc, batch, n_tokens, entries, keys, meta, count, max_entries,
     _check("csa_cache_append", lib().csa_cache_append(
         _stream(stream), ctypes.byref(desc), ctypes.byref(batch), n_tokens, _ptr(entries), _ptr(keys), _ptr(meta),
         _ptr(count), max_entries, _ptr(win), _ptr(kv_cache), _ptr(idx_cache), _ptr(state)))
+
+
+def compress_append(desc, batch, n_tokens, d, H, W, W_idx, B_a, B_b, B_a_idx, B_b_idx, gamma, state,
+                    out_entries, out_keys, out_meta, out_count, max_entries, out_win, kv_cache, idx_cache, ws,
+                    stream=None):
+    """compress_kv and then cache_append of its outputs, in one call."""
+    _check("csa_compress_append", lib().csa_compress_append(
+        _stream(stream), ctypes.byref(desc), ctypes.byref(batch), n_tokens, d, _ptr(H), _ptr(W), _ptr(W_idx),
+        _ptr(B_a), _ptr(B_b), _ptr(B_a_idx), _ptr(B_b_idx), _ptr(gamma), _ptr(state), _ptr(out_entries),
+        _ptr(out_keys), _ptr(out_meta), _ptr(out_count), max_entries, _ptr(out_win), _ptr(kv_cache),
+        _ptr(idx_cache), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size()))
 
 
 def index_scores(desc, batch, n_tokens, q_idx, w, idx_cache, scores, ld, n_valid, stream=None):

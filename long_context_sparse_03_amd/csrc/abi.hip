@@ -183,11 +183,16 @@ int csa_workspace_size(const csa_layer_desc* layer, int op, int n_rows, int max_
     }
 }
 
-int csa_compress_kv(void* stream, const csa_layer_desc* layer, const csa_batch* batch, int n_tokens, int d,
-                    const void* H, const void* W, const void* W_idx, const float* B_a, const float* B_b,
-                    const float* B_a_idx, const float* B_b_idx, const float* gamma, void* state,
-                    float* out_entries, float* out_keys, int32_t* out_meta, int32_t* out_count, int max_entries,
-                    float* out_win, void* ws, size_t ws_bytes)
+}  // extern "C"
+
+namespace {
+
+// Validates compress_kv's arguments and fills its kernel arguments.
+int compress_args(const csa_layer_desc* layer, const csa_batch* batch, int n_tokens, int d, const void* H,
+                  const void* W, const void* W_idx, const float* B_a, const float* B_b, const float* B_a_idx,
+                  const float* B_b_idx, const float* gamma, void* state, float* out_entries, float* out_keys,
+                  int32_t* out_meta, int32_t* out_count, int max_entries, float* out_win, void* ws, size_t ws_bytes,
+                  csa::CompressArgs* out)
 {
     CHECK(check_layer(layer));
     CHECK(check_batch(layer, batch, false, 0));
@@ -208,7 +213,7 @@ int csa_compress_kv(void* stream, const csa_layer_desc* layer, const csa_batch* 
     const size_t need = (size_t)n_tokens * proj_cols(layer) * 4;
     REQUIRE(ws_bytes >= need && (need == 0 || ws != nullptr), CSA_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes,
             need);
-    csa::CompressArgs a;
+    csa::CompressArgs& a = *out;
     memset(&a, 0, sizeof(a));
     a.invariant = invariant(layer);
     a.P = (float*)ws;
@@ -239,15 +244,13 @@ int csa_compress_kv(void* stream, const csa_layer_desc* layer, const csa_batch* 
     a.max_entries = max_entries;
     a.out_win = out_win;
     a.max_new = batch->max_new;
-    const int n_main = csa ? 4 * layer->c : 2 * layer->c;
-    return hip_status(csa::launch_compress((hipStream_t)stream, a, H, W, csa ? W_idx : W, n_main, d,
-                                           layer->act_fmt == CSA_FMT_BF16, n_tokens),
-                      "compress_kv launch");
+    return CSA_OK;
 }
 
-int csa_cache_append(void* stream, const csa_layer_desc* layer, const csa_batch* batch, int n_tokens,
-                     const float* entries, const float* keys, const int32_t* meta, const int32_t* count,
-                     int max_entries, const float* win, void* kv_cache, void* idx_cache, void* state)
+// Validates cache_append's arguments and fills its kernel arguments.
+int append_args(const csa_layer_desc* layer, const csa_batch* batch, int n_tokens, const float* entries,
+                const float* keys, const int32_t* meta, const int32_t* count, int max_entries, const float* win,
+                void* kv_cache, void* idx_cache, void* state, csa::AppendArgs* out)
 {
     CHECK(check_layer(layer));
     CHECK(check_batch(layer, batch, true, 1));
@@ -258,7 +261,7 @@ int csa_cache_append(void* stream, const csa_layer_desc* layer, const csa_batch*
     REQUIRE(!csa || max_entries == 0 || (keys != nullptr && idx_cache != nullptr), CSA_EINVAL,
             "keys / idx_cache is NULL");
     REQUIRE(n_tokens == 0 || (win != nullptr && state != nullptr), CSA_EINVAL, "win / state is NULL");
-    csa::AppendArgs a;
+    csa::AppendArgs& a = *out;
     memset(&a, 0, sizeof(a));
     a.entries = entries;
     a.keys = keys;
@@ -287,7 +290,59 @@ int csa_cache_append(void* stream, const csa_layer_desc* layer, const csa_batch*
     a.state = state;
     a.state_stride = state_bytes(layer);
     a.win_cap = layer->win_cap;
+    return CSA_OK;
+}
+
+hipError_t compress_launch(hipStream_t st, const csa_layer_desc* layer, const csa::CompressArgs& a, const void* H,
+                           const void* W, const void* W_idx, int d, int n_tokens, const csa::AppendArgs* app)
+{
+    const bool csa = is_csa(layer);
+    const int n_main = csa ? 4 * layer->c : 2 * layer->c;
+    return csa::launch_compress(st, a, H, W, csa ? W_idx : W, n_main, d, layer->act_fmt == CSA_FMT_BF16, n_tokens,
+                                app);
+}
+
+}  // namespace
+
+extern "C" {
+
+int csa_compress_kv(void* stream, const csa_layer_desc* layer, const csa_batch* batch, int n_tokens, int d,
+                    const void* H, const void* W, const void* W_idx, const float* B_a, const float* B_b,
+                    const float* B_a_idx, const float* B_b_idx, const float* gamma, void* state,
+                    float* out_entries, float* out_keys, int32_t* out_meta, int32_t* out_count, int max_entries,
+                    float* out_win, void* ws, size_t ws_bytes)
+{
+    csa::CompressArgs a;
+    CHECK(compress_args(layer, batch, n_tokens, d, H, W, W_idx, B_a, B_b, B_a_idx, B_b_idx, gamma, state, out_entries,
+                        out_keys, out_meta, out_count, max_entries, out_win, ws, ws_bytes, &a));
+    return hip_status(compress_launch((hipStream_t)stream, layer, a, H, W, W_idx, d, n_tokens, nullptr),
+                      "compress_kv launch");
+}
+
+int csa_cache_append(void* stream, const csa_layer_desc* layer, const csa_batch* batch, int n_tokens,
+                     const float* entries, const float* keys, const int32_t* meta, const int32_t* count,
+                     int max_entries, const float* win, void* kv_cache, void* idx_cache, void* state)
+{
+    csa::AppendArgs a;
+    CHECK(append_args(layer, batch, n_tokens, entries, keys, meta, count, max_entries, win, kv_cache, idx_cache,
+                      state, &a));
     return hip_status(csa::launch_append((hipStream_t)stream, a), "cache_append launch");
+}
+
+int csa_compress_append(void* stream, const csa_layer_desc* layer, const csa_batch* batch, int n_tokens, int d,
+                        const void* H, const void* W, const void* W_idx, const float* B_a, const float* B_b,
+                        const float* B_a_idx, const float* B_b_idx, const float* gamma, void* state,
+                        float* out_entries, float* out_keys, int32_t* out_meta, int32_t* out_count, int max_entries,
+                        float* out_win, void* kv_cache, void* idx_cache, void* ws, size_t ws_bytes)
+{
+    csa::CompressArgs a;
+    csa::AppendArgs b;
+    CHECK(compress_args(layer, batch, n_tokens, d, H, W, W_idx, B_a, B_b, B_a_idx, B_b_idx, gamma, state, out_entries,
+                        out_keys, out_meta, out_count, max_entries, out_win, ws, ws_bytes, &a));
+    CHECK(append_args(layer, batch, n_tokens, out_entries, out_keys, out_meta, out_count, max_entries, out_win,
+                      kv_cache, idx_cache, state, &b));
+    return hip_status(compress_launch((hipStream_t)stream, layer, a, H, W, W_idx, d, n_tokens, &b),
+                      "compress_append launch");
 }
 
 int csa_index_scores(void* stream, const csa_layer_desc* layer, const csa_batch* batch, int n_tokens,

@@ -15,6 +15,7 @@
 //               (after merge has read the old ring contents).
 #include "common.hpp"
 #include "kernels.hpp"
+#include "append.hpp"
 
 namespace csa {
 
@@ -219,7 +220,10 @@ CSA_DEV void norm_rope_store(float* xs, float* red, int c, int r, const float* g
 // merge: one workgroup per entry completed in this call
 // ---------------------------------------------------------------------------
 
-CSA_DEV void merge_entry(const CompressArgs& a, int e, float* xs, float* red)
+// (request, entry index) of the call's entry e, or request -1 when the call
+// completes no more than e entries or e >= max_entries.  Entry 0's
+// workgroup also writes the call's entry count.
+CSA_DEV int2 locate_entry(const CompressArgs& a, int e)
 {
     // locate the entry: requests in order, entries of a request in index
     // order.  The threads take one request each (256 at a time): the entries
@@ -257,8 +261,14 @@ CSA_DEV void merge_entry(const CompressArgs& a, int e, float* xs, float* red)
     }
     const int req = loc[0], ent = loc[1];
     if (e == 0 && threadIdx.x == 0) *a.out_count = total;
-    if (req < 0 || e >= a.max_entries) return;
+    if (req < 0 || e >= a.max_entries) return make_int2(-1, 0);
+    return make_int2(req, ent);
+}
 
+// Entry e = entry `ent` of request `req`: out_entries row e (and xs, in LDS),
+// out_keys row e (and ks when given), out_meta row e.
+CSA_DEV void merge_located(const CompressArgs& a, int e, int req, int ent, float* xs, float* red, float* ks)
+{
     const int s0 = a.start_pos[req], cu = a.cu_new[req];
     const float* tail = (const float*)((const char*)a.state + (size_t)req * a.state_stride + a.tail_off);
     const int m = a.m, c = a.c, cI = a.c_idx;
@@ -313,8 +323,12 @@ CSA_DEV void merge_entry(const CompressArgs& a, int e, float* xs, float* red)
             mx = nm;
         }
         float v = acc / den;
-        if (ix) a.out_keys[(size_t)e * cI + cc] = v;
-        else xs[cc] = v;
+        if (ix) {
+            a.out_keys[(size_t)e * cI + cc] = v;
+            if (ks != nullptr) ks[cc] = v;
+        } else {
+            xs[cc] = v;
+        }
     }
     __syncthreads();
     norm_rope_store(xs, red, c, a.r, a.gamma, a.eps, (double)m * (double)ent, a.theta, a.out_entries + (size_t)e * c);
@@ -322,6 +336,12 @@ CSA_DEV void merge_entry(const CompressArgs& a, int e, float* xs, float* red)
         a.out_meta[2 * e] = req;
         a.out_meta[2 * e + 1] = ent;
     }
+}
+
+CSA_DEV void merge_entry(const CompressArgs& a, int e, float* xs, float* red)
+{
+    const int2 re = locate_entry(a, e);
+    if (re.x >= 0) merge_located(a, e, re.x, re.y, xs, red, nullptr);
 }
 
 __global__ __launch_bounds__(256) void merge_kernel(CompressArgs a)
@@ -384,12 +404,50 @@ __global__ __launch_bounds__(256) void post_decode_kernel(CompressArgs a, int nm
     norm_rope_store(xs, red, a.c, a.r, a.gamma, a.eps, (double)pos, a.theta, a.out_win + (size_t)gtok * a.c);
 }
 
+// post_decode_kernel, then what a cache append of its outputs stores, in the
+// same workgroups.  With at most one new token per request a request
+// completes at most one entry per call, so each (request, block) receives one
+// new record and its merge workgroup applies the block-scale rule alone.  The
+// stores take the values this workgroup has just written (held in LDS), so
+// they are those the separate append would read back.
+__global__ __launch_bounds__(256) void post_decode_append_kernel(CompressArgs a, AppendArgs b, int nm)
+{
+    __shared__ __attribute__((aligned(16))) float xs[512];
+    __shared__ __attribute__((aligned(16))) float ks[128];
+    __shared__ float red[16];
+    __shared__ float s_sh[2];
+    if ((int)blockIdx.x < nm) {
+        const int2 re = locate_entry(a, blockIdx.x);
+        if (re.x < 0) return;
+        // the block's address and FP8 scale are loaded before the merge,
+        // which does not need them (no other workgroup of this call writes
+        // this block: it receives this one record)
+        const int blk = re.y / b.epb, slot = re.y % b.epb;
+        const int phys = b.block_table[(size_t)re.x * b.max_blocks + blk];
+        uint8_t* block = (uint8_t*)b.kv + (size_t)phys * b.kv_block_bytes;
+        const float s_old = (b.kv_fmt == 2 && slot > 0) ? *(const float*)block : 0.0f;
+        merge_located(a, blockIdx.x, re.x, re.y, xs, red, ks);
+        store_kv_records(b, block, slot, 1, xs, red, s_sh, true, s_old);
+        // ks was complete at the merge's barrier before normalisation
+        if (b.idx != nullptr && b.c_idx > 0) store_idx_key(b, phys, slot, ks);
+        return;
+    }
+    const int gtok = blockIdx.x - nm;
+    const int req = a.one_per_req ? gtok : find_request(a.cu_new, a.n_req, gtok);
+    const int pos = a.start_pos[req] + (a.one_per_req ? 0 : gtok - a.cu_new[req]);
+    float* tail = (float*)((char*)a.state + (size_t)req * a.state_stride + a.tail_off);
+    copy_row(tail + (size_t)(pos % a.R) * a.ncols, a.P + (size_t)gtok * a.ncols, a.ncols, xs, a.c);
+    __syncthreads();
+    norm_rope_store(xs, red, a.c, a.r, a.gamma, a.eps, (double)pos, a.theta, a.out_win + (size_t)gtok * a.c);
+    store_window_row(b, req, pos, xs);
+}
+
 // ---------------------------------------------------------------------------
 // host launcher
 // ---------------------------------------------------------------------------
 
 hipError_t launch_compress(hipStream_t st, const CompressArgs& a, const void* H, const void* W, const void* Wi,
-                           int n_main, int d, bool bf16, int n_tokens)
+                           int n_main, int d, bool bf16, int n_tokens, const AppendArgs* app)
 {
     const int N = a.ncols, M = n_tokens;
     const GemmShape sh{d, N, 0, 0, 0, 0};
@@ -421,13 +479,21 @@ hipError_t launch_compress(hipStream_t st, const CompressArgs& a, const void* H,
     if (a.max_new <= 1) {
         CompressArgs b = a;
         b.one_per_req = M == a.n_req;                           // at most one each, n_req of them
-        post_decode_kernel<<<nm + M, 256, 0, st>>>(b, nm);
-    } else {
-        merge_kernel<<<nm, 256, 0, st>>>(a);
-        if (M > 0) {
-            window_rows_kernel<<<M, 256, 0, st>>>(a);
-            tail_update_kernel<<<dim3(a.R, a.n_req), 256, 0, st>>>(a);
-        }
+        if (app != nullptr)
+            post_decode_append_kernel<<<nm + M, 256, 0, st>>>(b, *app, nm);
+        else
+            post_decode_kernel<<<nm + M, 256, 0, st>>>(b, nm);
+        return hipGetLastError();
+    }
+    merge_kernel<<<nm, 256, 0, st>>>(a);
+    if (M > 0) {
+        window_rows_kernel<<<M, 256, 0, st>>>(a);
+        tail_update_kernel<<<dim3(a.R, a.n_req), 256, 0, st>>>(a);
+    }
+    if (app != nullptr) {
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        return launch_append(st, *app);
     }
     return hipGetLastError();
 }

@@ -36,8 +36,12 @@ struct CompressArgs {
 hipError_t launch_linear(hipStream_t st, bool bf16, int M, int K, int N, int groups, const void* X, const void* W,
                          void* Y, bool out_bf16);
 
+struct AppendArgs;
+
+// app: also append the outputs to the caches (one fused decode kernel when
+// every request has at most one new token, else the append launch after)
 hipError_t launch_compress(hipStream_t st, const CompressArgs& a, const void* H, const void* W, const void* Wi,
-                           int n_main, int d, bool bf16, int n_tokens);
+                           int n_main, int d, bool bf16, int n_tokens, const AppendArgs* app = nullptr);
 
 struct AppendArgs {
     const float* entries;

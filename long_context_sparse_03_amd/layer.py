@@ -80,6 +80,23 @@ class LayerState:
                         stream=stream)
         return out_e, out_k, meta, count, win
 
+    def compress_append(self, bi: BatchInfo, n_tokens: int, H, W, W_idx, B_a, B_b, B_a_idx, B_b_idx, gamma,
+                        max_entries: int, stream=None):
+        """compress() and then append() of its outputs, in one library call."""
+        d = self.desc
+        c = d.c
+        out_e = torch.empty((max(max_entries, 1), c), dtype=torch.float32, device=self.device)
+        out_k = (torch.empty((max(max_entries, 1), d.c_idx), dtype=torch.float32, device=self.device)
+                 if self.is_csa else None)
+        meta = torch.empty((max(max_entries, 1), 2), dtype=torch.int32, device=self.device)
+        count = torch.zeros(1, dtype=torch.int32, device=self.device)
+        win = torch.empty((max(n_tokens, 1), c), dtype=torch.float32, device=self.device)
+        ws = self.workspace("compress", abi.workspace_size(d, abi.OP_COMPRESS, n_tokens))
+        abi.compress_append(d, bi.batch, n_tokens, H.shape[1] if H is not None else W.shape[1], H, W, W_idx, B_a,
+                            B_b, B_a_idx, B_b_idx, gamma, self.state, out_e, out_k, meta, count, max_entries, win,
+                            self.kv, self.idx, ws, stream=stream)
+        return out_e, out_k, meta, count, win
+
     # -- a2 ---------------------------------------------------------------
     def append(self, bi: BatchInfo, n_tokens: int, entries, keys, meta, count, max_entries: int, win, stream=None):
         abi.cache_append(self.desc, bi.batch, n_tokens, entries, keys, meta, count, max_entries, win, self.kv,

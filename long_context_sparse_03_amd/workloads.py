@@ -5,9 +5,10 @@ with ctx tokens already in the caches.  The caches are filled through the
 library itself (cache_append), from fp32 rows that a caller-supplied source
 produces, so the stored bytes follow the library's own formats.  One decode
 step runs, for every layer in order, the library's calls for one new token
-per request; all buffers are allocated up front, so a step allocates nothing
-and can be captured in a HIP graph (positions live in device memory and the
-step advances them itself).
+per request (compress_append, or compress_kv and cache_append); all buffers
+are allocated up front, so a step allocates nothing and can be captured in a
+HIP graph (positions live in device memory and the step advances them
+itself).
 """
 from __future__ import annotations
 
@@ -30,8 +31,9 @@ def torch_rows(seed: int):
 
 class DecodeWorkload:
     def __init__(self, descs, d_model: int, n_req: int, ctx: int, max_steps: int, rows, seed: int = 0,
-                 weight_std: float | None = None, fill_chunk: int = 1 << 16):
+                 weight_std: float | None = None, fill_chunk: int = 1 << 16, fused_append: bool = True):
         self.descs = list(descs)
+        self.fused_append = fused_append
         self.d = d_model
         self.n_req = n_req
         self.ctx = ctx
@@ -145,11 +147,17 @@ class DecodeWorkload:
         b = self.bufs[li]
         desc, n, bi = st.desc, self.n_req, self.bi
         s = None
-        abi.compress_kv(desc, bi.batch, n, self.d, self.H, P["W"], P["W_idx"], P["B_a"], P["B_b"], P["B_a_idx"],
-                        P["B_b_idx"], P["gamma"], st.state, b["entries"], b["keys"] if st.is_csa else None,
-                        b["meta"], b["count"], n, b["win"], b["ws_c"], stream=s)
-        abi.cache_append(desc, bi.batch, n, b["entries"], b["keys"] if st.is_csa else None, b["meta"], b["count"], n,
-                         b["win"], st.kv, st.idx, st.state, stream=s)
+        keys = b["keys"] if st.is_csa else None
+        if self.fused_append:
+            abi.compress_append(desc, bi.batch, n, self.d, self.H, P["W"], P["W_idx"], P["B_a"], P["B_b"],
+                                P["B_a_idx"], P["B_b_idx"], P["gamma"], st.state, b["entries"], keys, b["meta"],
+                                b["count"], n, b["win"], st.kv, st.idx, b["ws_c"], stream=s)
+        else:
+            abi.compress_kv(desc, bi.batch, n, self.d, self.H, P["W"], P["W_idx"], P["B_a"], P["B_b"],
+                            P["B_a_idx"], P["B_b_idx"], P["gamma"], st.state, b["entries"], keys, b["meta"],
+                            b["count"], n, b["win"], b["ws_c"], stream=s)
+            abi.cache_append(desc, bi.batch, n, b["entries"], keys, b["meta"], b["count"], n, b["win"], st.kv,
+                             st.idx, st.state, stream=s)
         if st.is_csa:
             if hooks:
                 hooks[0]()

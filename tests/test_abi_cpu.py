@@ -136,3 +136,27 @@ def test_prefix_argument_checks():
     assert L.csa_prefix_state(None, ctypes.byref(d), 8, 8, 3) == -1               # direction
     assert L.csa_prefix_state(None, ctypes.byref(d), None, 8, 0) == -1            # no slot
 
+
+
+def test_compress_append_argument_checks():
+    """The fused call validates both halves' arguments on the host."""
+    L = P.lib()
+    d = presets.csa_flash_decode()
+    b = abi.Batch(n_req=1, max_new=1, max_ctx=1024, max_blocks=8, cu_new=8, start_pos=8, block_table=8)
+    args = [1, 4096, 8, 8, 8, 8, 8, 8, 8, 8, 8, 8, 8, 8, 8, 1, 8, 8, 8, 8, 1 << 30]
+    # no block table: the append half needs one
+    nb = abi.Batch(n_req=1, max_new=1, max_ctx=1024, max_blocks=8, cu_new=8, start_pos=8, block_table=None)
+    assert L.csa_compress_append(None, ctypes.byref(d), ctypes.byref(nb), *args) == -1
+    assert b"block_table" in L.csa_last_error()
+    # CSA entries need the indexer pool
+    a2 = list(args)
+    a2[18] = None
+    assert L.csa_compress_append(None, ctypes.byref(d), ctypes.byref(b), *a2) == -1
+    # the compress half's workspace check
+    a3 = list(args)
+    a3[-1] = 16
+    assert L.csa_compress_append(None, ctypes.byref(d), ctypes.byref(b), *a3) == -3
+    # more new tokens than the window ring holds
+    b.max_new = 129
+    assert L.csa_compress_append(None, ctypes.byref(d), ctypes.byref(b), *args) == -1
+    assert b"win_cap" in L.csa_last_error()

@@ -1,0 +1,82 @@
+"""csa_compress_append against csa_compress_kv followed by csa_cache_append
+([DD] §7: entries and window rows go to the caches as they are produced).
+
+Two copies of a layer's caches and state receive the same calls, one copy
+through the two separate calls, the other through the fused one.  After
+every call the KV pool, the indexer-key pool, the state slots and every
+output (entries, keys, meta, count, window rows) must be equal byte for
+byte.  The calls: a ragged prefill (several new tokens per request: the two
+kernels run in order), decode steps with one token per request (the fused
+kernel) across entry and block boundaries, decode steps where one request
+has no new token, and an empty call.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from harness import batch, to_dev
+from long_context_sparse_03_amd import abi, presets
+from long_context_sparse_03_amd.layer import LayerState
+from test_gpu_layers import Params
+
+pytestmark = pytest.mark.gpu
+
+# window rings of 512 rows: the prefill call writes 300 rows per request
+CASES = {
+    "tiny_fp32": (lambda: presets.tiny_csa_fp32(win_cap=512), 512),
+    "flash_fp8": (lambda: presets.csa_flash_decode(win_cap=512), 1024),
+    "pro_mxfp4": (lambda: presets.csa_pro(win_cap=512, idx_fmt=abi.IDX_MXFP4), 1024),
+    "hca_bf16": (lambda: presets.hca_bf16(win_cap=512), 1024),
+    "hca_fp8": (lambda: presets.hca_pro(win_cap=512), 1024),
+}
+
+
+def _calls():
+    """(start positions, new tokens) per call for three requests."""
+    start = np.zeros(3, np.int64)
+    out = []
+    for n_new in [(300, 129, 5)] + [(1, 1, 1)] * 90 + [(1, 0, 1)] * 6 + [(0, 0, 0)] + [(1, 1, 1)] * 3:
+        out.append((start.copy(), np.asarray(n_new, np.int64)))
+        start += n_new
+    return out
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_compress_append_matches_separate_calls(case):
+    make, d = CASES[case]
+    desc = make()
+    g = synth.rng(77)
+    P = Params(g, desc, d)
+    dv = P.dev
+    calls = _calls()
+    max_ctx = int(calls[-1][0].max() + calls[-1][1].max())
+    n_blocks = max_ctx // 128 + 2
+    bt = g.permutation(3 * n_blocks).astype(np.int32).reshape(3, n_blocks)
+    sep = LayerState(desc, 3, bt.size)
+    fus = LayerState(desc, 3, bt.size)
+    adt = torch.bfloat16 if desc.act_fmt == abi.ACT_BF16 else torch.float32
+    print(f"compress_append {case}: {len(calls)} calls", flush=True)
+    for i, (start, n_new) in enumerate(calls):
+        T = int(n_new.sum())
+        bi = batch(start, n_new, bt, max_ctx=max_ctx)
+        max_e = int(sum((s + n) // desc.m - s // desc.m for s, n in zip(start, n_new)))
+        H = to_dev(synth.normal(g, (T, d)), adt) if T > 0 else None
+        args = (bi, T, H, dv["W"], dv["W_I"], dv["Ba"], dv["Bb"], dv["BaI"], dv["BbI"], dv["gamma"], max_e)
+        a = sep.compress(*args)
+        sep.append(bi, T, *a[:4], max_e, a[4])
+        b = fus.compress_append(*args)
+        torch.cuda.synchronize()
+        what = f"{case} call {i} (start {start.tolist()}, new {n_new.tolist()})"
+        assert torch.equal(sep.kv, fus.kv), f"{what}: KV pool differs"
+        if sep.idx is not None:
+            assert torch.equal(sep.idx, fus.idx), f"{what}: indexer pool differs"
+        assert torch.equal(sep.state, fus.state), f"{what}: state differs"
+        cnt = int(a[3].item())
+        assert cnt == int(b[3].item()) == max_e, what
+        assert torch.equal(a[0][:cnt].view(torch.int32), b[0][:cnt].view(torch.int32)), f"{what}: entries"
+        if a[1] is not None:
+            assert torch.equal(a[1][:cnt].view(torch.int32), b[1][:cnt].view(torch.int32)), f"{what}: keys"
+        assert torch.equal(a[2][:cnt], b[2][:cnt]), f"{what}: meta"
+        assert torch.equal(a[4][:T].view(torch.int32), b[4][:T].view(torch.int32)), f"{what}: window rows"
+    print(f"  {case}: caches and outputs identical after every call", flush=True)
