@@ -975,26 +975,45 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
 }
 
 // Merge the split partials of one (query, head) in split order, add the sink,
-// normalise, rotate back at -t and store.  One workgroup of 128 threads per
-// (query, head); each thread owns 4 consecutive channels.  The partials'
-// (max, sum) pairs and (up to CB splits) the thread's channels of every
-// partial are loaded at once; the weights and the denominator come from
-// fixed-order reductions, so the result does not depend on scheduling.
-constexpr int CB = 16;                                         // splits whose channels load in one batch
-__global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a)
+// normalise, rotate back at -t and store.  The weights and the denominator
+// come from fixed-order reductions, so the result does not depend on
+// scheduling.
+constexpr int CB = 8;                                          // splits whose channels load in one batch
+// One wave per (query, head), four per workgroup, no LDS and no barrier: lane
+// l holds split l's (max, sum) (64 splits at a time) and output channels
+// 8l .. 8l+7.  The reference max M (with the sink) and the denominator are
+// wave reductions (butterfly; further chunks of 64 splits added in order);
+// every lane then adds its channels of each split in split order, weighted
+// 2^(m_s - M), and rotates its channel pairs of the RoPE part back by the
+// query position.
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a)
 {
-    __shared__ float red[2][2];
-    __shared__ float o_sh[512];
-    __shared__ float rc[32], rs[32];
-    const int gq = blockIdx.x, head = blockIdx.y;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int gq = blockIdx.x, head = blockIdx.y * 4 + (int)(threadIdx.x >> 6);
+    if (head >= a.nh) return;                                  // wave-uniform
     const int C = a.c, S = a.n_splits, nf = C - a.r;
-    const size_t pstride = a.out_bf16 ? 2 * (size_t)C + 16 : 4 * (size_t)C + 16;
+    const bool bf = a.out_bf16;
+    const size_t pstride = bf ? 2 * (size_t)C + 16 : 4 * (size_t)C + 16;
     const char* pp = (const char*)a.ws + ((size_t)gq * a.nh + head) * S * pstride;
-    const int d4 = threadIdx.x;                                // channels 4 d4 .. 4 d4 + 3
-    const bool dv = d4 < C / 4;
-    // loads first: position, (max, sum) of splits tid and tid + 128, and the
-    // thread's channels of the first CB splits
+    const int d0 = 8 * lane;
+    const bool dv = d0 < C;
+    // loads first: (max, sum) of split `lane`, the lane's channels of the
+    // first CB splits, the position
+    const float2 ml0 = lane < S ? *(const float2*)(pp + (size_t)lane * pstride) : make_float2(-INFINITY, 0.f);
+    uint4 ov[CB][2];
+#pragma unroll
+    for (int sb = 0; sb < CB; ++sb) {
+        const char* src = pp + (size_t)min(sb, S - 1) * pstride + 16;
+        ov[sb][0] = ov[sb][1] = make_uint4(0u, 0u, 0u, 0u);
+        if (dv && sb < S) {
+            if (bf) {
+                ov[sb][0] = *(const uint4*)(src + 2 * (size_t)d0);
+            } else {
+                ov[sb][0] = *(const uint4*)(src + 4 * (size_t)d0);
+                ov[sb][1] = *(const uint4*)(src + 4 * (size_t)d0 + 16);
+            }
+        }
+    }
     int req, tok;
     if (a.one_per_req) {
         req = gq;
@@ -1003,87 +1022,83 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a)
         req = find_request(a.cu_new, a.n_req, gq);
         tok = gq - a.cu_new[req];
     }
-    float2 ml[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int sidx = threadIdx.x + 128 * u;
-        ml[u] = sidx < S ? *(const float2*)(pp + sidx * pstride) : make_float2(-INFINITY, 0.f);
-    }
-    uint4 ov[CB];
-#pragma unroll
-    for (int sb = 0; sb < CB; ++sb) {
-        const char* src = pp + (size_t)min(sb, S - 1) * pstride + 16;
-        if (a.out_bf16) {
-            const uint2 u = dv ? *(const uint2*)(src + 8 * (size_t)d4) : make_uint2(0u, 0u);
-            ov[sb] = make_uint4(u.x, u.y, 0u, 0u);
-        } else {
-            ov[sb] = dv ? *(const uint4*)(src + 16 * (size_t)d4) : make_uint4(0u, 0u, 0u, 0u);
-        }
-    }
     const int t = a.start_pos[req] + tok;
     const float zs = a.sinks[head] * LOG2E;
-    for (int j = threadIdx.x; j < a.r / 2; j += blockDim.x) rope_cs_f((double)t, a.inv_freq[j], &rc[j], &rs[j]);
     // the common reference max (with the sink)
-    float M = fmaxf(ml[0].x, ml[1].x);
-    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-    if (lane == 0) red[0][wave] = M;
-    __syncthreads();
-    M = fmaxf(fmaxf(red[0][0], red[0][1]), zs);
-    // the denominator: sum of l_s * 2^(m_s - M) over splits in a fixed tree order
-    float w0 = ml[0].x == -INFINITY ? 0.f : exp2f(ml[0].x - M);
-    float w1 = ml[1].x == -INFINITY ? 0.f : exp2f(ml[1].x - M);
-    float Lp = ml[0].y * w0 + ml[1].y * w1;
-    for (int o = 32; o > 0; o >>= 1) Lp += __shfl_xor(Lp, o, 64);
-    if (lane == 0) red[1][wave] = Lp;
-    __syncthreads();
-    const float inv = 1.0f / (exp2f(zs - M) + (red[1][0] + red[1][1]));
+    float M = ml0.x;
+    for (int s0 = 64; s0 < S; s0 += 64)
+        M = fmaxf(M, s0 + lane < S ? *(const float*)(pp + (size_t)(s0 + lane) * pstride) : -INFINITY);
+    M = fmaxf(wave_max(M), zs);
+    // the denominator: sum of l_s * 2^(m_s - M)
+    float L = wave_sum(ml0.y * (ml0.x == -INFINITY ? 0.f : exp2f(ml0.x - M)));
+    for (int s0 = 64; s0 < S; s0 += 64) {
+        const float2 v = s0 + lane < S ? *(const float2*)(pp + (size_t)(s0 + lane) * pstride)
+                                       : make_float2(-INFINITY, 0.f);
+        L += wave_sum(v.y * (v.x == -INFINITY ? 0.f : exp2f(v.x - M)));
+    }
+    const float inv = 1.0f / (exp2f(zs - M) + L);
     // weighted sum of the partial outputs in split order
-    float o4[4] = {0.f, 0.f, 0.f, 0.f};
-    auto accum = [&](int sidx, uint4 u) {
-        const float ms = *(const float*)(pp + sidx * pstride);    // the split's max (cached)
+    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    auto accum = [&](int sidx, const uint4& u0, const uint4& u1) {
+        const float ms = sidx < 64 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ml0.x), sidx))
+                                   : *(const float*)(pp + (size_t)sidx * pstride);
         const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
         if (w == 0.f) return;                                  // empty splits add nothing, not even +0
-        float v[4];
-        if (a.out_bf16) {
-            v[0] = bf16_to_f32(u.x & 0xFFFF); v[1] = bf16_to_f32(u.x >> 16);
-            v[2] = bf16_to_f32(u.y & 0xFFFF); v[3] = bf16_to_f32(u.y >> 16);
+        float v[8];
+        if (bf) {
+            const uint32_t h[4] = {u0.x, u0.y, u0.z, u0.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[2 * i] = bf16_to_f32(h[i] & 0xFFFF);
+                v[2 * i + 1] = bf16_to_f32(h[i] >> 16);
+            }
         } else {
-            v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y);
-            v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
+            const uint32_t h[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(h[i]);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o4[i] += v[i] * w;
+        for (int i = 0; i < 8; ++i) o[i] += v[i] * w;
     };
 #pragma unroll
     for (int sb = 0; sb < CB; ++sb)
-        if (sb < S) accum(sb, ov[sb]);
+        if (sb < S) accum(sb, ov[sb][0], ov[sb][1]);
     for (int sidx = CB; sidx < S; ++sidx) {
         const char* src = pp + (size_t)sidx * pstride + 16;
-        uint4 u = make_uint4(0u, 0u, 0u, 0u);
+        uint4 u0 = make_uint4(0u, 0u, 0u, 0u), u1 = u0;
         if (dv) {
-            if (a.out_bf16) {
-                const uint2 h = *(const uint2*)(src + 8 * (size_t)d4);
-                u = make_uint4(h.x, h.y, 0u, 0u);
+            if (bf) {
+                u0 = *(const uint4*)(src + 2 * (size_t)d0);
             } else {
-                u = *(const uint4*)(src + 16 * (size_t)d4);
+                u0 = *(const uint4*)(src + 4 * (size_t)d0);
+                u1 = *(const uint4*)(src + 4 * (size_t)d0 + 16);
             }
         }
-        accum(sidx, u);
+        accum(sidx, u0, u1);
     }
-    if (dv) {
+    if (!dv) return;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o_sh[4 * d4 + i] = o4[i] * inv;
-    }
-    __syncthreads();
-    for (int d = threadIdx.x; d < C; d += blockDim.x) {
-        float o = o_sh[d];
+    for (int i = 0; i < 8; ++i) o[i] *= inv;
+    // channel pairs (d, d+1) of the RoPE part: nf is even, so pairs never
+    // straddle a lane's eight channels or the RoPE boundary
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int d = d0 + 2 * q;
         if (d >= nf) {
-            const int pj = (d - nf) >> 1;
-            const float u0 = o_sh[nf + 2 * pj], u1 = o_sh[nf + 2 * pj + 1];
-            o = ((d - nf) & 1) ? (-u0 * rs[pj] + u1 * rc[pj]) : (u0 * rc[pj] + u1 * rs[pj]);
+            float cs, sn;
+            rope_cs_f((double)t, a.inv_freq[(d - nf) >> 1], &cs, &sn);
+            const float u0 = o[2 * q], u1 = o[2 * q + 1];
+            o[2 * q] = u0 * cs + u1 * sn;
+            o[2 * q + 1] = -u0 * sn + u1 * cs;
         }
-        if (a.out_bf16) ((uint16_t*)a.out)[((size_t)gq * a.nh + head) * C + d] = f32_to_bf16(o);
-        else ((float*)a.out)[((size_t)gq * a.nh + head) * C + d] = o;
+    }
+    const size_t ob = ((size_t)gq * a.nh + head) * C + d0;
+    if (bf) {
+        *(uint4*)((uint16_t*)a.out + ob) = make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                                                       pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7]));
+    } else {
+        *(float4*)((float*)a.out + ob) = make_float4(o[0], o[1], o[2], o[3]);
+        *(float4*)((float*)a.out + ob + 4) = make_float4(o[4], o[5], o[6], o[7]);
     }
 }
 
@@ -1153,6 +1168,9 @@ hipError_t launch_attention(hipStream_t st, AttnArgs a)
     } else {
         a.n_splits = attention_splits(a.n_tokens, a.nh, a.rows_max);
         a.tiles_per_split = (tiles + a.n_splits - 1) / a.n_splits;
+        // no split left without tiles (20 tiles over 8 splits of 3: seven),
+        // so no workgroup writes and no combine reads an empty partial
+        a.n_splits = (tiles + a.tiles_per_split - 1) / a.tiles_per_split;
     }
     for (int j = 0; j < a.r / 2 && j < 32; ++j) a.inv_freq[j] = rope_inv_freq(j, a.r, (double)a.theta);
     const dim3 grid(a.n_tokens, hg, a.n_splits);
@@ -1160,7 +1178,7 @@ hipError_t launch_attention(hipStream_t st, AttnArgs a)
         attn_ht_kernel<512, 64, 4><<<grid, 512, 0, st>>>(a);     // FP8 serving shapes: two waves per head tile
     else if (ht == 4) launch_ht<4>(st, a, grid);
     else launch_ht<1>(st, a, grid);
-    if (a.n_splits > 1 || a.invariant) attn_combine_kernel<<<dim3(a.n_tokens, a.nh), 128, 0, st>>>(a);
+    if (a.n_splits > 1 || a.invariant) attn_combine_kernel<<<dim3(a.n_tokens, (a.nh + 3) / 4), 256, 0, st>>>(a);
     return hipGetLastError();
 }
 
