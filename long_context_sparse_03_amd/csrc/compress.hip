@@ -149,6 +149,91 @@ __global__ __launch_bounds__(64 * NW) void proj_small(const T* __restrict__ X, c
     }
 }
 
+// Few-row bf16 products with both operands staged through LDS.  Wave w owns
+// channels [w K/NW, (w+1) K/NW); per batch of up to 256 channels it copies the
+// 16 rows of X and the 16 rows of W that its fragments need into its own LDS
+// region, row after row (two rows of 512 bytes per instruction: 16-byte
+// chunk c of row r lands at slot c ^ r), and reads the MFMA fragments from
+// there (fragment lanes of one chunk index sit in 16 different banks).
+// Reading the fragments straight from memory makes every load instruction
+// touch 16 rows 64 bytes at a time, so the weight stream spreads over 16
+// DRAM pages per instruction instead of one or two.  Requires K % (32 NW)
+// == 0 and 16-byte aligned rows.
+constexpr int PL_NW = 8;                      // waves per workgroup
+constexpr int PL_KB = 256;                    // channels per wave and batch (512 bytes of a bf16 row)
+
+__global__ __launch_bounds__(64 * PL_NW) void proj_small_lds(const uint16_t* __restrict__ X,
+                                                             const uint16_t* __restrict__ W,
+                                                             const uint16_t* __restrict__ Wi, int n_main, int N,
+                                                             int M, int K, void* __restrict__ P, GemmShape sh)
+{
+    constexpr int NW = PL_NW, RB = PL_KB * 2;                  // bytes of a row's batch
+    __shared__ __attribute__((aligned(16))) uint16_t Xs[NW][16 * PL_KB];
+    __shared__ __attribute__((aligned(16))) uint16_t Ws[NW][16 * PL_KB];
+    __shared__ float red[NW][64][4];
+    X += blockIdx.z * sh.gx;
+    W += blockIdx.z * sh.gw;
+    Wi += blockIdx.z * sh.gw;
+    const size_t p0 = blockIdx.z * sh.gp;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
+    const int kq = K / NW, kb = wave * kq;
+    // the two rows this lane copies: r = 2i + lane / 32 for instruction i;
+    // rows past M or N read row 0 (their outputs are not stored)
+    const char* xr[8];
+    const char* wr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = 2 * i + (lane >> 5);
+        const int m = blockIdx.y * 16 + r, n = blockIdx.x * 16 + r;
+        const int mm = m < M ? m : 0, nn = n < N ? n : 0;
+        xr[i] = (const char*)(X + (size_t)mm * sh.ldx + kb);
+        wr[i] = (const char*)(nn < n_main ? W + (size_t)nn * K : Wi + (size_t)(nn - n_main) * K) + 2 * (size_t)kb;
+    }
+    f32x4_t acc[4] = {zero4(), zero4(), zero4(), zero4()};
+    for (int k0 = 0; k0 < kq; k0 += PL_KB) {
+        const int nb = min(8, (kq - k0) / MmaBF16::K);       // 32-channel steps in this batch
+        // this wave's fragment reads of the previous batch have completed
+        // (their MFMAs consumed them) before its region is refilled
+        __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 2 * i + (lane >> 5);
+            // chunks past the batch (a short last batch) repeat its last chunk
+            const int c = min((lane & 31) ^ r, 4 * nb - 1);
+            const size_t off = 2 * (size_t)k0 + 16 * (size_t)c;
+            __builtin_amdgcn_global_load_lds((const CSA_GLOBAL void*)(xr[i] + off), (CSA_LDS void*)&Xs[wave][i * RB],
+                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const CSA_GLOBAL void*)(wr[i] + off), (CSA_LDS void*)&Ws[wave][i * RB],
+                                             16, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);                    // vmcnt(0): both regions filled
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (u < nb) {
+                const int slot = (4 * u + g) ^ li;
+                const uint4 av = *(const uint4*)&Xs[wave][li * PL_KB + 8 * slot];
+                const uint4 bv = *(const uint4*)&Ws[wave][li * PL_KB + 8 * slot];
+                acc[u & 3] = MmaBF16::step(av, bv, acc[u & 3]);
+            }
+        }
+    }
+    const f32x4_t acc0 = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) red[wave][lane][q] = acc0[q];
+    __syncthreads();
+    if (wave == 0) {
+        const int col = blockIdx.x * 16 + li;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float v = red[0][lane][q];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) v += red[w][lane][q];
+            int row = blockIdx.y * 16 + 4 * g + q;
+            if (row < M && col < N) store_out(P, p0 + (size_t)row * sh.ldp + col, sh.out_bf16, v);
+        }
+    }
+}
+
 // Copy n floats from src to dst (and the first n2 of them also to dst2) with
 // the threads of the block: 16-byte pieces when every pointer is 16-byte
 // aligned and n, n2 are multiples of 4, each thread's pieces of a batch all
@@ -456,9 +541,9 @@ hipError_t launch_compress(hipStream_t st, const CompressArgs& a, const void* H,
         // for a row do not depend on the other rows)
         if (M <= 64 || a.invariant) {
             dim3 grid((N + 15) / 16, (M + 15) / 16);
-            if (bf16 && d % (16 * MmaBF16::K) == 0)              // 16 waves of whole steps
-                proj_small<uint16_t, MmaBF16, 16><<<grid, 1024, 0, st>>>((const uint16_t*)H, (const uint16_t*)W,
-                                                                         (const uint16_t*)Wi, n_main, N, M, d, a.P, sh);
+            if (bf16 && d % (PL_NW * MmaBF16::K) == 0 && d >= PL_NW * PL_KB)   // whole steps, full batches
+                proj_small_lds<<<grid, 64 * PL_NW, 0, st>>>((const uint16_t*)H, (const uint16_t*)W, (const uint16_t*)Wi,
+                                                            n_main, N, M, d, a.P, sh);
             else if (bf16)
                 proj_small<uint16_t, MmaBF16, 4><<<grid, 256, 0, st>>>((const uint16_t*)H, (const uint16_t*)W,
                                                                        (const uint16_t*)Wi, n_main, N, M, d, a.P, sh);
@@ -511,10 +596,10 @@ hipError_t launch_linear(hipStream_t st, bool bf16, int M, int K, int N, int gro
     const GemmShape sh{K * groups, N * groups, out_bf16 ? 1 : 0, (size_t)K, (size_t)N * K, (size_t)N};
     if (M <= 64) {
         dim3 grid((N + 15) / 16, (M + 15) / 16, groups);
-        // sixteen waves per column tile only when each gets a long slice of K
-        if (bf16 && K % (16 * MmaBF16::K) == 0 && K >= 4096)
-            proj_small<uint16_t, MmaBF16, 16><<<grid, 1024, 0, st>>>((const uint16_t*)X, (const uint16_t*)W,
-                                                                     (const uint16_t*)W, N, N, M, K, Y, sh);
+        // operands through LDS only when each wave gets at least one full batch of K
+        if (bf16 && K % (PL_NW * MmaBF16::K) == 0 && K >= PL_NW * PL_KB)
+            proj_small_lds<<<grid, 64 * PL_NW, 0, st>>>((const uint16_t*)X, (const uint16_t*)W, (const uint16_t*)W, N,
+                                                        N, M, K, Y, sh);
         else if (bf16)
             proj_small<uint16_t, MmaBF16, 4><<<grid, 256, 0, st>>>((const uint16_t*)X, (const uint16_t*)W,
                                                                    (const uint16_t*)W, N, N, M, K, Y, sh);
