@@ -1063,18 +1063,25 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a)
 #pragma unroll
     for (int sb = 0; sb < CB; ++sb)
         if (sb < S) accum(sb, ov[sb][0], ov[sb][1]);
-    for (int sidx = CB; sidx < S; ++sidx) {
-        const char* src = pp + (size_t)sidx * pstride + 16;
-        uint4 u0 = make_uint4(0u, 0u, 0u, 0u), u1 = u0;
-        if (dv) {
-            if (bf) {
-                u0 = *(const uint4*)(src + 2 * (size_t)d0);
-            } else {
-                u0 = *(const uint4*)(src + 4 * (size_t)d0);
-                u1 = *(const uint4*)(src + 4 * (size_t)d0 + 16);
+    // further splits in batches of CB, each batch's loads issued before its
+    // accumulation (same order of additions)
+    for (int s0 = CB; s0 < S; s0 += CB) {
+#pragma unroll
+        for (int sb = 0; sb < CB; ++sb) {
+            const char* src = pp + (size_t)min(s0 + sb, S - 1) * pstride + 16;
+            ov[sb][0] = ov[sb][1] = make_uint4(0u, 0u, 0u, 0u);
+            if (dv) {
+                if (bf) {
+                    ov[sb][0] = *(const uint4*)(src + 2 * (size_t)d0);
+                } else {
+                    ov[sb][0] = *(const uint4*)(src + 4 * (size_t)d0);
+                    ov[sb][1] = *(const uint4*)(src + 4 * (size_t)d0 + 16);
+                }
             }
         }
-        accum(sidx, u0, u1);
+#pragma unroll
+        for (int sb = 0; sb < CB; ++sb)
+            if (s0 + sb < S) accum(s0 + sb, ov[sb][0], ov[sb][1]);
     }
     if (!dv) return;
 #pragma unroll
