@@ -32,7 +32,7 @@ constexpr int CAP32 = 20480;                  // fp32 keys per workgroup
 constexpr int KPT16 = CAP16 / TOPK_THREADS;   // keys per thread at the capacity
 constexpr int KPT32 = CAP32 / TOPK_THREADS;
 constexpr int SMALL_NT = 256, SMALL_KPT = 32; // workgroups of up to 8192 keys
-constexpr int MID_KPT = 40;                   // 256 threads for up to 10240 keys
+constexpr int MID_KPT = 16;                   // 1024 threads for up to 16384 keys
 constexpr int SURV_CAP = 4096;                // keys kept after the lower bound (1024-thread workgroups)
 
 // Order-preserving key of a score: sign-magnitude flip; -0 and +0 share the key.
@@ -607,9 +607,9 @@ static void launch_chunks(hipStream_t st, dim3 grid, int chunk, const void* scor
     if (chunk <= SMALL_NT * SMALL_KPT)
         topk_chunk_kernel<BF16, SMALL_NT, SMALL_KPT><<<grid, SMALL_NT, 0, st>>>(scores, ld, n_valid, k, chunk,
                                                                                 n_chunks, out, ck, ci);
-    else if (BF16 && chunk <= SMALL_NT * MID_KPT)
-        topk_chunk_kernel<BF16, SMALL_NT, MID_KPT><<<grid, SMALL_NT, 0, st>>>(scores, ld, n_valid, k, chunk,
-                                                                              n_chunks, out, ck, ci);
+    else if (BF16 && chunk <= TOPK_THREADS * MID_KPT)        // faster than 256 threads x 40 keys here
+        topk_chunk_kernel<BF16, TOPK_THREADS, BF16 ? MID_KPT : KPT32><<<grid, TOPK_THREADS, 0, st>>>(
+            scores, ld, n_valid, k, chunk, n_chunks, out, ck, ci);
     else
         topk_chunk_kernel<BF16, TOPK_THREADS, BF16 ? KPT16 : KPT32><<<grid, TOPK_THREADS, 0, st>>>(
             scores, ld, n_valid, k, chunk, n_chunks, out, ck, ci);
