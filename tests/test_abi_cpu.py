@@ -111,8 +111,10 @@ def test_workspace_sizes():
     assert P.workspace_size(d, abi.OP_COMPRESS, 16) == 16 * (4 * 512 + 4 * 128) * 4
     assert P.workspace_size(d, abi.OP_TOPK, 4096, 32768, 512) == 0        # rows that fit a workgroup: one stage
     assert P.workspace_size(d, abi.OP_TOPK, 16, 32768, 512) == 0
-    assert P.workspace_size(d, abi.OP_TOPK, 16, 40961, 512) == 16 * 17 * 512 * 8   # few long rows: 17 chunks of 2560
-    assert P.workspace_size(d, abi.OP_TOPK, 4, 262144, 1024) == 4 * 26 * 1024 * 8  # 26 chunks of 10240
+    # few long bf16 rows: equal chunks of at most 16384 keys (multiples of 64)
+    assert P.workspace_size(d, abi.OP_TOPK, 16, 40961, 512) == 16 * 3 * 512 * 8    # 3 chunks of 13696
+    assert P.workspace_size(d, abi.OP_TOPK, 4, 262144, 1024) == 4 * 16 * 1024 * 8  # 16 chunks of 16384
+    assert P.workspace_size(d, abi.OP_TOPK, 4096, 262144, 1024) == 4096 * 7 * 1024 * 8   # many rows: 40960
     assert P.workspace_size(d, abi.OP_ATTENTION, 16, 640) > 0               # few queries: split-KV partials
     assert P.workspace_size(d, abi.OP_ATTENTION, 4096, 640) == 0
     # batch-invariant layer: partials of splits every 128 rows, whatever the
