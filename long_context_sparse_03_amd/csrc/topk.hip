@@ -31,7 +31,8 @@ constexpr int CAP16 = 40960;                  // bf16 keys per workgroup
 constexpr int CAP32 = 20480;                  // fp32 keys per workgroup
 constexpr int KPT16 = CAP16 / TOPK_THREADS;   // keys per thread at the capacity
 constexpr int KPT32 = CAP32 / TOPK_THREADS;
-constexpr int SMALL_NT = 256, SMALL_KPT = 32; // workgroups of up to 8192 keys
+constexpr int SMALL_NT = 512, SMALL_KPT = 16; // workgroups of up to 8192 keys (512 threads: 9 us for
+                                              // 16 rows of 8192, 12 us with 256 x 32)
 constexpr int MID_KPT = 16;                   // 1024 threads for up to 16384 keys
 constexpr int SURV_CAP = 4096;                // keys kept after the lower bound (1024-thread workgroups)
 
