@@ -525,3 +525,139 @@ def test_query_path_is_the_low_rank_product():
     bound = 2.0 ** -8 * np.abs(H @ W_DQ.T) @ np.abs(W_UQ).T
     assert np.all(np.abs(qr - q) <= bound + 1e-15)
     assert np.any(qr != q)                       # the rounding is applied
+
+
+# ---------------------------------------------------------------------------
+# whole-layer composition of the compressor (oracle/layer.py compress_layer)
+# and of the query side (csa_queries)
+# ---------------------------------------------------------------------------
+
+def _golden_cols(rows):
+    return np.array([[math.log(3) if v == "ln3" else math.log(2) if v == "ln2" else float(v) for v in r]
+                     for r in rows])
+
+
+def test_compress_layer_worked_example():
+    """Hand-derived composition (tests/golden/compress_layer_worked.json):
+    fixes the projection's column order C^a | C^b | Z^a | Z^b, the pairing of
+    a- and b-rows, RMSNorm before RoPE, entry i rotated at pos0 + m*i, window
+    row j at pos0 + j, and raw (unnormalised, unrotated) indexer keys."""
+    d = _gold("compress_layer_worked.json")
+    m, c, r, cI = d["m"], d["c"], d["r"], d["c_I"]
+    spec = L.Spec("csa", m=m, c=c, r=r, n_h=1, n_hI=1, c_I=cI, top_k=1, eps=0.0, theta=10000.0)
+    W = np.concatenate([_golden_cols(d[k]) for k in ("Ca", "Cb", "Za", "Zb")], axis=1)      # [4, 4c]
+    W_I = np.concatenate([_golden_cols(d[k]) for k in ("CaI", "CbI", "ZaI", "ZbI")], axis=1)  # [4, 4cI]
+    H = np.eye(4)
+    z, zI = np.zeros((m, c)), np.zeros((m, cI))
+    gam = np.array(d["gamma"])
+    E, K, R = L.compress_layer(spec, H, W, z, z, gam, W_I, zI, zI)
+    assert np.allclose(E, d["expected_entries"], atol=1e-12)
+    assert np.allclose(K, d["expected_keys"], atol=1e-12)
+    assert np.allclose(R, d["expected_window"], atol=1e-12)
+    E2, K2, R2 = L.compress_layer(spec, H, W, z, z, gam, W_I, zI, zI, pos0=2)
+    assert np.allclose(E2, d["pos0_2"]["expected_entries"], atol=1e-12)
+    assert np.allclose(K2, d["expected_keys"], atol=1e-12)              # keys carry no position
+    assert np.allclose(R2[:2], d["pos0_2"]["expected_window_01"], atol=1e-12)
+
+
+@pytest.mark.parametrize("kind", ["csa", "hca"])
+def test_compress_layer_prefix_and_continuation(kind):
+    """Causality: entries, keys and window rows of a prefix do not depend on
+    later tokens, and a sequence restarted at pos0 = a (a multiple of m, the
+    last 2m rows of history given again, as the decode path does) reproduces
+    the full run's later entries, keys and window rows.  For CSA the restart's
+    first entry lacks the b-half of the block before it (by design: that
+    block's rows are not part of the restarted sequence), so it differs."""
+    g = np.random.default_rng(40)
+    m = 4 if kind == "csa" else 8
+    c, r, cI, dm, n = 16, 4, 8, 24, 72
+    spec = L.Spec(kind, m=m, c=c, r=r, n_h=1, n_hI=2, c_I=cI, top_k=4)
+    ncol = 4 * c if kind == "csa" else 2 * c
+    W = g.standard_normal((dm, ncol)) / math.sqrt(dm)
+    W_I = g.standard_normal((dm, 4 * cI)) / math.sqrt(dm) if kind == "csa" else None
+    Ba, Bb = g.standard_normal((m, c)), g.standard_normal((m, c)) if kind == "csa" else None
+    BaI = g.standard_normal((m, cI)) if kind == "csa" else None
+    BbI = g.standard_normal((m, cI)) if kind == "csa" else None
+    gam = 1.0 + 0.1 * g.standard_normal(c)
+    H = g.standard_normal((n, dm))
+    E, K, R = L.compress_layer(spec, H, W, Ba, Bb, gam, W_I, BaI, BbI)
+    assert E.shape == (n // m, c) and R.shape == (n, c)
+    # prefix: the first n - 8 tokens alone give the same (complete) entries
+    Ep, Kp, Rp = L.compress_layer(spec, H[:n - 8], W, Ba, Bb, gam, W_I, BaI, BbI)
+    assert np.allclose(Ep, E[:(n - 8) // m], atol=1e-12, rtol=0)
+    assert np.allclose(Rp, R[:n - 8], atol=1e-12, rtol=0)
+    if kind == "csa":
+        assert np.allclose(Kp, K[:(n - 8) // m], atol=1e-12, rtol=0)
+    for a in (2 * m, 5 * m):
+        Es, Ks, Rs = L.compress_layer(spec, H[a:], W, Ba, Bb, gam, W_I, BaI, BbI, pos0=a)
+        first = 1 if kind == "csa" else 0
+        assert np.allclose(Es[first:], E[a // m + first:], atol=1e-12, rtol=0)
+        assert np.allclose(Rs, R[a:], atol=1e-12, rtol=0)
+        if kind == "csa":
+            assert np.allclose(Ks[1:], K[a // m + 1:], atol=1e-12, rtol=0)
+            assert not np.allclose(Es[0], E[a // m], atol=1e-6)            # b-half missing
+            assert not np.allclose(Ks[0], K[a // m], atol=1e-6)
+    # a chunked run (prefill n-8, then 8 single tokens, each restarted from the
+    # last 2m tokens of history) reproduces every entry and window row
+    E_c, R_c = [E[:(n - 8) // m]], [R[:n - 8]]
+    for t in range(n - 8, n):
+        p0 = (t + 1 - 2 * m) // m * m
+        El, _, Rl = L.compress_layer(spec, H[p0:t + 1], W, Ba, Bb, gam, W_I, BaI, BbI, pos0=p0)
+        R_c.append(Rl[t - p0:t - p0 + 1])
+        if (t + 1) % m == 0:
+            E_c.append(El[-1:])
+    assert np.allclose(np.concatenate(E_c), E, atol=1e-12, rtol=0)
+    assert np.allclose(np.concatenate(R_c), R, atol=1e-12, rtol=0)
+
+
+def _rot_matrix(c, r, pos, theta):
+    """Explicit block-diagonal RoPE matrix: identity on the first c-r channels,
+    one 2x2 rotation per pair of the last r channels."""
+    M = np.eye(c)
+    for j in range(r // 2):
+        a = pos * theta ** (-2.0 * j / r)
+        i = c - r + 2 * j
+        M[i:i + 2, i:i + 2] = [[math.cos(a), -math.sin(a)], [math.sin(a), math.cos(a)]]
+    return M
+
+
+def test_csa_queries_brute_force():
+    """The query side of a CSA layer (scores, top-k, attention) against loops
+    and explicit matrices: queries with fewer visible entries than k (every
+    entry selected, padded with -1) and with more."""
+    g = np.random.default_rng(41)
+    m, c, r, nh, nhI, cI, k, nwin = 4, 8, 4, 3, 2, 4, 6, 3
+    spec = L.Spec("csa", m=m, c=c, r=r, n_h=nh, n_hI=nhI, c_I=cI, top_k=k, n_win=nwin)
+    n_tok = 60
+    keys = g.standard_normal((n_tok // m, cI))
+    ents = g.standard_normal((n_tok // m, c))
+    win = g.standard_normal((n_tok, c))
+    pos = np.array([2, 9, 22, 23, 45, 59])               # V = 0, 2, 5, 6, 11, 15
+    q = g.standard_normal((len(pos), nh, c)).astype(np.float32)
+    qI = g.standard_normal((len(pos), nhI, cI)).astype(np.float32)
+    w = g.standard_normal((len(pos), nhI)).astype(np.float32)
+    sinks = g.standard_normal(nh)
+    gq = 1.0 + 0.1 * g.standard_normal(c)
+    sc, sel, o = L.csa_queries(spec, q, qI, w, pos, keys, ents, win, sinks, gq)
+    for i, t in enumerate(pos):
+        V = (t + 1) // m
+        ref = np.zeros(V)
+        for s in range(V):
+            for h in range(nhI):
+                ref[s] += float(w[i, h]) * max(0.0, float(np.dot(qI[i, h].astype(np.float64), keys[s])))
+        ref32 = ref.astype(np.float32)
+        assert np.array_equal(sc[i, :V], ref32) or np.allclose(sc[i, :V], ref32, rtol=2 ** -23, atol=0)
+        order = sorted(range(V), key=lambda s: (-float(ref32[s]), s))[:k]
+        want = sorted(order) + [-1] * (k - min(k, V))
+        assert list(sel[i]) == want
+        rows = [ents[s] for s in sorted(order)] + [win[j] for j in range(max(0, t - nwin + 1), t + 1)]
+        X = np.array(rows)
+        Rt = _rot_matrix(c, r, float(t), spec.theta)
+        for h in range(nh):
+            qh = q[i, h].astype(np.float64)
+            qn = Rt @ (gq * qh / math.sqrt(np.mean(qh * qh) + spec.eps))
+            z = X @ qn / math.sqrt(c)
+            zmax = max(z.max(), sinks[h])
+            p = np.exp(z - zmax) / (np.exp(z - zmax).sum() + math.exp(sinks[h] - zmax))
+            oh = Rt.T @ (p @ X)                               # rotated back at -t
+            assert np.allclose(o[i, h], oh, atol=1e-12, rtol=0)
