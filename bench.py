@@ -6,9 +6,10 @@ sparse_mqa per CSA layer; compress_kv, cache_append and hca_attention per HCA
 layer.  Inputs (caches, window rings, compressor tails, weights, queries) are
 synthetic, resident in HBM before timing starts, and the cache is rotated
 over several replicas so that the 256 MB last-level cache cannot hold a
-step's working set.  One HIP graph holds one step of every replica in
-rotation order (single-replica graphs time a remainder), and the graphs are
-replayed.  Prints one JSON line.
+step's working set.  One HIP graph holds two steps of every replica in
+rotation order, one per position buffer (each step's first compress call
+writes the next positions into the other buffer), single-step graphs time a
+remainder, and the graphs are replayed.  Prints one JSON line.
 
 Workloads:
   csa_decode_128k  16 requests x 131072 cached tokens, one CSA layer
@@ -145,7 +146,7 @@ def time_decode(name, steps, warmup, replicas=0, graph=True, fused_append=True):
 
     wd = workload_def(name)
     reps = replicas or wd["replicas"]
-    total_steps = warmup + steps + 64
+    total_steps = warmup + steps + 2 * reps + 64
     t_build = time.time()
     wls = [DecodeWorkload(wd["descs"], wd["d"], wd["n_req"], wd["ctx"], max_steps=total_steps,
                           rows=torch_rows(1000 + i), seed=i, fused_append=fused_append) for i in range(reps)]
@@ -153,41 +154,59 @@ def time_decode(name, steps, warmup, replicas=0, graph=True, fused_append=True):
     build_s = time.time() - t_build
 
     stream = torch.cuda.Stream()
+    # the order of steps: every replica at position buffer 0, then every
+    # replica at buffer 1 (each step's first layer writes the advanced
+    # positions into the other buffer), so 2 * reps steps return every
+    # replica to buffer 0
+    seq = [(r, p) for p in (0, 1) for r in range(reps)]
     with torch.cuda.stream(stream):
-        for i in range(4):
-            wls[i % reps].step()
+        for r, p in seq:
+            wls[r].step(parity=p)
         stream.synchronize()
 
-    # One graph holds one decode step of every replica, in rotation order, so
-    # a replay is `reps` consecutive steps (the launch of the graph is shared
-    # by them, as a serving loop that captures several steps would share it).
-    # Single-step graphs of each replica time the remainder when the step
-    # count is not a multiple of the replica count.
-    gph, gph_one = None, []
+    # One graph holds 2 * reps consecutive steps (the launch of the graph is
+    # shared by them, as a serving loop that captures several steps would
+    # share it); single-step graphs time the steps before and after whole
+    # replays.
+    gph, gph_one = None, {}
     if graph:
         gph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gph, stream=stream):
-            for wl in wls:
-                wl.step()
-        for wl in wls:
+            for r, p in seq:
+                wls[r].step(parity=p)
+        for r, p in seq:
             g1 = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g1, stream=stream):
-                wl.step()
-            gph_one.append(g1)
+                wls[r].step(parity=p)
+            gph_one[(r, p)] = g1
         torch.cuda.synchronize()
 
+    done = [0]
+
+    def one(i):
+        r, p = seq[i % len(seq)]
+        if gph is not None:
+            gph_one[(r, p)].replay()
+        else:
+            wls[r].step(parity=p)
+
     def run_steps(n):
-        for _ in range(n // reps):
+        L = len(seq)
+        while n > 0 and done[0] % L != 0:
+            one(done[0])
+            done[0] += 1
+            n -= 1
+        full, rem = divmod(n, L)
+        for _ in range(full):
             if gph is not None:
                 gph.replay()
             else:
-                for wl in wls:
-                    wl.step()
-        for j in range(n % reps):
-            if gph is not None:
-                gph_one[j].replay()
-            else:
-                wls[j].step()
+                for r, p in seq:
+                    wls[r].step(parity=p)
+        done[0] += full * L
+        for _ in range(rem):
+            one(done[0])
+            done[0] += 1
 
     with torch.cuda.stream(stream):
         run_steps(warmup)

@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 2
+#define CSA_ABI_VERSION 3
 
 typedef enum {
     CSA_OK = 0,
@@ -136,6 +136,11 @@ typedef struct {
     const int32_t* cu_new;         /* [n_req+1] prefix sums of new tokens, cu_new[0] = 0 */
     const int32_t* start_pos;      /* [n_req] position of each request's first new token */
     const int32_t* block_table;    /* [n_req*max_blocks] physical block ids (-1 = unused) */
+    int32_t* next_start_pos;       /* [n_req] or NULL.  csa_compress_kv and csa_compress_append write
+                                      start_pos[r] + (cu_new[r+1] - cu_new[r]) here (must not alias
+                                      start_pos); other calls ignore it.  A decode loop replayed as a
+                                      graph alternates two position buffers with it instead of advancing
+                                      positions with work of its own. */
 } csa_batch;
 
 /* Sizes the caller allocates.  [host] */
@@ -305,7 +310,8 @@ int csa_index_scores(void* stream, const csa_layer_desc* layer, const csa_batch*
  * g: the k largest of scores[g*ld + 0 .. n_valid[g]-1] (ties: the lower index
  * wins), written to out_idx[g*k ..] in ascending index order, padded with -1
  * when n_valid[g] < k.  Exact (integer radix selection on order-preserving
- * keys).  ws >= csa_workspace_size(CSA_OP_TOPK, n_rows, ld, k).
+ * keys).  ws >= csa_workspace_size(CSA_OP_TOPK, n_rows, ld, k).  n_valid[g]
+ * above ld is taken as ld (a row never reads past its ld columns).
  */
 int csa_topk_select(void* stream, int score_fmt, int n_rows, const void* scores, int ld,
                     const int32_t* n_valid, int k, int32_t* out_idx, void* ws, size_t ws_bytes);

@@ -38,7 +38,7 @@ class LayerDesc(ctypes.Structure):
 class Batch(ctypes.Structure):
     _fields_ = [("n_req", ctypes.c_int32), ("max_new", ctypes.c_int32), ("max_ctx", ctypes.c_int32),
                 ("max_blocks", ctypes.c_int32), ("cu_new", ctypes.c_void_p), ("start_pos", ctypes.c_void_p),
-                ("block_table", ctypes.c_void_p)]
+                ("block_table", ctypes.c_void_p), ("next_start_pos", ctypes.c_void_p)]
 
 
 class Sizes(ctypes.Structure):

@@ -244,6 +244,9 @@ int compress_args(const csa_layer_desc* layer, const csa_batch* batch, int n_tok
     a.max_entries = max_entries;
     a.out_win = out_win;
     a.max_new = batch->max_new;
+    REQUIRE(batch->next_start_pos == nullptr || (const int32_t*)batch->next_start_pos != batch->start_pos,
+            CSA_EINVAL, "next_start_pos must not alias start_pos");
+    a.next_pos = batch->next_start_pos;
     return CSA_OK;
 }
 
@@ -385,8 +388,13 @@ int csa_index_scores(void* stream, const csa_layer_desc* layer, const csa_batch*
     return hip_status(csa::launch_index((hipStream_t)stream, a, max_vis, batch->max_new), "index_scores launch");
 }
 
-int csa_topk_select(void* stream, int score_fmt, int n_rows, const void* scores, int ld, const int32_t* n_valid,
-                    int k, int32_t* out_idx, void* ws, size_t ws_bytes)
+}  // extern "C"
+
+namespace {
+
+// Validates topk_select's arguments; *need = the workspace it uses.
+int topk_args(int score_fmt, int n_rows, const void* scores, int ld, const int32_t* n_valid, int k,
+              const int32_t* out_idx, size_t* need)
 {
     REQUIRE(score_fmt == CSA_FMT_F32 || score_fmt == CSA_FMT_BF16, CSA_EINVAL, "score_fmt=%d", score_fmt);
     REQUIRE(n_rows >= 0 && ld >= 1, CSA_EINVAL, "n_rows=%d ld=%d", n_rows, ld);
@@ -395,7 +403,19 @@ int csa_topk_select(void* stream, int score_fmt, int n_rows, const void* scores,
             "NULL pointer argument");
     REQUIRE(csa::topk_supported(ld, k, score_fmt == CSA_FMT_BF16), CSA_EUNSUPPORTED,
             "rows of %d scores with k=%d exceed the two-stage selector's capacity", ld, k);
-    const size_t need = csa::topk_workspace(n_rows, ld, k, score_fmt == CSA_FMT_BF16);
+    *need = csa::topk_workspace(n_rows, ld, k, score_fmt == CSA_FMT_BF16);
+    return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int csa_topk_select(void* stream, int score_fmt, int n_rows, const void* scores, int ld, const int32_t* n_valid,
+                    int k, int32_t* out_idx, void* ws, size_t ws_bytes)
+{
+    size_t need = 0;
+    CHECK(topk_args(score_fmt, n_rows, scores, ld, n_valid, k, out_idx, &need));
     REQUIRE(ws_bytes >= need && (need == 0 || ws != nullptr), CSA_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes,
             need);
     return hip_status(csa::launch_topk((hipStream_t)stream, score_fmt == CSA_FMT_BF16, n_rows, scores, ld, n_valid, k,

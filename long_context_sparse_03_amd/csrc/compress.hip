@@ -423,6 +423,15 @@ CSA_DEV void merge_located(const CompressArgs& a, int e, int req, int ent, float
     }
 }
 
+// Workgroup 0 of the kernel after the projection writes every request's
+// next start position (the caller's position buffer for the following call).
+CSA_DEV void write_next_positions(const CompressArgs& a)
+{
+    if (a.next_pos == nullptr || blockIdx.x != 0) return;
+    for (int r = threadIdx.x; r < a.n_req; r += blockDim.x)
+        a.next_pos[r] = a.start_pos[r] + (a.cu_new[r + 1] - a.cu_new[r]);
+}
+
 CSA_DEV void merge_entry(const CompressArgs& a, int e, float* xs, float* red)
 {
     const int2 re = locate_entry(a, e);
@@ -433,6 +442,7 @@ __global__ __launch_bounds__(256) void merge_kernel(CompressArgs a)
 {
     __shared__ __attribute__((aligned(16))) float xs[512];
     __shared__ float red[16];
+    write_next_positions(a);
     merge_entry(a, blockIdx.x, xs, red);
 }
 
@@ -474,6 +484,7 @@ __global__ __launch_bounds__(256) void post_decode_kernel(CompressArgs a, int nm
 {
     __shared__ __attribute__((aligned(16))) float xs[512];
     __shared__ float red[16];
+    write_next_positions(a);
     if ((int)blockIdx.x < nm) {
         merge_entry(a, blockIdx.x, xs, red);
         return;
@@ -501,6 +512,7 @@ __global__ __launch_bounds__(256) void post_decode_append_kernel(CompressArgs a,
     __shared__ __attribute__((aligned(16))) float ks[128];
     __shared__ float red[16];
     __shared__ float s_sh[2];
+    write_next_positions(a);
     if ((int)blockIdx.x < nm) {
         const int2 re = locate_entry(a, blockIdx.x);
         if (re.x < 0) return;

@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S <= 4 ? 2 
         tok = 0;
     } else {
         req = find_request_block(a.cu_new, a.n_req, gq, cu_sh);
-        tok = gq - cu_sh[req];
+        tok = gq - (a.n_req < 1024 ? cu_sh[req] : a.cu_new[req]);   // cu_sh is filled only below 1024
     }
 
     // ---- prologue: position, block-table slice, query fragments and head
@@ -444,7 +444,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
         tok = 0;
     } else {
         req = find_request_block(a.cu_new, a.n_req, gq, cu_sh);
-        tok = gq - cu_sh[req];
+        tok = gq - (a.n_req < 1024 ? cu_sh[req] : a.cu_new[req]);   // cu_sh is filled only below 1024
     }
     // position, block-table slice (every block the workgroup can touch,
     // clamped to the row), query block of this wave's head tile and head

@@ -29,6 +29,7 @@ struct CompressArgs {
     int max_new;               // largest number of new tokens of one request
     int one_per_req;           // set by launch_compress: every request has exactly one new token
     int invariant;             // batch-invariant layer: the projection kernel does not depend on the row count
+    int32_t* next_pos;         // [n_req] or null: start_pos + new tokens, written by the post-projection kernel
 };
 
 // Y[M x groups*N] = per group g: X[:, g*K .. g*K+K) . W[g]^T, W [groups x N x K];

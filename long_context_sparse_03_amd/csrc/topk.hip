@@ -223,7 +223,8 @@ CSA_DEV void range_threshold(const uint32_t (&kr)[KPT], uint32_t lo, uint32_t hi
             rem_out = rem;
             return;
         }
-        hi = min(hi, nlo + ((1u << shift) - 1u));
+        // the selected bin's last key, without wrapping past 2^32 - 1
+        hi = nlo + min(hi - nlo, (1u << shift) - 1u);
         lo = nlo;
     }
 }
@@ -409,7 +410,7 @@ __global__ __launch_bounds__(NT) void topk_chunk_kernel(const void* scores, int 
     using KT = typename std::conditional<BF16, uint16_t, uint32_t>::type;
     constexpr int EPL = BF16 ? 8 : 4;
     const int row = blockIdx.y, ch = blockIdx.x;
-    const int V = n_valid[row];
+    const int V = min(n_valid[row], ld);                    // never past the row
     const int start = ch * chunk;
     const int n = max(0, min(V, start + chunk) - start);
     const int kk = min(k, n);
@@ -496,14 +497,14 @@ __global__ __launch_bounds__(NT) void topk_chunk_kernel(const void* scores, int 
 // candidates carry key 0, below every real key; candidates are in ascending
 // index order, so position order is index order.
 template <bool BF16, int KPT = (BF16 ? KPT16 : KPT32)>
-__global__ __launch_bounds__(TOPK_THREADS) void topk_merge_kernel(const int32_t* n_valid, int k, int n_chunks,
+__global__ __launch_bounds__(TOPK_THREADS) void topk_merge_kernel(const int32_t* n_valid, int ld, int k, int n_chunks,
                                                                   const uint32_t* cand_key, const int32_t* cand_idx,
                                                                   int32_t* out)
 {
     using KT = typename std::conditional<BF16, uint16_t, uint32_t>::type;
     __shared__ __attribute__((aligned(16))) KT keys[TOPK_THREADS * KPT];
     const int row = blockIdx.x;
-    const int V = n_valid[row];
+    const int V = min(n_valid[row], ld);
     const int kk = min(k, V);
     const int n = n_chunks * k;
     const uint32_t* ck = cand_key + (size_t)row * n;
@@ -639,9 +640,11 @@ hipError_t launch_topk(hipStream_t st, int score_bf16, int n_rows, const void* s
     else launch_chunks<false>(st, g1, chunk, scores, ld, n_valid, k, n_chunks, out, ck, ci);
     if (n_chunks > 1) {
         if (bf && (long)n_chunks * k <= TOPK_THREADS * MID_KPT)   // few candidates: 16 per thread
-            topk_merge_kernel<true, MID_KPT><<<n_rows, TOPK_THREADS, 0, st>>>(n_valid, k, n_chunks, ck, ci, out);
-        else if (bf) topk_merge_kernel<true><<<n_rows, TOPK_THREADS, 0, st>>>(n_valid, k, n_chunks, ck, ci, out);
-        else topk_merge_kernel<false><<<n_rows, TOPK_THREADS, 0, st>>>(n_valid, k, n_chunks, ck, ci, out);
+            topk_merge_kernel<true, MID_KPT><<<n_rows, TOPK_THREADS, 0, st>>>(n_valid, ld, k, n_chunks, ck, ci, out);
+        else if (bf && (long)n_chunks * k <= TOPK_THREADS * 24)   // e.g. 17 chunks of 1024 (rows just past 2^18)
+            topk_merge_kernel<true, 24><<<n_rows, TOPK_THREADS, 0, st>>>(n_valid, ld, k, n_chunks, ck, ci, out);
+        else if (bf) topk_merge_kernel<true><<<n_rows, TOPK_THREADS, 0, st>>>(n_valid, ld, k, n_chunks, ck, ci, out);
+        else topk_merge_kernel<false><<<n_rows, TOPK_THREADS, 0, st>>>(n_valid, ld, k, n_chunks, ck, ci, out);
     }
     return hipGetLastError();
 }

@@ -24,19 +24,24 @@ class BatchInfo:
     cu_new: torch.Tensor
     start_pos: torch.Tensor
     block_table: torch.Tensor
+    next_start_pos: torch.Tensor | None = None
     keep: list = field(default_factory=list)
 
 
 def make_batch(cu_new: torch.Tensor, start_pos: torch.Tensor, block_table: torch.Tensor, max_new: int,
-               max_ctx: int, n_tokens: int) -> BatchInfo:
+               max_ctx: int, n_tokens: int, next_start_pos: torch.Tensor | None = None) -> BatchInfo:
     """Wrap int32 device tensors (cu_new [n_req+1], start_pos [n_req],
-    block_table [n_req, max_blocks]) and host bounds into a csa_batch."""
+    block_table [n_req, max_blocks], optionally next_start_pos [n_req]) and
+    host bounds into a csa_batch."""
     assert cu_new.dtype == torch.int32 and start_pos.dtype == torch.int32 and block_table.dtype == torch.int32
     cu_new, start_pos, block_table = cu_new.contiguous(), start_pos.contiguous(), block_table.contiguous()
+    if next_start_pos is not None:
+        assert next_start_pos.dtype == torch.int32 and next_start_pos.is_contiguous()
     b = Batch(n_req=start_pos.numel(), max_new=int(max_new), max_ctx=int(max_ctx),
               max_blocks=block_table.shape[1], cu_new=cu_new.data_ptr(), start_pos=start_pos.data_ptr(),
-              block_table=block_table.data_ptr())
-    return BatchInfo(b, int(n_tokens), cu_new, start_pos, block_table)
+              block_table=block_table.data_ptr(),
+              next_start_pos=None if next_start_pos is None else next_start_pos.data_ptr())
+    return BatchInfo(b, int(n_tokens), cu_new, start_pos, block_table, next_start_pos)
 
 
 class LayerState:

@@ -7,8 +7,10 @@ produces, so the stored bytes follow the library's own formats.  One decode
 step runs, for every layer in order, the library's calls for one new token
 per request (compress_append, or compress_kv and cache_append); all buffers
 are allocated up front, so a step allocates nothing and can be captured in a
-HIP graph (positions live in device memory and the step advances them
-itself).
+HIP graph.  Positions live in two device buffers that alternate: a step reads
+one, and its first layer's compress call writes the advanced positions into
+the other (csa_batch.next_start_pos), so no other work advances them; a graph
+holds steps of both parities.
 """
 from __future__ import annotations
 
@@ -108,8 +110,14 @@ class DecodeWorkload:
     def _alloc_step_buffers(self):
         n, dev = self.n_req, self.dev
         self.cu_new = torch.arange(n + 1, dtype=torch.int32, device=dev)
-        self.pos = torch.full((n,), self.ctx, dtype=torch.int32, device=dev)
-        self.bi = make_batch(self.cu_new, self.pos, self.block_table, 1, self.max_ctx, n)
+        # two position buffers: a step of parity p reads pos[p]; its first
+        # layer's compress call writes the next positions into pos[1 - p]
+        self.pos = [torch.full((n,), self.ctx, dtype=torch.int32, device=dev) for _ in range(2)]
+        self.bi_adv = [make_batch(self.cu_new, self.pos[p], self.block_table, 1, self.max_ctx, n,
+                                  next_start_pos=self.pos[1 - p]) for p in range(2)]
+        self.bis = [make_batch(self.cu_new, self.pos[p], self.block_table, 1, self.max_ctx, n) for p in range(2)]
+        self.parity = 0
+        self.bi = self.bis[0]
         self.H = torch.randn((n, self.d), device=dev).to(torch.bfloat16)
         self.bufs = []
         for st, P in self.layers:
@@ -141,19 +149,22 @@ class DecodeWorkload:
             self.bufs.append(b)
 
     # ------------------------------------------------------------------
-    def layer_calls(self, li: int, hooks=None):
-        """The library calls of layer li for one decode token per request."""
+    def layer_calls(self, li: int, hooks=None, parity: int = 0):
+        """The library calls of layer li for one decode token per request, at
+        the positions of buffer `parity` (layer 0 also advances them into the
+        other buffer)."""
         st, P = self.layers[li]
         b = self.bufs[li]
-        desc, n, bi = st.desc, self.n_req, self.bi
+        desc, n, bi = st.desc, self.n_req, self.bis[parity]
+        bic = self.bi_adv[parity] if li == 0 else bi
         s = None
         keys = b["keys"] if st.is_csa else None
         if self.fused_append:
-            abi.compress_append(desc, bi.batch, n, self.d, self.H, P["W"], P["W_idx"], P["B_a"], P["B_b"],
+            abi.compress_append(desc, bic.batch, n, self.d, self.H, P["W"], P["W_idx"], P["B_a"], P["B_b"],
                                 P["B_a_idx"], P["B_b_idx"], P["gamma"], st.state, b["entries"], keys, b["meta"],
                                 b["count"], n, b["win"], st.kv, st.idx, b["ws_c"], stream=s)
         else:
-            abi.compress_kv(desc, bi.batch, n, self.d, self.H, P["W"], P["W_idx"], P["B_a"], P["B_b"],
+            abi.compress_kv(desc, bic.batch, n, self.d, self.H, P["W"], P["W_idx"], P["B_a"], P["B_b"],
                             P["B_a_idx"], P["B_b_idx"], P["gamma"], st.state, b["entries"], keys, b["meta"],
                             b["count"], n, b["win"], b["ws_c"], stream=s)
             abi.cache_append(desc, bi.batch, n, b["entries"], keys, b["meta"], b["count"], n, b["win"], st.kv,
@@ -176,11 +187,15 @@ class DecodeWorkload:
         """Only the index_scores call of CSA layer li (same buffers as the step)."""
         st, _ = self.layers[li]
         b = self.bufs[li]
-        abi.index_scores(st.desc, self.bi.batch, self.n_req, b["qI"], b["w"], st.idx, b["scores"], b["ld"],
-                         b["n_valid"])
+        abi.index_scores(st.desc, self.bis[self.parity].batch, self.n_req, b["qI"], b["w"], st.idx, b["scores"],
+                         b["ld"], b["n_valid"])
 
-    def step(self, hooks=None):
-        """One decode step: every layer, then the positions advance by one."""
+    def step(self, hooks=None, parity: int | None = None):
+        """One decode step through every layer at the positions of buffer
+        `parity` (default: the workload's current one, which then flips); the
+        first layer writes the next positions into the other buffer."""
+        p = self.parity if parity is None else parity
         for li in range(len(self.layers)):
-            self.layer_calls(li, hooks[li] if hooks else None)
-        self.pos.add_(1)
+            self.layer_calls(li, hooks[li] if hooks else None, parity=p)
+        if parity is None:
+            self.parity ^= 1

@@ -24,7 +24,7 @@ def test_header_symbols_exported():
     L = P.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert P.abi_version() == 2
+    assert P.abi_version() == 3
 
 
 def test_sizes_follow_layouts():
@@ -162,3 +162,13 @@ def test_compress_append_argument_checks():
     b.max_new = 129
     assert L.csa_compress_append(None, ctypes.byref(d), ctypes.byref(b), *args) == -1
     assert b"win_cap" in L.csa_last_error()
+
+
+def test_next_start_pos_must_not_alias_start_pos():
+    L = P.lib()
+    d = presets.csa_flash_decode()
+    b = abi.Batch(n_req=1, max_new=1, max_ctx=1024, max_blocks=8, cu_new=8, start_pos=64, block_table=8,
+                  next_start_pos=64)
+    args = [1, 4096, 8, 8, 8, 8, 8, 8, 8, 8, 8, 8, 8, 8, 8, 1, 8, 8, 8, 8, 1 << 30]
+    assert L.csa_compress_append(None, ctypes.byref(d), ctypes.byref(b), *args) == -1
+    assert b"alias" in L.csa_last_error()

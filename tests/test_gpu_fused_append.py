@@ -80,3 +80,32 @@ def test_compress_append_matches_separate_calls(case):
         assert torch.equal(a[2][:cnt], b[2][:cnt]), f"{what}: meta"
         assert torch.equal(a[4][:T].view(torch.int32), b[4][:T].view(torch.int32)), f"{what}: window rows"
     print(f"  {case}: caches and outputs identical after every call", flush=True)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_next_start_pos(fused):
+    """csa_batch.next_start_pos receives start_pos + new tokens of every
+    request (idle ones included), from the decode kernel (at most one new token
+    each) and from the general path."""
+    from long_context_sparse_03_amd.layer import make_batch
+    from harness import i32
+    desc = presets.csa_flash_decode(win_cap=512)
+    g = synth.rng(320)
+    P = Params(g, desc, 1024)
+    bt = np.arange(3 * 8, dtype=np.int32).reshape(3, 8)
+    st = LayerState(desc, 3, bt.size)
+    for start, n_new in (([40, 9, 63], [1, 0, 1]), ([41, 9, 64], [5, 0, 2])):
+        n_new = np.asarray(n_new)
+        cu = i32(np.concatenate([[0], np.cumsum(n_new)]))
+        sp = i32(start)
+        nxt = torch.full((3,), -1, dtype=torch.int32, device="cuda")
+        T = int(n_new.sum())
+        bi = make_batch(cu, sp, i32(bt), int(n_new.max()), int(max(np.asarray(start) + n_new)), T,
+                        next_start_pos=nxt)
+        H = to_dev(synth.to_bf16_values(synth.normal(g, (T, 1024))), torch.bfloat16)
+        dv = P.dev
+        call = st.compress_append if fused else st.compress
+        call(bi, T, H, dv["W"], dv["W_I"], dv["Ba"], dv["Bb"], dv["BaI"], dv["BbI"], dv["gamma"], 4)
+        torch.cuda.synchronize()
+        assert nxt.cpu().tolist() == list(np.asarray(start) + n_new)
+        assert sp.cpu().tolist() == list(start)

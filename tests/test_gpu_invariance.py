@@ -7,16 +7,22 @@ caches filled the same way: once alone, once with other requests in every
 call (longer and shorter contexts, several new tokens per call, so the
 calls take other kernels and split counts).  Every output of A is compared
 bit for bit: compressed entries, indexer keys, window rows, index scores,
-selected entries and the attention output.
+selected entries and the attention output.  Request 0's outputs are also
+checked against the oracle (every call, a sample of the prefill chunk's
+queries), so the flagged kernels (fixed attention splits with the ordered
+merge, the small-row projection) are held to the same tolerances as the
+unflagged ones.
 """
 import numpy as np
 import pytest
 import torch
 
 import synth
+from harness import assert_close, spec_of, tol_of
 from long_context_sparse_03_amd import abi, presets
 from long_context_sparse_03_amd.layer import LayerState
-from test_gpu_layers import Params, gpu_layer_call
+from oracle import layer as OL
+from test_gpu_layers import Params, QueryOracle, compare_csa_queries, gpu_layer_call
 
 pytestmark = pytest.mark.gpu
 
@@ -73,6 +79,53 @@ def _run(desc, P, reqs, calls, n_blocks):
     return outs
 
 
+def oracle_check_request(desc, P, x, calls, outs, max_queries=48):
+    """Outputs of one request against the oracle.  x: the request's token
+    inputs (H, q, qI, w); calls: (first position, count) of each of its calls
+    from position 0; outs: per call its outputs (entries and keys the call
+    completed, window rows, selections, scores, attention output) or None
+    (not checked).  The cache state a call's queries see is the oracle's
+    storage of every entry completed up to and including that call, appended
+    call by call (the FP8 block-scale rule applies per call).  At most
+    max_queries queries of a call are checked (evenly spaced, first and last
+    included)."""
+    spec = spec_of(desc)
+    m, csa = desc.m, desc.kind == abi.KIND_CSA
+    n = calls[-1][0] + calls[-1][1]
+    E, K, R = OL.compress_layer(spec, x["H"][:n], P.W, P.Ba, P.Bb, P.gamma, P.W_I, P.BaI, P.BbI)
+    tol = tol_of(desc)
+    ecalls = []
+    for ci, ((s, c), o) in enumerate(zip(calls, outs)):
+        i0, i1 = s // m, (s + c) // m
+        if i1 > i0:
+            ecalls.append((i0, i1 - i0))
+        if o is None or c == 0:
+            continue
+        if i1 > i0:
+            assert_close(o["entries"], E[i0:i1], 1e-3, f"call {ci} entries")
+            if csa:
+                assert_close(o["keys"], K[i0:i1], 1e-3, f"call {ci} keys")
+        assert_close(o["win"], R[s:s + c], 1e-3, f"call {ci} window rows")
+        _, edeq = OL.store_entries(spec, E[:i1].astype(np.float32), ecalls)
+        wdeq = OL.round_rows(spec.win_fmt, R[:s + c].astype(np.float32))
+        rows = np.arange(c) if c <= max_queries else np.unique(np.linspace(0, c - 1, max_queries).astype(int))
+        pos = s + rows
+        if csa:
+            kdeq = OL.store_keys(spec, K[:i1].astype(np.float32))[1]
+            qo = QueryOracle(spec, x["q"][pos], x["qI"][pos], x["w"][pos], pos, kdeq, edeq, wdeq, P.sinks,
+                             P.q_gamma)
+            V = (pos + 1) // m
+            sc = np.full((len(rows), max(1, int(V.max()))), np.nan, np.float32)
+            for j, rj in enumerate(rows):
+                sc[j, :V[j]] = o["scores"][rj]
+            sub = {"scores": sc, "sel": o["sel"][rows], "out": o["out"][rows]}
+            e, msame = compare_csa_queries(desc, sub, 0, qo, f"call {ci}")
+        else:
+            want = OL.attend(spec, x["q"][pos], P.q_gamma, pos, edeq, wdeq, P.sinks)
+            e = assert_close(o["out"][rows], want, tol, f"call {ci} attention")
+        print(f"  oracle: call {ci} ({len(rows)} of {c} queries) attention err {e:.2e}", flush=True)
+
+
 def _same(a, b, what):
     if isinstance(a, list):
         for j, (x, y) in enumerate(zip(a, b)):
@@ -109,3 +162,4 @@ def test_batch_invariant_request(kind):
         for key in x:
             _same(x[key], y[key], f"call {i} {key}")
     print(f"  request 0 bit-identical over {len(a)} calls", flush=True)
+    oracle_check_request(desc, P, reqs[0], [(s, c) for [(_, s, c)] in alone], a)

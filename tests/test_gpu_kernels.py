@@ -194,6 +194,26 @@ INDEX_CASES = {
 }
 
 
+def check_score_row(desc, a, b, qdq, kdeq, w, what):
+    """GPU scores a against the oracle's b for one query: fp32 scores to
+    1e-4; bf16 scores within one bf16 step of b plus the worst-case error of
+    fp32 sums over the channels and the heads, (c_I + n_hI) 2^-24
+    sum_h |w_h| sum_c |q_hc k_c| on the dequantised operands (scores of heads
+    with weights of both signs can cancel far below the size of their
+    terms), and at least 97 % of them identical."""
+    if desc.score_fmt != abi.ACT_BF16:
+        assert_close(a, b, 1e-4, f"scores {what}")
+        return
+    V = len(b)
+    qa = np.abs(np.asarray(qdq, np.float64)).reshape(desc.n_idx_heads, -1)
+    ka = np.abs(np.asarray(kdeq[:V], np.float64))
+    acc = (desc.c_idx + desc.n_idx_heads) * 2.0 ** -24 * (np.abs(np.asarray(w, np.float64)) @ (qa @ ka.T))
+    ulp = np.maximum(np.abs(b), 1e-30) * 2.0 ** -7
+    bad = np.abs(a - b) > ulp + acc + 1e-30
+    assert not bad.any(), f"{what}: {bad.sum()} scores off by more than one bf16 step"
+    assert V == 0 or np.mean(a == b) > 0.97
+
+
 def _fill_keys(st, desc, bt, E_per_req, g):
     keys = [synth.normal(g, (E, desc.c_idx)) for E in E_per_req]
     ents = [synth.normal(g, (E, desc.c)) for E in E_per_req]
@@ -244,22 +264,55 @@ def test_index_scores(name):
         for j in range(n_new[r]):
             V = (pos[r][j] + 1) // desc.m
             assert gv[row + j] == V
-            a, b = got[row + j, :V], want[j, :V]
-            if spec.score_fmt == "bf16":
-                # one bf16 step, plus the worst-case error of fp32 sums over
-                # the channels and the heads (scores of heads with weights of
-                # both signs can cancel far below the size of their terms)
-                qa = np.abs(np.asarray(qdq[j], np.float64)).reshape(desc.n_idx_heads, -1)
-                ka = np.abs(np.asarray(kdeq[:V], np.float64))
-                acc = (desc.c_idx + desc.n_idx_heads) * 2.0 ** -24 * (np.abs(w[row + j]) @ (qa @ ka.T))
-                ulp = np.maximum(np.abs(b), 1e-30) * 2.0 ** -7
-                bad = np.abs(a - b) > ulp + acc + 1e-30
-                assert not bad.any(), f"row {row + j}: {bad.sum()} scores off by more than one bf16 step"
-                assert V == 0 or np.mean(a == b) > 0.97
-            else:
-                assert_close(a, b, 1e-4, f"scores row {row + j}")
+            check_score_row(desc, got[row + j, :V], want[j, :V], qdq[j], kdeq[:V], w[row + j], f"row {row + j}")
             assert np.all(np.isnan(got[row + j, V:V + 8]))
         row += n_new[r]
+
+
+def test_index_scores_many_requests():
+    """More than 1024 requests with uneven new-token counts (0 to 3 per
+    request): the decode launches look each query's request up in global
+    memory (the LDS copy of cu_new holds at most 1024 requests); every score
+    of a sample of requests against the oracle, bf16 and MXFP4 keys."""
+    for desc in (presets.csa_flash_decode(), presets.csa_pro(idx_fmt=abi.IDX_MXFP4)):
+        spec = spec_of(desc)
+        _flush(f"index_scores 1100 requests idx_fmt={desc.idx_fmt}")
+        g = synth.rng(108)
+        n_req = 1100
+        n_new = g.integers(0, 4, n_req)
+        n_new[1050] = 3
+        E = g.integers(1, 64, n_req)                 # entries cached per request (at most 2 blocks)
+        start = [4 * int(e) + int(g.integers(0, 4)) for e in E]
+        epb = desc.block_tokens // desc.m
+        bt = synth.block_table(g, n_req, 3)
+        st = LayerState(desc, n_req, bt.size)
+        E_all = [(s + n) // desc.m for s, n in zip(start, n_new)]
+        ents, keys = _fill_keys(st, desc, bt, E_all, g)
+        bi = batch(start, n_new, bt)
+        T = int(n_new.sum())
+        qd = synth.queries(g, T, 1, 1, desc.n_idx_heads, desc.c_idx)
+        qI, w = synth.to_bf16_values(qd["qI"]), qd["w"]
+        ld = 72
+        scores = torch.full((T, ld), float("nan"), dtype=torch.bfloat16, device="cuda")
+        nvalid = torch.zeros(T, dtype=torch.int32, device="cuda")
+        st.index(bi, T, to_dev(qI, torch.bfloat16), to_dev(w), scores, ld, nvalid)
+        torch.cuda.synchronize()
+        got = scores.float().cpu().numpy()
+        gv = nvalid.cpu().numpy()
+        cu = np.concatenate([[0], np.cumsum(n_new)])
+        for r in list(range(0, n_req, 37)) + [1023, 1024, 1050, n_req - 1]:
+            if n_new[r] == 0:
+                continue
+            pos = np.arange(start[r], start[r] + n_new[r])
+            _, kdeq = OL.store_keys(spec, keys[r])
+            qdq = OL.quantize_index_queries(spec, qI[cu[r]:cu[r + 1]])
+            want = OL.scores(spec, qdq, w[cu[r]:cu[r + 1]], pos, kdeq)
+            for j in range(n_new[r]):
+                V = (pos[j] + 1) // desc.m
+                assert gv[cu[r] + j] == V
+                check_score_row(desc, got[cu[r] + j, :V], want[j, :V], qdq[j], kdeq[:V], w[cu[r] + j],
+                                f"request {r} token {j}")
+                assert np.all(np.isnan(got[cu[r] + j, V:]))
 
 
 def test_index_prefill_matches_decode():
@@ -304,12 +357,16 @@ ATTN_CASES = {
     "fp8_sparse_64h": (presets.csa_flash_decode(), [[40000, 1], [9000, 1], [131072, 1], [100, 1]]),
     "fp8_sparse_128h_prefill": (presets.csa_pro(win_cap=512), [[5000, 33]]),
     "fp8_hca_128h": (presets.hca_pro(), [[70000, 1], [20000, 1]]),
+    # sinks of -inf (the ordinary softmax) and queries that see no compressed
+    # entry yet (V = 0: window rows only; V = 1), 128 heads, FP8 entries
+    "fp8_sparse_128h_sink_neg_inf": (presets.csa_pro(), [[0, 1], [2, 1], [3, 1], [130, 1], [5000, 2]], "-inf"),
 }
 
 
 @pytest.mark.parametrize("name", list(ATTN_CASES))
 def test_attention(name):
-    desc, reqs = ATTN_CASES[name]
+    desc, reqs = ATTN_CASES[name][:2]
+    sink_mode = ATTN_CASES[name][2] if len(ATTN_CASES[name]) > 2 else None
     spec = spec_of(desc)
     _flush(f"attention {name}")
     g = synth.rng(104)
@@ -336,6 +393,8 @@ def test_attention(name):
     if desc.act_fmt == abi.ACT_BF16:
         q = synth.to_bf16_values(q)
     sinks = synth.sinks(g, desc.n_heads)
+    if sink_mode == "-inf":
+        sinks = np.full(desc.n_heads, -np.inf, np.float32)
     gq = synth.normal(g, (desc.c,)) * 0.1 + 1.0
     sel = None
     if desc.kind == abi.KIND_CSA:

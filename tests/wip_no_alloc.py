@@ -1,0 +1,53 @@
+"""The allocation-free top-k (csa_topk_select_static, a static scratch array
+inside the library) against csa_topk_select with a caller workspace: same
+selections, two calls in a row, the second with a smaller input, bf16 and
+fp32 scores, rows long enough to take the two-stage path that uses the
+scratch."""
+import numpy as np
+import pytest
+import torch
+
+from long_context_sparse_03_amd import abi
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(seed, n_rows, ld, fmt, k):
+    g = np.random.default_rng(seed)
+    sc = np.round(g.standard_normal((n_rows, ld)) * 40).astype(np.float32)       # many ties
+    nv = g.integers(0, ld + 1, n_rows).astype(np.int32)
+    nv[0] = ld
+    if n_rows > 1:
+        nv[1] = min(k - 3, ld)
+    dt = torch.bfloat16 if fmt == abi.ACT_BF16 else torch.float32
+    return torch.from_numpy(sc).to("cuda").to(dt), torch.from_numpy(nv).to("cuda")
+
+
+@pytest.mark.parametrize("fmt", [abi.ACT_BF16, abi.ACT_F32])
+def test_static_scratch_topk_matches_workspace_topk(fmt):
+    calls = [(16, 100_000, 512), (5, 60_000, 300)] if fmt == abi.ACT_BF16 else [(12, 50_000, 512),
+                                                                               (3, 30_000, 64)]
+    for i, (n_rows, ld, k) in enumerate(calls):
+        print(f"static top-k fmt={fmt} call {i}: rows={n_rows} ld={ld} k={k}", flush=True)
+        sc, nv = _case(100 + i, n_rows, ld, fmt, k)
+        need = abi.workspace_size(_desc(fmt, k), abi.OP_TOPK, n_rows, ld, k)
+        assert 0 < need <= 8 << 20                      # two-stage: the scratch is used
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        ref = torch.full((n_rows, k), -7, dtype=torch.int32, device="cuda")
+        got = torch.full((n_rows, k), -9, dtype=torch.int32, device="cuda")
+        abi.topk_select(fmt, n_rows, sc, ld, nv, k, ref, ws)
+        abi.topk_select_static(fmt, n_rows, sc, ld, nv, k, got)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref)
+        # the reference selection is itself exact: ascending, -1 padded, right count
+        r = ref.cpu().numpy()
+        for row in range(n_rows):
+            cnt = min(k, int(nv[row]))
+            assert np.all(np.diff(r[row, :cnt]) > 0) and np.all(r[row, cnt:] == -1)
+
+
+def _desc(fmt, k):
+    from long_context_sparse_03_amd import presets
+    d = presets.csa_flash_decode() if fmt == abi.ACT_BF16 else presets.tiny_csa_fp32()
+    d.top_k = k
+    return d
