@@ -317,6 +317,25 @@ int csa_topk_select(void* stream, int score_fmt, int n_rows, const void* scores,
                     const int32_t* n_valid, int k, int32_t* out_idx, void* ws, size_t ws_bytes);
 
 /*
+ * csa_topk_select without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and errors as
+ * csa_topk_select; the candidate lists of the two-stage selection (rows
+ * longer than one workgroup's share) live in a static device array of
+ * CSA_STATIC_TOPK_SCRATCH_BYTES inside the library, one per GPU, held until
+ * the process ends.  A call whose csa_workspace_size(CSA_OP_TOPK, n_rows, ld,
+ * k) exceeds it returns CSA_EWORKSPACE before anything runs.  The array's
+ * address on the current device is looked up on the first call on that
+ * device.  Every call on a GPU shares that GPU's array (it keeps the last
+ * call's candidates; nothing in it needs to start at zero): calls that
+ * overlap on one GPU (other streams, unordered host threads) race, so the
+ * caller must order them.  Allocates nothing.
+ */
+#define CSA_STATIC_TOPK_SCRATCH_BYTES (8u << 20)
+int csa_topk_select_static(void* stream, int score_fmt, int n_rows, const void* scores, int ld,
+                           const int32_t* n_valid, int k, int32_t* out_idx);
+
+/*
  * a5: sparse shared-KV MQA with window and sink ([DD] §1.2 Step 2, §1.4
  * table and sink equation; [YP] eq. (9)).  For each new token t (row g) and
  * head h: q = RoPE_t(RMSNorm_gamma_q(q_raw[g][h])); rows X = the entries

@@ -70,6 +70,7 @@ def lib():
             "csa_compress_append": (I, [P, LP, BP, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, I, P, P, P, P, Z]),
             "csa_index_scores": (I, [P, LP, BP, I, P, P, P, P, I, P]),
             "csa_topk_select": (I, [P, I, I, P, I, P, I, P, P, Z]),
+            "csa_topk_select_static": (I, [P, I, I, P, I, P, I, P]),
             "csa_sparse_mqa": (I, [P, LP, BP, I, P, P, P, P, P, P, P, P, Z]),
             "csa_hca_attention": (I, [P, LP, BP, I, P, P, P, P, P, P, P, Z]),
             "csa_linear": (I, [P, I, I, I, I, I, P, P, P]),
@@ -157,6 +158,12 @@ def topk_select(score_fmt, n_rows, scores, ld, n_valid, k, out_idx, ws, stream=N
     _check("csa_topk_select", lib().csa_topk_select(
         _stream(stream), score_fmt, n_rows, _ptr(scores), ld, _ptr(n_valid), k, _ptr(out_idx), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size()))
+
+
+def topk_select_static(score_fmt, n_rows, scores, ld, n_valid, k, out_idx, stream=None):
+    """topk_select with the library's static scratch array instead of a workspace."""
+    _check("csa_topk_select_static", lib().csa_topk_select_static(
+        _stream(stream), score_fmt, n_rows, _ptr(scores), ld, _ptr(n_valid), k, _ptr(out_idx)))
 
 
 def sparse_mqa(desc, batch, n_tokens, q, q_gamma, sel, kv_cache, state, sinks, out, ws, stream=None):

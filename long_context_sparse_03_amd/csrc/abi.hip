@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/csa.h"
 #include "kernels.hpp"
 
@@ -390,6 +392,13 @@ int csa_index_scores(void* stream, const csa_layer_desc* layer, const csa_batch*
 
 }  // extern "C"
 
+// The allocation-free top-k keeps its candidate lists in this file-scope
+// device array (one copy per GPU, held until the process ends).  Host code
+// never uses the array's name as an address: the device address of each
+// GPU's copy is looked up once per device (hipGetSymbolAddress with that
+// device current) and kept in scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[CSA_STATIC_TOPK_SCRATCH_BYTES];
+
 namespace {
 
 // Validates topk_select's arguments; *need = the workspace it uses.
@@ -407,6 +416,28 @@ int topk_args(int score_fmt, int n_rows, const void* scores, int ld, const int32
     return CSA_OK;
 }
 
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[MAX_DEVICES] = {};
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device).
+int scratch_address(void** out)
+{
+    int dev = -1;
+    CHECK(hip_status(hipGetDevice(&dev), "hipGetDevice"));
+    REQUIRE(dev >= 0 && dev < MAX_DEVICES, CSA_EUNSUPPORTED, "device %d", dev);
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        CHECK(hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"));
+        REQUIRE(p != nullptr, CSA_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return CSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -421,6 +452,22 @@ int csa_topk_select(void* stream, int score_fmt, int n_rows, const void* scores,
     return hip_status(csa::launch_topk((hipStream_t)stream, score_fmt == CSA_FMT_BF16, n_rows, scores, ld, n_valid, k,
                                        out_idx, ws, ld),
                       "topk_select launch");
+}
+
+int csa_topk_select_static(void* stream, int score_fmt, int n_rows, const void* scores, int ld,
+                           const int32_t* n_valid, int k, int32_t* out_idx)
+{
+    size_t need = 0;
+    CHECK(topk_args(score_fmt, n_rows, scores, ld, n_valid, k, out_idx, &need));
+    REQUIRE(need <= (size_t)CSA_STATIC_TOPK_SCRATCH_BYTES, CSA_EWORKSPACE,
+            "candidate lists of %zu bytes exceed the static scratch of %zu bytes", need,
+            (size_t)CSA_STATIC_TOPK_SCRATCH_BYTES);
+    if (n_rows == 0) return CSA_OK;
+    void* ws = nullptr;
+    if (need > 0) CHECK(scratch_address(&ws));
+    return hip_status(csa::launch_topk((hipStream_t)stream, score_fmt == CSA_FMT_BF16, n_rows, scores, ld, n_valid, k,
+                                       out_idx, ws, ld),
+                      "topk_select_static launch");
 }
 
 static int attention_common(void* stream, const csa_layer_desc* layer, const csa_batch* batch, int n_tokens,

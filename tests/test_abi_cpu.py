@@ -164,6 +164,20 @@ def test_compress_append_argument_checks():
     assert b"win_cap" in L.csa_last_error()
 
 
+def test_static_topk_rejects_oversize_before_launch():
+    """csa_topk_select_static refuses inputs whose candidate lists exceed its
+    static scratch, before any HIP call (so it is checked here without a GPU)."""
+    L = P.lib()
+    fake = ctypes.c_void_p(0x1000)
+    # 2048 rows of 262,144 bf16 scores, k = 1024: far more candidates than 8 MiB
+    rc = L.csa_topk_select_static(None, abi.ACT_BF16, 2048, fake, 262144, fake, 1024, fake)
+    assert rc == -3 and b"static scratch" in L.csa_last_error()
+    rc = L.csa_topk_select_static(None, 7, 1, fake, 10, fake, 4, fake)
+    assert rc == -1
+    rc = L.csa_topk_select_static(None, abi.ACT_BF16, 1, fake, 10, fake, 4096, fake)
+    assert rc == -2
+
+
 def test_next_start_pos_must_not_alias_start_pos():
     L = P.lib()
     d = presets.csa_flash_decode()
