@@ -43,7 +43,7 @@ def workload_def(name: str):
     if name == "hybrid_decode_1m":
         return dict(descs=[presets.csa_pro(idx_fmt=abi.IDX_MXFP4), presets.hca_pro(),
                            presets.csa_pro(idx_fmt=abi.IDX_MXFP4), presets.hca_pro()],
-                    d=presets.D_PRO, n_req=4, ctx=1 << 20, replicas=2)
+                    d=presets.D_PRO, n_req=4, ctx=1 << 20, replicas=4)
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -77,42 +77,154 @@ def algorithmic_bytes(wd) -> dict:
     return tot
 
 
+def _oracle_spec(desc):
+    from oracle import layer as OL
+    from long_context_sparse_03_amd import abi
+    kv = {abi.KV_F32: "f32", abi.KV_BF16: "bf16", abi.KV_FP8: "fp8"}[desc.kv_fmt]
+    idx = {abi.IDX_F32: "f32", abi.IDX_BF16: "bf16", abi.IDX_MXFP4: "mxfp4"}[desc.idx_fmt]
+    fmt = {abi.ACT_F32: "f32", abi.ACT_BF16: "bf16"}
+    return OL.Spec("csa" if desc.kind == abi.KIND_CSA else "hca", m=desc.m, c=desc.c, r=desc.rope_dim,
+                   n_h=desc.n_heads, n_hI=desc.n_idx_heads, c_I=desc.c_idx, top_k=desc.top_k, n_win=desc.n_win,
+                   kv_fmt=kv, idx_fmt=idx, score_fmt=fmt[desc.score_fmt], win_fmt=fmt[desc.act_fmt])
+
+
+def _oracle_cache(spec, g, E, synth, OL):
+    """Dequantised synthetic entries (and CSA keys) as the oracle stores them."""
+    ents = synth.normal(g, (E, spec.c))
+    _, edeq = OL.store_entries(spec, ents, [(i, min(spec.epb, E - i)) for i in range(0, E, spec.epb)])
+    kdeq = OL.store_keys(spec, synth.normal(g, (E, spec.c_I)))[1] if spec.kind == "csa" else None
+    return edeq, kdeq
+
+
 def cpu_baseline(wd, n_tok: int, seed: int = 11) -> dict:
-    """The oracle (fp64, as it stands) on a bounded sample of the workload:
-    n_tok consecutive decode tokens of one request of the first CSA layer,
-    through the projection of the new tokens, index scores, top-k and
-    attention (the oracle runs a request's queries in parallel)."""
+    """The oracle (fp64, as it stands) on a bounded sample of a decode
+    workload.  One CSA layer (128K): n_tok consecutive decode tokens of one
+    request through the projection of the new tokens, index scores, top-k
+    and attention (the oracle runs a request's queries in parallel).  The
+    hybrid 1M workload: one decode step of one request through all four
+    layers (projection, then index scores, top-k and attention for CSA,
+    dense attention for HCA)."""
     import oracle as O
     from oracle import layer as OL
     import synth
     from long_context_sparse_03_amd import abi
-    desc = next(d for d in wd["descs"] if d.kind == abi.KIND_CSA)
-    spec = OL.Spec("csa", m=desc.m, c=desc.c, r=desc.rope_dim, n_h=desc.n_heads, n_hI=desc.n_idx_heads,
-                   c_I=desc.c_idx, top_k=desc.top_k, n_win=desc.n_win, kv_fmt="fp8",
-                   idx_fmt={abi.IDX_BF16: "bf16", abi.IDX_MXFP4: "mxfp4"}[desc.idx_fmt], score_fmt="bf16",
-                   win_fmt="bf16")
     g = synth.rng(seed)
     ctx, d = wd["ctx"], wd["d"]
-    E = (ctx + n_tok) // desc.m
-    W = synth.weights(g, d, 4 * desc.c + 4 * desc.c_idx)
-    ents = synth.normal(g, (E, desc.c))
-    keys = synth.normal(g, (E, desc.c_idx))
-    _, edeq = OL.store_entries(spec, ents, [(i, min(32, E - i)) for i in range(0, E, 32)])
-    _, kdeq = OL.store_keys(spec, keys)
-    win = np.zeros((ctx + n_tok, desc.c))
-    win[ctx - 127:] = OL.round_rows("bf16", synth.normal(g, (n_tok + 127, desc.c)))
-    qd = synth.queries(g, n_tok, desc.n_heads, desc.c, desc.n_idx_heads, desc.c_idx)
-    H = synth.normal(g, (n_tok, d))
-    sinks = synth.sinks(g, desc.n_heads)
-    pos = np.arange(ctx, ctx + n_tok)
+    if len(wd["descs"]) == 1:
+        desc = wd["descs"][0]
+        spec = _oracle_spec(desc)
+        E = (ctx + n_tok) // desc.m
+        W = synth.weights(g, d, 4 * desc.c + 4 * desc.c_idx)
+        edeq, kdeq = _oracle_cache(spec, g, E, synth, OL)
+        win = np.zeros((ctx + n_tok, desc.c))
+        win[ctx - 127:] = OL.round_rows("bf16", synth.normal(g, (n_tok + 127, desc.c)))
+        qd = synth.queries(g, n_tok, desc.n_heads, desc.c, desc.n_idx_heads, desc.c_idx)
+        H = synth.normal(g, (n_tok, d))
+        sinks = synth.sinks(g, desc.n_heads)
+        pos = np.arange(ctx, ctx + n_tok)
+        t0 = time.perf_counter()
+        OL.project(H, W)
+        OL.csa_queries(spec, qd["q"], qd["qI"], qd["w"], pos, kdeq, edeq, win, sinks)
+        elapsed = time.perf_counter() - t0
+        return {"value": round(n_tok / elapsed, 3), "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
+                "sample": f"{n_tok} consecutive decode tokens of one request at {ctx} cached tokens, first CSA "
+                          f"layer ({E} entries): new-token projection, index scores, top-{desc.top_k}, attention; "
+                          f"fp64; {elapsed:.1f} s"}
+    # one request, one step through every layer (the two CSA layers, and
+    # the two HCA layers, share one synthetic cache each)
+    caches, parts = {}, []
+    for desc in wd["descs"]:
+        spec = _oracle_spec(desc)
+        key = (desc.kind, desc.m)
+        if key not in caches:
+            E = (ctx + 1) // desc.m
+            edeq, kdeq = _oracle_cache(spec, g, E, synth, OL)
+            win = np.zeros((ctx + 1, desc.c))
+            win[ctx - 127:] = OL.round_rows("bf16", synth.normal(g, (128, desc.c)))
+            ncols = 4 * desc.c + 4 * desc.c_idx if desc.kind == abi.KIND_CSA else 2 * desc.c
+            caches[key] = (edeq, kdeq, win, synth.weights(g, d, ncols))
+        qd = synth.queries(g, 1, desc.n_heads, desc.c, desc.n_idx_heads, desc.c_idx)
+        parts.append((desc, spec, qd, synth.sinks(g, desc.n_heads), synth.normal(g, (1, d))))
+    pos = np.array([ctx])
     t0 = time.perf_counter()
-    OL.project(H, W)
-    OL.csa_queries(spec, qd["q"], qd["qI"], qd["w"], pos, kdeq, edeq, win, sinks)
+    for desc, spec, qd, sinks, H in parts:
+        edeq, kdeq, win, W = caches[(desc.kind, desc.m)]
+        OL.project(H, W)
+        if desc.kind == abi.KIND_CSA:
+            OL.csa_queries(spec, qd["q"], qd["qI"], qd["w"], pos, kdeq, edeq, win, sinks)
+        else:
+            OL.attend(spec, qd["q"], None, pos, edeq, win, sinks)
     elapsed = time.perf_counter() - t0
-    return {"value": round(n_tok / elapsed, 3), "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
-            "sample": f"{n_tok} consecutive decode tokens of one request at {ctx} cached tokens, first CSA layer "
-                      f"({E} entries): new-token projection, index scores, top-{desc.top_k}, attention; fp64; "
-                      f"{elapsed:.1f} s"}
+    return {"value": round(1.0 / elapsed, 4), "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"one decode step of one request at {ctx} cached tokens through all {len(parts)} layers "
+                      f"(projection; CSA: index scores over {(ctx + 1) // 4} entries, top-k, attention; HCA: "
+                      f"dense attention); fp64; {elapsed:.1f} s (whole-job rate of one request)"}
+
+
+def cpu_baseline_prefill(n_q: int = 32, seed: int = 12) -> dict:
+    """The oracle on a stratified sample of n_q of the 4096 chunk queries at
+    1,048,576 cached tokens (index scores over ~262K entries, top-1024,
+    attention), extrapolated to the chunk."""
+    import oracle as O
+    from oracle import layer as OL
+    import synth
+    from long_context_sparse_03_amd import presets
+    desc = presets.csa_pro()
+    spec = _oracle_spec(desc)
+    g = synth.rng(seed)
+    ctx, T = 1 << 20, 4096
+    E = (ctx + T) // desc.m
+    edeq, kdeq = _oracle_cache(spec, g, E, synth, OL)
+    win = np.zeros((ctx + T, desc.c))
+    win[ctx - 127:] = OL.round_rows("bf16", synth.normal(g, (T + 127, desc.c)))
+    rows = np.linspace(0, T - 1, n_q).astype(int)
+    qd = synth.queries(g, n_q, desc.n_heads, desc.c, desc.n_idx_heads, desc.c_idx)
+    sinks = synth.sinks(g, desc.n_heads)
+    t0 = time.perf_counter()
+    OL.csa_queries(spec, qd["q"], qd["qI"], qd["w"], ctx + rows, kdeq, edeq, win, sinks)
+    elapsed = time.perf_counter() - t0
+    per_chunk = elapsed * T / n_q
+    return {"value": round(T / per_chunk, 3), "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"{n_q} stratified queries of the 4096-token chunk at {ctx} cached tokens (index scores, "
+                      f"top-{desc.top_k}, attention), {elapsed:.1f} s, extrapolated x{T // n_q} to the chunk "
+                      f"(compressor projection excluded)", "extrapolated": True}
+
+
+def cpu_baseline_small(name: str) -> dict:
+    """The oracle on a whole small workload: the tiny fp32 CSA layer
+    (prefill 2048 + 8 decode tokens) or the HCA bf16 layer (2 x 8192)."""
+    import oracle as O
+    from oracle import layer as OL
+    import synth
+    from long_context_sparse_03_amd import presets
+    if name == "tiny_csa":
+        desc, d, reqs = presets.tiny_csa_fp32(), presets.D_TINY, [2056]
+    else:
+        desc, d, reqs = presets.hca_bf16(), presets.D_HCA, [8192, 8192]
+    spec = _oracle_spec(desc)
+    g = synth.rng(13)
+    w = synth.csa_weights(g, d, desc.c, desc.m, desc.c_idx) if desc.c_idx else synth.hca_weights(g, d, desc.c,
+                                                                                               desc.m)
+    ins = [(synth.normal(g, (n, d)), synth.queries(g, n, desc.n_heads, desc.c, desc.n_idx_heads, desc.c_idx))
+           for n in reqs]
+    sinks = synth.sinks(g, desc.n_heads)
+    t0 = time.perf_counter()
+    for H, qd in ins:
+        pos = np.arange(H.shape[0])
+        E, K, R = OL.compress_layer(spec, H, w["W"], w["Ba"], w.get("Bb"), None, w.get("W_I"), w.get("BaI"),
+                                    w.get("BbI"))
+        _, edeq = OL.store_entries(spec, E.astype(np.float32), [(0, E.shape[0])])
+        win = OL.round_rows(spec.win_fmt, R.astype(np.float32))
+        if desc.c_idx:
+            kdeq = OL.store_keys(spec, K.astype(np.float32))[1]
+            OL.csa_queries(spec, qd["q"], qd["qI"], qd["w"], pos, kdeq, edeq, win, sinks)
+        else:
+            OL.attend(spec, qd["q"], None, pos, edeq, win, sinks)
+    elapsed = time.perf_counter() - t0
+    n = sum(reqs)
+    return {"value": round(n / elapsed, 1), "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"the whole workload ({' + '.join(map(str, reqs))} tokens: compressor, storage, "
+                      f"{'index scores, top-k, ' if desc.c_idx else ''}attention); fp64; {elapsed:.2f} s"}
 
 
 def profiled_traffic(kernel: str, workload: str):
@@ -138,7 +250,7 @@ def profiled_traffic(kernel: str, workload: str):
     return int(float(vals["traffic_bytes_per_launch"]))
 
 
-def time_decode(name, steps, warmup, replicas=0, graph=True, fused_append=True):
+def time_decode(name, steps, warmup, replicas=0, graph=True, fused_append=True, fused_topk=True):
     """Decode throughput of one workload; returns a dict of measurements."""
     import torch
     from long_context_sparse_03_amd import abi
@@ -149,7 +261,8 @@ def time_decode(name, steps, warmup, replicas=0, graph=True, fused_append=True):
     total_steps = warmup + steps + 2 * reps + 64
     t_build = time.time()
     wls = [DecodeWorkload(wd["descs"], wd["d"], wd["n_req"], wd["ctx"], max_steps=total_steps,
-                          rows=torch_rows(1000 + i), seed=i, fused_append=fused_append) for i in range(reps)]
+                          rows=torch_rows(1000 + i), seed=i, fused_append=fused_append, fused_topk=fused_topk)
+           for i in range(reps)]
     torch.cuda.synchronize()
     build_s = time.time() - t_build
 
@@ -218,25 +331,31 @@ def time_decode(name, steps, warmup, replicas=0, graph=True, fused_append=True):
         t1.record(stream)
         torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
-    # Per-launch time of the index scan of the first CSA layer, on the launch
-    # stream, right after the timed steps: HIP events cannot be recorded
-    # inside a captured graph here (torch on ROCm refuses external events),
-    # so the same launches run back to back over the rotated cache replicas
-    # (the rotation keeps the keys out of the last-level cache) between one
-    # pair of events.
-    li = next(i for i, (st, _) in enumerate(wls[0].layers) if st.is_csa)
-    n_idx = 12 * reps
+    # Per-launch time of the index scan, on the launch stream, right after
+    # the timed steps: HIP events cannot be recorded inside a captured graph
+    # here (torch on ROCm refuses external events), so csa_index_scores
+    # launches (the same kernel without the fused top-k's counts) run back to
+    # back over every CSA layer of every cache replica in turn, between one
+    # pair of events.  The key sets visited in turn (replicas x CSA layers:
+    # 3 x 135.5 MB at 128K, 8 x 73.4 MB at 1M) exceed the 256 MB last-level
+    # cache, so every launch reads its keys from HBM.
+    csa_layers = [i for i, (st, _) in enumerate(wls[0].layers) if st.is_csa]
+    li = csa_layers[0]
+    sets = [(r, l) for l in csa_layers for r in range(reps)]
+    n_idx = 12 * len(sets)
     with torch.cuda.stream(stream):
-        for j in range(reps):
-            wls[j].index_call(li)
+        for r, l in sets:
+            wls[r].index_call(l)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for j in range(n_idx):
-            wls[j % reps].index_call(li)
+            r, l = sets[j % len(sets)]
+            wls[r].index_call(l)
         e1.record(stream)
         torch.cuda.synchronize()
     idx_avg_ms = e0.elapsed_time(e1) / n_idx
+    key_set_bytes = algorithmic_bytes(wd)["index_launch"] * len(sets)
     ab = algorithmic_bytes(wd)
     kname = "index_decode_fp4_kernel" if wls[0].layers[li][0].desc.idx_fmt == abi.IDX_MXFP4 else "index_decode_kernel"
     roof = None
@@ -245,7 +364,8 @@ def time_decode(name, steps, warmup, replicas=0, graph=True, fused_append=True):
         roof = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": profiled_traffic(kname, name),
-                "launch_ms": round(idx_avg_ms, 5), "algorithmic_bytes_per_launch": ab["index_launch"]}
+                "launch_ms": round(idx_avg_ms, 5), "algorithmic_bytes_per_launch": ab["index_launch"],
+                "rotated_key_sets": len(sets), "rotated_bytes": key_set_bytes}
     step_gbs = ab["total"] / (ms * 1e-3) / 1e9
     del wls, gph, gph_one
     torch.cuda.empty_cache()
@@ -339,6 +459,79 @@ def time_prefill(steps, warmup):
             "attention_tflops": round(attn_flop / (parts[3] * 1e-3) / 1e12, 1)}
 
 
+def time_small(name: str, reps: int = 5):
+    """The two small workloads end to end on the GPU (launch-bound; absolute
+    times): the tiny fp32 CSA layer (one request: a 2048-token prefill call,
+    then 8 one-token decode calls) and the HCA bf16 layer (one call with 2
+    requests x 8192 tokens).  Every call runs compress_kv, cache_append and
+    the attention (CSA: index_topk in between)."""
+    import torch
+    from long_context_sparse_03_amd import abi, presets
+    from long_context_sparse_03_amd.layer import LayerState, make_batch
+    dev = "cuda"
+    gen = torch.Generator(device=dev).manual_seed(21)
+    if name == "tiny_csa":
+        desc, d, n_req, sched = presets.tiny_csa_fp32(win_cap=2304), presets.D_TINY, 1, [(0, 2048)] + [
+            (2048 + i, 1) for i in range(8)]
+    else:
+        desc, d, n_req, sched = presets.hca_bf16(win_cap=8320), presets.D_HCA, 2, [(0, 8192)]
+    adt = torch.bfloat16 if desc.act_fmt == abi.ACT_BF16 else torch.float32
+    csa = desc.kind == abi.KIND_CSA
+    ncols = 4 * desc.c + 4 * desc.c_idx if csa else 2 * desc.c
+    n_main = 4 * desc.c if csa else 2 * desc.c
+
+    def rnd(*shape, std=1.0, dt=torch.float32):
+        return (torch.randn(*shape, generator=gen, device=dev) * std).to(dt)
+    Wt = rnd(ncols, d, std=d ** -0.5, dt=adt)
+    P = dict(W=Wt[:n_main].contiguous(), W_idx=Wt[n_main:].contiguous() if csa else None, B_a=rnd(desc.m, desc.c),
+             B_b=rnd(desc.m, desc.c) if csa else None, B_a_idx=rnd(desc.m, desc.c_idx) if csa else None,
+             B_b_idx=rnd(desc.m, desc.c_idx) if csa else None, gamma=torch.ones(desc.c, device=dev),
+             sinks=rnd(desc.n_heads))
+    nb = (max(s + n for s, n in sched) + desc.block_tokens - 1) // desc.block_tokens + 1
+    bt = torch.arange(n_req * nb, dtype=torch.int32, device=dev).view(n_req, nb)
+    st = LayerState(desc, n_req, n_req * nb)
+    calls = []
+    for s0, n in sched:
+        T = n * n_req
+        cu = torch.arange(n_req + 1, dtype=torch.int32, device=dev) * n
+        sp = torch.full((n_req,), s0, dtype=torch.int32, device=dev)
+        bi = make_batch(cu, sp, bt, n, s0 + n, T)
+        max_e = n_req * ((s0 + n) // desc.m - s0 // desc.m)
+        ld = ((s0 + n) // desc.m + 7) // 8 * 8 + 8
+        b = dict(bi=bi, T=T, max_e=max_e, ld=ld, H=rnd(T, d, dt=adt), q=rnd(T, desc.n_heads, desc.c, dt=adt),
+                 out=torch.empty((T, desc.n_heads, desc.c), dtype=torch.float32 if desc.out_fmt == abi.ACT_F32
+                                 else torch.bfloat16, device=dev))
+        if csa:
+            b.update(qI=rnd(T, desc.n_idx_heads, desc.c_idx, dt=adt), w=rnd(T, desc.n_idx_heads, std=0.125),
+                     sc=torch.empty((T, ld), dtype=torch.float32, device=dev),
+                     nv=torch.empty(T, dtype=torch.int32, device=dev),
+                     sel=torch.empty((T, desc.top_k), dtype=torch.int32, device=dev))
+        calls.append(b)
+
+    def run():
+        for b in calls:
+            st.compress_append(b["bi"], b["T"], b["H"], P["W"], P["W_idx"], P["B_a"], P["B_b"], P["B_a_idx"],
+                               P["B_b_idx"], P["gamma"], max(b["max_e"], 1))
+            if csa:
+                st.index_topk(b["bi"], b["T"], b["qI"], b["w"], b["sc"], b["ld"], b["nv"], b["sel"])
+            st.attend(b["bi"], b["T"], b["q"], P["gamma"], P["sinks"], b["out"], sel=b["sel"] if csa else None)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    n_tok = sum(n for _, n in sched) * n_req
+    del st
+    torch.cuda.empty_cache()
+    return {"workload": name, "tokens": n_tok, "calls": len(sched), "ms": round(ms, 3),
+            "tokens_per_s": round(n_tok / (ms * 1e-3), 1),
+            "note": "launch-bound parity workload; absolute time, no roofline"}
+
+
 def time_prefix(reps=3):
     """Prefix reuse, host-memory tier: the blocks of a 1,048,576-token CSA
     prefix (Pro shape, 8192 blocks of KV and indexer keys) to and from pinned
@@ -423,6 +616,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=640, help="decode tokens in the CPU-oracle sample (0: skip)")
     ap.add_argument("--separate-append", action="store_true",
                     help="decode steps call compress_kv and cache_append instead of compress_append")
+    ap.add_argument("--separate-topk", action="store_true",
+                    help="decode steps call index_scores and topk_select instead of the fused index_topk")
     ap.add_argument("--copy-probe", action="store_true", help="also run a 1 GiB device copy (HBM counter scale)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -439,18 +634,21 @@ def main():
         del a, b
 
     fused = not args.separate_append
-    prim = time_decode(args.workload, args.steps, args.warmup, args.replicas, not args.no_graph, fused)
+    ftk = not args.separate_topk
+    prim = time_decode(args.workload, args.steps, args.warmup, args.replicas, not args.no_graph, fused, ftk)
     extras = {}
     if not args.no_extras:
         other = "hybrid_decode_1m" if args.workload == "csa_decode_128k" else "csa_decode_128k"
-        extras[other] = time_decode(other, max(20, args.steps // 2), args.warmup, 0, not args.no_graph, fused)
+        extras[other] = time_decode(other, max(20, args.steps // 2), args.warmup, 0, not args.no_graph, fused, ftk)
         extras["csa_prefill_1m"] = time_prefill(max(2, min(5, args.steps // 40)), 1)
         extras["csa_prefix_1m_host"] = time_prefix()
         extras["pro_projections_decode"] = time_projections()
+        for small in ("tiny_csa", "hca_bf16"):
+            extras[small] = time_small(small)
         # warm: one cache replica, whose step working set stays in the 256 MB
         # last-level cache between steps (the primary number rotates
         # replicas so that it does not)
-        w = time_decode(args.workload, max(20, args.steps // 2), args.warmup, 1, not args.no_graph, fused)
+        w = time_decode(args.workload, max(20, args.steps // 2), args.warmup, 1, not args.no_graph, fused, ftk)
         extras[args.workload + "_warm"] = {
             "workload": args.workload, "replicas": 1, "tokens_per_s": w["tokens_per_s"],
             "ms_per_step": w["ms_per_step"], "index_launch_ms": w["roofline"]["launch_ms"],
@@ -458,6 +656,12 @@ def main():
             "note": "keys partly served from the last-level cache; not an HBM rate"}
     wd = workload_def(args.workload)
     cpu = cpu_baseline(wd, args.cpu_tokens) if args.cpu_tokens > 0 else None
+    if args.cpu_tokens > 0 and not args.no_extras:
+        other = "hybrid_decode_1m" if args.workload == "csa_decode_128k" else "csa_decode_128k"
+        extras[other]["cpu_baseline"] = cpu_baseline(workload_def(other), args.cpu_tokens)
+        extras["csa_prefill_1m"]["cpu_baseline"] = cpu_baseline_prefill()
+        for small in ("tiny_csa", "hca_bf16"):
+            extras[small]["cpu_baseline"] = cpu_baseline_small(small)
     line = {
         "metric": "CSA decode tokens/s @128K & 1M ctx; achieved HBM GB/s and MFMA % of peak",
         "value": prim["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -465,7 +669,7 @@ def main():
         "dtype": "bf16/fp8 storage, fp32 accumulate", "data": "synthetic",
         "config": {"workload": args.workload, "requests": prim["requests"], "ctx": prim["ctx"],
                    "layers": prim["layers"], "d": prim["d"], "replicas": prim["replicas"], "graph": prim["graph"],
-                   "compress_append": fused},
+                   "compress_append": fused, "index_topk": ftk},
         "step_hbm_gbs": prim["step_hbm_gbs"], "step_hbm_frac": prim["step_hbm_frac"],
         "step_algorithmic_bytes": prim["step_algorithmic_bytes"],
         "roofline": prim["roofline"],

@@ -162,8 +162,9 @@ int csa_layer_sizes(const csa_layer_desc* layer, csa_sizes* out);
  *   CSA_OP_COMPRESS  projection rows [n_rows x ncols] fp32
  *   CSA_OP_TOPK      candidate lists for n_rows score rows of up to max_cols
  *   CSA_OP_ATTENTION split-KV partial results for n_rows queries, max_cols =
- *                    the largest number of rows (entries + window) a query reads */
-enum { CSA_OP_COMPRESS = 0, CSA_OP_TOPK = 1, CSA_OP_ATTENTION = 2 };
+ *                    the largest number of rows (entries + window) a query reads
+ *   CSA_OP_INDEX_TOPK csa_index_topk for n_rows queries, max_cols = ld (CSA layers) */
+enum { CSA_OP_COMPRESS = 0, CSA_OP_TOPK = 1, CSA_OP_ATTENTION = 2, CSA_OP_INDEX_TOPK = 3 };
 int csa_workspace_size(const csa_layer_desc* layer, int op, int n_rows, int max_cols, int top_k,
                        size_t* bytes);
 
@@ -304,6 +305,28 @@ int csa_grouped_linear(void* stream, int act_fmt, int out_fmt, int n_rows, int g
 int csa_index_scores(void* stream, const csa_layer_desc* layer, const csa_batch* batch,
                      int n_tokens, const void* q_idx, const float* w, const void* idx_cache,
                      void* scores, int ld, int32_t* n_valid);
+
+/*
+ * a3 + a4 fused ([DD] §6.2: FP4 indexer QK, BF16 index scores, top-k selector;
+ * the selection of csa_topk_select on the scores of csa_index_scores).  Same
+ * arguments, scores and n_valid as csa_index_scores, plus out_idx
+ * [n_tokens x top_k] int32 with exactly the selection csa_topk_select would
+ * make from those scores (k = layer->top_k: the k largest, ties to the lower
+ * index, ascending, -1 padded).  With bf16 scores the indexer's workgroups
+ * also count their chunk's scores by the top 8 bits of the order-preserving
+ * score key while they stream the keys (the selection's first radix digit,
+ * into ws), so the selection needs only a counting and an emitting pass over
+ * segments of each row (many workgroups per row), instead of a histogram
+ * pipeline of its own.
+ * Requires ld % 8 == 0 and 16-byte aligned scores and ws (bf16 scores).
+ * fp32 scores run the two calls' kernels in order.
+ *   ws >= csa_workspace_size(CSA_OP_INDEX_TOPK, n_tokens, ld): per (query,
+ *   chunk of entries) 256 counts and per (query, segment) 258 counts (bf16),
+ *   or the top-k candidates (fp32).
+ */
+int csa_index_topk(void* stream, const csa_layer_desc* layer, const csa_batch* batch, int n_tokens,
+                   const void* q_idx, const float* w, const void* idx_cache, void* scores, int ld,
+                   int32_t* n_valid, int32_t* out_idx, void* ws, size_t ws_bytes);
 
 /*
  * a4: top-k selector ([DD] §1.2 Step 2; [AD]: k = 512 / 1024).  For each row

@@ -13,7 +13,7 @@ KIND_CSA, KIND_HCA = 0, 1
 KV_F32, KV_BF16, KV_FP8 = 0, 1, 2
 IDX_F32, IDX_BF16, IDX_MXFP4 = 0, 1, 2
 ACT_F32, ACT_BF16 = 0, 1
-OP_COMPRESS, OP_TOPK, OP_ATTENTION = 0, 1, 2
+OP_COMPRESS, OP_TOPK, OP_ATTENTION, OP_INDEX_TOPK = 0, 1, 2, 3
 FLAG_BATCH_INVARIANT = 1
 TO_HOST, FROM_HOST = 0, 1
 
@@ -69,6 +69,7 @@ def lib():
             "csa_cache_append": (I, [P, LP, BP, I, P, P, P, P, I, P, P, P, P]),
             "csa_compress_append": (I, [P, LP, BP, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, I, P, P, P, P, Z]),
             "csa_index_scores": (I, [P, LP, BP, I, P, P, P, P, I, P]),
+            "csa_index_topk": (I, [P, LP, BP, I, P, P, P, P, I, P, P, P, Z]),
             "csa_topk_select": (I, [P, I, I, P, I, P, I, P, P, Z]),
             "csa_topk_select_static": (I, [P, I, I, P, I, P, I, P]),
             "csa_sparse_mqa": (I, [P, LP, BP, I, P, P, P, P, P, P, P, P, Z]),
@@ -152,6 +153,14 @@ def index_scores(desc, batch, n_tokens, q_idx, w, idx_cache, scores, ld, n_valid
     _check("csa_index_scores", lib().csa_index_scores(
         _stream(stream), ctypes.byref(desc), ctypes.byref(batch), n_tokens, _ptr(q_idx), _ptr(w), _ptr(idx_cache),
         _ptr(scores), ld, _ptr(n_valid)))
+
+
+def index_topk(desc, batch, n_tokens, q_idx, w, idx_cache, scores, ld, n_valid, out_idx, ws, stream=None):
+    """index_scores and topk_select (k = desc.top_k) in one call."""
+    _check("csa_index_topk", lib().csa_index_topk(
+        _stream(stream), ctypes.byref(desc), ctypes.byref(batch), n_tokens, _ptr(q_idx), _ptr(w), _ptr(idx_cache),
+        _ptr(scores), ld, _ptr(n_valid), _ptr(out_idx), _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size()))
 
 
 def topk_select(score_fmt, n_rows, scores, ld, n_valid, k, out_idx, ws, stream=None):

@@ -15,8 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcsa.so")
-SOURCES = ["abi.hip", "compress.hip", "append.hip", "index.hip", "topk.hip", "attention.hip", "prefix.hip",
-           "static_ws.hip"]
+SOURCES = ["abi.hip", "compress.hip", "append.hip", "index.hip", "topk.hip", "attention.hip", "prefix.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -31,7 +30,7 @@ def _clean(stderr: str) -> str:
 
 
 def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
     with tempfile.TemporaryDirectory(prefix="csa_build_") as tmpd:
         def compile_one(src):
             obj = os.path.join(tmpd, os.path.basename(src) + ".o")

@@ -147,6 +147,21 @@ int check_batch(const csa_layer_desc* L, const csa_batch* B, bool need_blocks, i
 
 #define CHECK(expr) do { int _rc = (expr); if (_rc != CSA_OK) return _rc; } while (0)
 
+// Workspace of the fused index + top-k: per-chunk score counts (bf16
+// scores), or the two-stage top-k's candidates (fp32 scores).
+size_t index_topk_hist_bytes(const csa_layer_desc* layer, int n_rows, int ld)
+{
+    const int chunk = csa::index_min_chunk(layer->idx_fmt);
+    const size_t b = (size_t)n_rows * ((ld + chunk - 1) / chunk) * 256 * sizeof(uint16_t);
+    return (b + 255) & ~(size_t)255;
+}
+
+size_t index_topk_workspace(const csa_layer_desc* layer, int n_rows, int ld)
+{
+    if (layer->score_fmt != CSA_FMT_BF16) return csa::topk_workspace(n_rows, ld, layer->top_k, false);
+    return index_topk_hist_bytes(layer, n_rows, ld) + csa::topk_hist_workspace(n_rows, ld);
+}
+
 }  // namespace
 
 extern "C" {
@@ -180,6 +195,11 @@ int csa_workspace_size(const csa_layer_desc* layer, int op, int n_rows, int max_
         return CSA_OK;
     case CSA_OP_ATTENTION:
         *bytes = csa::attention_workspace(n_rows, layer->n_heads, layer->c, max_cols, invariant(layer));
+        return CSA_OK;
+    case CSA_OP_INDEX_TOPK:
+        REQUIRE(is_csa(layer), CSA_EINVAL, "index_topk needs a CSA layer");
+        REQUIRE(max_cols >= 1, CSA_EINVAL, "max_cols=%d (ld)", max_cols);
+        *bytes = index_topk_workspace(layer, n_rows, max_cols);
         return CSA_OK;
     default: return fail(CSA_EINVAL, "op=%d", op);
     }
@@ -350,9 +370,13 @@ int csa_compress_append(void* stream, const csa_layer_desc* layer, const csa_bat
                       "compress_append launch");
 }
 
-int csa_index_scores(void* stream, const csa_layer_desc* layer, const csa_batch* batch, int n_tokens,
-                     const void* q_idx, const float* w, const void* idx_cache, void* scores, int ld,
-                     int32_t* n_valid)
+}  // extern "C"
+
+namespace {
+
+// Validates index_scores' arguments and fills its kernel arguments.
+int index_args(const csa_layer_desc* layer, const csa_batch* batch, int n_tokens, const void* q_idx, const float* w,
+               const void* idx_cache, void* scores, int ld, int32_t* n_valid, csa::IndexArgs* out)
 {
     CHECK(check_layer(layer));
     REQUIRE(is_csa(layer), CSA_EINVAL, "index_scores needs a CSA layer");
@@ -364,7 +388,7 @@ int csa_index_scores(void* stream, const csa_layer_desc* layer, const csa_batch*
     REQUIRE(n_tokens == 0 || (q_idx != nullptr && w != nullptr && idx_cache != nullptr && scores != nullptr &&
                               n_valid != nullptr),
             CSA_EINVAL, "NULL pointer argument");
-    csa::IndexArgs a;
+    csa::IndexArgs& a = *out;
     memset(&a, 0, sizeof(a));
     a.q = q_idx;
     a.w = w;
@@ -387,7 +411,56 @@ int csa_index_scores(void* stream, const csa_layer_desc* layer, const csa_batch*
     a.ld = ld;
     a.n_valid = n_valid;
     a.n_tokens = n_tokens;
-    return hip_status(csa::launch_index((hipStream_t)stream, a, max_vis, batch->max_new), "index_scores launch");
+    return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int csa_index_scores(void* stream, const csa_layer_desc* layer, const csa_batch* batch, int n_tokens,
+                     const void* q_idx, const float* w, const void* idx_cache, void* scores, int ld,
+                     int32_t* n_valid)
+{
+    csa::IndexArgs a;
+    CHECK(index_args(layer, batch, n_tokens, q_idx, w, idx_cache, scores, ld, n_valid, &a));
+    return hip_status(csa::launch_index((hipStream_t)stream, a, batch->max_ctx / layer->m, batch->max_new),
+                      "index_scores launch");
+}
+
+int csa_index_topk(void* stream, const csa_layer_desc* layer, const csa_batch* batch, int n_tokens,
+                   const void* q_idx, const float* w, const void* idx_cache, void* scores, int ld, int32_t* n_valid,
+                   int32_t* out_idx, void* ws, size_t ws_bytes)
+{
+    csa::IndexArgs a;
+    CHECK(index_args(layer, batch, n_tokens, q_idx, w, idx_cache, scores, ld, n_valid, &a));
+    const bool bf = layer->score_fmt == CSA_FMT_BF16;
+    REQUIRE(n_tokens == 0 || out_idx != nullptr, CSA_EINVAL, "out_idx is NULL");
+    REQUIRE(!bf || (ld % 8 == 0 && ((uintptr_t)scores & 15) == 0), CSA_EINVAL,
+            "bf16 scores: ld (%d) must be a multiple of 8 and scores 16-byte aligned", ld);
+    REQUIRE(bf || csa::topk_supported(ld, layer->top_k, false), CSA_EUNSUPPORTED,
+            "rows of %d scores with k=%d exceed the two-stage selector's capacity", ld, layer->top_k);
+    const size_t need = index_topk_workspace(layer, n_tokens, ld);
+    REQUIRE(ws_bytes >= need && (need == 0 || ws != nullptr), CSA_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes,
+            need);
+    REQUIRE(!bf || ((uintptr_t)ws & 15) == 0, CSA_EINVAL, "workspace must be 16-byte aligned");
+    if (n_tokens == 0) return CSA_OK;
+    const hipStream_t st = (hipStream_t)stream;
+    const int max_vis = batch->max_ctx / layer->m;
+    if (!bf) {
+        hipError_t e = csa::launch_index(st, a, max_vis, batch->max_new);
+        if (e == hipSuccess)
+            e = csa::launch_topk(st, 0, n_tokens, scores, ld, n_valid, layer->top_k, out_idx, ws, ld);
+        return hip_status(e, "index_topk launch");
+    }
+    a.hist = (uint16_t*)ws;
+    int chunk = 0;
+    hipError_t e = csa::launch_index(st, a, max_vis, batch->max_new, &chunk);
+    if (e == hipSuccess)
+        e = csa::launch_topk_hist(st, n_tokens, scores, ld, n_valid, (const uint16_t*)ws, (ld + chunk - 1) / chunk,
+                                  chunk, layer->top_k, out_idx,
+                                  (char*)ws + index_topk_hist_bytes(layer, n_tokens, ld));
+    return hip_status(e, "index_topk launch");
 }
 
 }  // extern "C"

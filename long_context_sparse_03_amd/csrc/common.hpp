@@ -35,6 +35,14 @@ CSA_DEV uint32_t pack_bf16x2(float a, float b)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+// Order-preserving 16-bit key of a bf16 score (sign-magnitude flip; -0 and
+// +0 share the key): larger scores have larger keys.
+CSA_DEV uint32_t key16(uint32_t b)
+{
+    if ((b & 0x7FFFu) == 0u) b = 0u;
+    return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+}
+
 // OCP E4M3FN -> fp32 (exact).  0x7F/0xFF (NaN) never occur in stored data.
 CSA_DEV float e4m3_to_f32(uint32_t q)
 {

@@ -121,7 +121,23 @@ CSA_DEV void load_keys(const IndexArgs& a, const int* bt, int blk0, int e0, int 
     }
 }
 
-template <int IDXF, int HT, int S>
+// bf16 bits with -0 (a tiny negative score that rounds to zero) made +0, as
+// the scores are stored and counted
+CSA_DEV uint16_t canon_bf16(uint16_t b) { return (b & 0x7FFFu) == 0u ? (uint16_t)0u : b; }
+
+// Fused top-k: the chunk's 256 counts of query row gq (threads 0..255, one
+// coalesced 512-byte store), after every wave has counted its scores.  Every
+// wave of the workgroup must call it (it holds a barrier when HIST).
+template <bool HIST>
+CSA_DEV void store_hist(const IndexArgs& a, int gq, int chunk, const uint32_t* hcnt)
+{
+    if (!HIST) return;
+    __syncthreads();
+    if (threadIdx.x < 256)
+        a.hist[((size_t)gq * a.hist_chunks + chunk) * 256 + threadIdx.x] = (uint16_t)hcnt[threadIdx.x];
+}
+
+template <int IDXF, int HT, int S, bool HIST>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S <= 4 ? 2 : 1))) void index_decode_kernel(IndexArgs a)
 {
     // IDXF 0: fp32 keys and queries; 1: bf16 keys and queries.
@@ -131,10 +147,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S <= 4 ? 2 
     // registers, so that two workgroups fit on a compute unit and twice the
     // key bytes are in flight)
     __shared__ uint4 qfrag[HT][S][64];
+    __shared__ uint32_t hcnt[256];               // fused top-k: this chunk's scores by key16 >> 8
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
     // query fastest in the dispatch order: every query's near-empty last
     // key chunk comes after all full chunks, not among them
     const int gq = blockIdx.x;
+    hcnt[threadIdx.x] = 0u;                      // 256 threads, published by the prologue's barrier
     const int wg0 = blockIdx.y * IDXD_EPW;
     const int cI = a.cI, nh = a.nh;
     constexpr int QES = IDXF == 0 ? 4 : 2;      // query element size
@@ -246,10 +264,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S <= 4 ? 2 
         const int e = e_base + 16 * (2 * (g & 1) + (g >> 1)) + li;
         if (e < V) {
             if (x == 0.0f) x = 0.0f;                    // -0 is stored as +0
-            if (a.score_bf16) ((uint16_t*)a.scores)[(size_t)gq * a.ld + e] = f32_to_bf16(x);
-            else ((float*)a.scores)[(size_t)gq * a.ld + e] = x;
+            if (a.score_bf16) {
+                const uint16_t b = canon_bf16(f32_to_bf16(x));   // a value rounding to -0 is stored as +0
+                ((uint16_t*)a.scores)[(size_t)gq * a.ld + e] = b;
+                if (HIST) atomicAdd(&hcnt[key16(b) >> 8], 1u);
+            } else {
+                ((float*)a.scores)[(size_t)gq * a.ld + e] = x;
+            }
         }
     }
+    store_hist<HIST>(a, gq, blockIdx.y, hcnt);
 }
 
 // Prefill-shaped launch (bf16 keys, 128 channels): eight queries of one
@@ -265,7 +289,7 @@ constexpr int PF_TILE = 128;                  // keys per LDS tile
 constexpr int PF_ECH = 8192;                  // keys per workgroup
 constexpr int PF_CI = 128;                    // key channels (16 chunks of 16 bytes)
 
-template <int HT, int S, bool BF16OUT>
+template <int HT, int S, bool BF16OUT, bool HIST>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void index_prefill_kernel(IndexArgs a, int groups_per_req)
 {
     static_assert(S * 8 * 4 == PF_CI, "S steps of eight channels in each of four lane groups cover a key");
@@ -276,10 +300,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void i
     __shared__ __attribute__((aligned(16))) uint16_t Ks1[PF_TILE * PF_CI];
     __shared__ int bt[PF_ECH / 32 + 2];
     __shared__ int cu_sh[1025];
+    __shared__ uint32_t hcnt[PF_QPW][256];                          // fused top-k: per wave (query) counts
     const int lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int req = blockIdx.y / groups_per_req, grp = blockIdx.y % groups_per_req;
     if (a.n_req >= 1024) return;                                    // host dispatch keeps n_req small here
+    for (int i = threadIdx.x; i < PF_QPW * 256; i += blockDim.x) (&hcnt[0][0])[i] = 0u;
     for (int i = threadIdx.x; i <= a.n_req; i += blockDim.x) cu_sh[i] = a.cu_new[i];
     __syncthreads();
     const int cu = cu_sh[req], n_tok = cu_sh[req + 1] - cu;
@@ -352,8 +378,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void i
             if (e < V) {
                 float x = xs[eb];
                 if (x == 0.0f) x = 0.0f;                            // -0 is stored as +0
-                if constexpr (BF16OUT) ((uint16_t*)a.scores)[(size_t)gq * a.ld + e] = f32_to_bf16(x);
-                else ((float*)a.scores)[(size_t)gq * a.ld + e] = x;
+                if constexpr (BF16OUT) {
+                    const uint16_t b = canon_bf16(f32_to_bf16(x));   // a value rounding to -0 is stored as +0
+                    ((uint16_t*)a.scores)[(size_t)gq * a.ld + e] = b;
+                    if (HIST) atomicAdd(&hcnt[wave][key16(b) >> 8], 1u);
+                } else {
+                    ((float*)a.scores)[(size_t)gq * a.ld + e] = x;
+                }
             }
         }
         es = -1;
@@ -421,12 +452,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void i
         tile_done();
     }
     store_scores();
+    // fused top-k: each valid query's counts of this chunk, lane l bins 4l..4l+3
+    if (HIST) {
+        __syncthreads();
+        if (qvalid) {
+            uint16_t* h = a.hist + ((size_t)gq * a.hist_chunks + blockIdx.x) * 256 + 4 * lane;
+            const uint32_t* c = &hcnt[wave][4 * lane];
+            *(uint2*)h = make_uint2(c[0] | (c[1] << 16), c[2] | (c[3] << 16));
+        }
+    }
 }
 
 // MXFP4 decode launch: as the bf16 decode kernel, with the stored key bytes
 // fed straight into the scaled FP4 MFMA (one instruction per 16 keys and 16
 // heads covers the whole 128-wide key).
-template <int HT>
+template <int HT, bool HIST>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void index_decode_fp4_kernel(IndexArgs a)
 {
     static_assert(HT <= 4, "one wave quantises each head tile");
@@ -434,8 +474,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
     __shared__ int cu_sh[1025];
     __shared__ uint4 qc_sh[HT][64];              // quantised query: E2M1 codes ...
     __shared__ int qs_sh[HT][64];                // ... and E8M0 scales per (head tile, lane)
+    __shared__ uint32_t hcnt[256];               // fused top-k: this chunk's scores by key16 >> 8
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
     const int gq = blockIdx.x;                   // query fastest (as the bf16 kernel)
+    hcnt[threadIdx.x] = 0u;                      // 256 threads, published by the barrier below
     const int wg0 = blockIdx.y * IDX_EPW;
     const int cI = a.cI, nh = a.nh;                // cI == 128: lane group g holds MX block g
     int req, tok;
@@ -545,76 +587,99 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
         const int e = e_base + 16 * (2 * (g & 1) + (g >> 1)) + li;
         if (e < V) {
             if (x == 0.0f) x = 0.0f;                    // -0 is stored as +0
-            if (a.score_bf16) ((uint16_t*)a.scores)[(size_t)gq * a.ld + e] = f32_to_bf16(x);
-            else ((float*)a.scores)[(size_t)gq * a.ld + e] = x;
+            if (a.score_bf16) {
+                const uint16_t b = canon_bf16(f32_to_bf16(x));   // a value rounding to -0 is stored as +0
+                ((uint16_t*)a.scores)[(size_t)gq * a.ld + e] = b;
+                if (HIST) atomicAdd(&hcnt[key16(b) >> 8], 1u);
+            } else {
+                ((float*)a.scores)[(size_t)gq * a.ld + e] = x;
+            }
         }
     }
+    store_hist<HIST>(a, gq, blockIdx.y, hcnt);
 }
 
-template <int IDXF, int HT>
+template <int IDXF, int HT, bool HIST>
 static void launch_ht(hipStream_t st, const IndexArgs& a, dim3 grid)
 {
     // fragments per lane group: quarter of the key width / elements per fragment
     const int quarter = a.cI / 4;
     const int epf = IDXF == 0 ? 4 : 8;
     const int S = quarter / epf;
-    {
-        switch (S) {
-        case 1: index_decode_kernel<IDXF, HT, 1><<<grid, 256, 0, st>>>(a); break;
-        case 2: index_decode_kernel<IDXF, HT, 2><<<grid, 256, 0, st>>>(a); break;
-        case 4: index_decode_kernel<IDXF, HT, 4><<<grid, 256, 0, st>>>(a); break;
-        case 8: index_decode_kernel<IDXF, HT, 8><<<grid, 256, 0, st>>>(a); break;
-        default: break;
-        }
+    switch (S) {
+    case 1: index_decode_kernel<IDXF, HT, 1, HIST><<<grid, 256, 0, st>>>(a); break;
+    case 2: index_decode_kernel<IDXF, HT, 2, HIST><<<grid, 256, 0, st>>>(a); break;
+    case 4: index_decode_kernel<IDXF, HT, 4, HIST><<<grid, 256, 0, st>>>(a); break;
+    case 8: index_decode_kernel<IDXF, HT, 8, HIST><<<grid, 256, 0, st>>>(a); break;
+    default: break;
     }
 }
 
-template <int IDXF>
+template <int IDXF, bool HIST>
 static void launch_fmt(hipStream_t st, const IndexArgs& a, dim3 grid)
 {
     const int HT = (a.nh + 15) / 16;
     switch (HT) {
-    case 1: launch_ht<IDXF, 1>(st, a, grid); break;
-    case 2: launch_ht<IDXF, 2>(st, a, grid); break;
-    case 3: launch_ht<IDXF, 3>(st, a, grid); break;
-    default: launch_ht<IDXF, 4>(st, a, grid); break;
+    case 1: launch_ht<IDXF, 1, HIST>(st, a, grid); break;
+    case 2: launch_ht<IDXF, 2, HIST>(st, a, grid); break;
+    case 3: launch_ht<IDXF, 3, HIST>(st, a, grid); break;
+    default: launch_ht<IDXF, 4, HIST>(st, a, grid); break;
     }
 }
 
-template <bool BF16OUT>
+template <bool BF16OUT, bool HIST>
 static void launch_prefill(hipStream_t st, const IndexArgs& a, dim3 grid, int groups)
 {
     const int HT = (a.nh + 15) / 16;
-    if (HT == 4) index_prefill_kernel<4, 4, BF16OUT><<<grid, 512, 0, st>>>(a, groups);
-    else if (HT == 3) index_prefill_kernel<3, 4, BF16OUT><<<grid, 512, 0, st>>>(a, groups);
-    else if (HT == 2) index_prefill_kernel<2, 4, BF16OUT><<<grid, 512, 0, st>>>(a, groups);
-    else index_prefill_kernel<1, 4, BF16OUT><<<grid, 512, 0, st>>>(a, groups);
+    if (HT == 4) index_prefill_kernel<4, 4, BF16OUT, HIST><<<grid, 512, 0, st>>>(a, groups);
+    else if (HT == 3) index_prefill_kernel<3, 4, BF16OUT, HIST><<<grid, 512, 0, st>>>(a, groups);
+    else if (HT == 2) index_prefill_kernel<2, 4, BF16OUT, HIST><<<grid, 512, 0, st>>>(a, groups);
+    else index_prefill_kernel<1, 4, BF16OUT, HIST><<<grid, 512, 0, st>>>(a, groups);
 }
 
-hipError_t launch_index(hipStream_t st, const IndexArgs& args, int max_visible, int max_new)
+template <bool HIST>
+static void launch_fp4(hipStream_t st, const IndexArgs& a, dim3 grid)
+{
+    const int HT = (a.nh + 15) / 16;
+    if (HT == 4) index_decode_fp4_kernel<4, HIST><<<grid, 256, 0, st>>>(a);
+    else if (HT == 3) index_decode_fp4_kernel<3, HIST><<<grid, 256, 0, st>>>(a);
+    else if (HT == 2) index_decode_fp4_kernel<2, HIST><<<grid, 256, 0, st>>>(a);
+    else index_decode_fp4_kernel<1, HIST><<<grid, 256, 0, st>>>(a);
+}
+
+int index_min_chunk(int idx_fmt) { return idx_fmt == 2 ? IDX_EPW : IDXD_EPW; }
+
+hipError_t launch_index(hipStream_t st, const IndexArgs& args, int max_visible, int max_new, int* chunk)
 {
     if (args.n_tokens <= 0) return hipSuccess;
     IndexArgs a = args;
     // n_tokens tokens over n_req requests with at most one each: one apiece
     a.one_per_req = max_new <= 1 && a.n_tokens == a.n_req;
+    // the per-chunk counts of the fused top-k (bf16 scores only)
+    const bool hist = a.hist != nullptr && a.score_bf16;
     if (a.idx_fmt == 1 && a.cI == 128 && a.nh <= 64 && max_new >= 2 * PF_QPW && a.n_req < 1024) {
+        if (chunk) *chunk = PF_ECH;
+        a.hist_chunks = (a.ld + PF_ECH - 1) / PF_ECH;
         const int groups = (max_new + PF_QPW - 1) / PF_QPW;
         dim3 grid(max_visible > 0 ? (max_visible + PF_ECH - 1) / PF_ECH : 1, a.n_req * groups);
-        const int HT = (a.nh + 15) / 16;
-        if (a.score_bf16) launch_prefill<true>(st, a, grid, groups);
-        else launch_prefill<false>(st, a, grid, groups);
+        if (!a.score_bf16) launch_prefill<false, false>(st, a, grid, groups);
+        else if (hist) launch_prefill<true, true>(st, a, grid, groups);
+        else launch_prefill<true, false>(st, a, grid, groups);
         return hipGetLastError();
     }
     const int epw = a.idx_fmt == 2 ? IDX_EPW : IDXD_EPW;
+    if (chunk) *chunk = epw;
+    a.hist_chunks = (a.ld + epw - 1) / epw;
     dim3 grid(a.n_tokens, max_visible > 0 ? (max_visible + epw - 1) / epw : 1);
-    if (a.idx_fmt == 0) launch_fmt<0>(st, a, grid);
-    else if (a.idx_fmt == 1) launch_fmt<1>(st, a, grid);
-    else {
-        const int HT = (a.nh + 15) / 16;
-        if (HT == 4) index_decode_fp4_kernel<4><<<grid, 256, 0, st>>>(a);
-        else if (HT == 3) index_decode_fp4_kernel<3><<<grid, 256, 0, st>>>(a);
-        else if (HT == 2) index_decode_fp4_kernel<2><<<grid, 256, 0, st>>>(a);
-        else index_decode_fp4_kernel<1><<<grid, 256, 0, st>>>(a);
+    if (a.idx_fmt == 0) {
+        if (hist) launch_fmt<0, true>(st, a, grid);
+        else launch_fmt<0, false>(st, a, grid);
+    } else if (a.idx_fmt == 1) {
+        if (hist) launch_fmt<1, true>(st, a, grid);
+        else launch_fmt<1, false>(st, a, grid);
+    } else {
+        if (hist) launch_fp4<true>(st, a, grid);
+        else launch_fp4<false>(st, a, grid);
     }
     return hipGetLastError();
 }

@@ -86,9 +86,23 @@ struct IndexArgs {
     int32_t* n_valid;
     int n_tokens;
     int one_per_req;           // set by launch_index: every request has exactly one new token
+    uint16_t* hist;            // or null: per (row, chunk of entries) counts of the bf16 scores by the top 8
+                               // bits of their order-preserving key, 256 per chunk (the fused top-k's first digit)
+    int hist_chunks;           // chunks per row in hist (set by launch_index from the chunk it launches)
 };
 
-hipError_t launch_index(hipStream_t st, const IndexArgs& a, int max_visible, int max_new);
+// *chunk (if not null): entries per histogram chunk of the launch chosen
+hipError_t launch_index(hipStream_t st, const IndexArgs& a, int max_visible, int max_new, int* chunk = nullptr);
+// Entries per histogram chunk of the smallest chunk any index launch of this key format uses.
+int index_min_chunk(int idx_fmt);
+
+// The fused top-k's selection (bf16 scores, ld % 8 == 0): the k-th key's top 8
+// bits from the indexer's per-chunk counts, then a counting and an emitting
+// pass over segments of each row (many workgroups per row); ws holds the
+// per-segment counts (topk_hist_workspace bytes, 16-byte aligned).
+hipError_t launch_topk_hist(hipStream_t st, int n_rows, const void* scores, int ld, const int32_t* n_valid,
+                            const uint16_t* hist, int hist_chunks, int chunk, int k, int32_t* out, void* ws);
+size_t topk_hist_workspace(int n_rows, int ld);
 
 hipError_t launch_topk(hipStream_t st, int score_bf16, int n_rows, const void* scores, int ld,
                        const int32_t* n_valid, int k, int32_t* out, void* ws, int max_cols);

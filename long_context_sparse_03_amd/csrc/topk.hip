@@ -36,13 +36,8 @@ constexpr int SMALL_NT = 512, SMALL_KPT = 16; // workgroups of up to 8192 keys (
 constexpr int MID_KPT = 16;                   // 1024 threads for up to 16384 keys
 constexpr int SURV_CAP = 4096;                // keys kept after the lower bound (1024-thread workgroups)
 
-// Order-preserving key of a score: sign-magnitude flip; -0 and +0 share the key.
-CSA_DEV uint32_t key16(uint32_t b)
-{
-    if ((b & 0x7FFFu) == 0u) b = 0u;
-    return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
-}
-
+// Order-preserving key of an fp32 score (key16 for bf16 is in common.hpp):
+// sign-magnitude flip; -0 and +0 share the key.
 CSA_DEV uint32_t key32(uint32_t u)
 {
     if ((u & 0x7FFFFFFFu) == 0u) u = 0u;
@@ -568,6 +563,341 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_merge_kernel(const int32_t*
     __syncthreads();
     int32_t* o = out + (size_t)row * k;
     for (int r = threadIdx.x; r < k; r += blockDim.x) o[r] = r < kk ? ci[spos[r]] : -1;
+}
+
+// ---------------------------------------------------------------------------
+// Fused top-k (bf16 scores): selection from the indexer's counts, over
+// segments of each row.
+//
+// The indexer counted each chunk's scores by the top 8 bits of their
+// order-preserving key (csa::key16), so the coarse digit b* of the k-th
+// largest key, and its rank r1 inside that bin, come from adding those
+// counts without reading a score.  Two kernels then cover each row in
+// segments of SEL_ROUND * rounds keys, many workgroups per row:
+//   count: each segment counts its keys above bin b* and, for the keys in
+//          b*, a histogram of their low 8 bits, stored as suffix sums
+//          cum[f] = #(keys in b* with low bits >= f), f = 0..256;
+//   emit:  each segment adds every segment's suffix sums, which gives the
+//          exact k-th key T = (b*, f*) and how many keys equal to T are
+//          taken; the counts of the segments before it give its first
+//          output rank, and it emits its keys above T and the first of
+//          those equal to T in position order (ties to the lower index).
+// No workgroup waits for another: the kernel boundary orders the two passes.
+// ---------------------------------------------------------------------------
+constexpr int SEL_NT = 256;                   // threads per segment workgroup
+constexpr int SEL_KPT = 16;                   // keys per thread and round
+constexpr int SEL_ROUND = SEL_NT * SEL_KPT;   // 4096 keys per round
+constexpr int SEL_REC = 260;                  // words per (row, segment): keys above b*, cum[0..256], b*, rank
+
+// Two exclusive prefix sums over the workgroup with one barrier (as
+// BlockScan::exscan, pairs of wave totals in alternating LDS slots).
+CSA_DEV void block_exscan2(uint32_t a, uint32_t b, uint32_t& a_before, uint32_t& b_before, uint32_t& a_total,
+                           uint32_t& b_total, int& parity)
+{
+    __shared__ uint32_t part2[2][2][16];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const uint32_t ia = wave_incl_scan(a), ib = wave_incl_scan(b);
+    if (lane == 63) {
+        part2[parity][0][w] = ia;
+        part2[parity][1][w] = ib;
+    }
+    __syncthreads();
+    uint32_t oa = 0, ob = 0, ta = 0, tb = 0;
+    for (int i = 0; i < nw; ++i) {
+        const uint32_t xa = part2[parity][0][i], xb = part2[parity][1][i];
+        ta += xa;
+        tb += xb;
+        oa += i < w ? xa : 0u;
+        ob += i < w ? xb : 0u;
+    }
+    parity ^= 1;
+    a_before = oa + ia - a;
+    b_before = ob + ib - b;
+    a_total = ta;
+    b_total = tb;
+}
+
+// Wave 0: among 256 counts (cnt(b) for bin b), the bin holding the rem-th
+// largest key counting from bin 255 down, and the rank of that key inside
+// its bin.  Lane l holds bins 255-4l .. 252-4l.
+template <class CountF>
+CSA_DEV void wave_pick_bin(CountF cnt, uint32_t rem, uint32_t* out_bin, uint32_t* out_rem)
+{
+    const int lane = threadIdx.x & 63;
+    uint32_t c4[4], tot = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        c4[j] = cnt(255 - 4 * lane - j);
+        tot += c4[j];
+    }
+    const uint32_t inc = wave_incl_scan(tot), exc = inc - tot;
+    if (exc < rem && rem <= inc) {
+        uint32_t above = exc;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (rem <= above + c4[j]) {
+                *out_bin = (uint32_t)(255 - 4 * lane - j);
+                *out_rem = rem - above;
+                break;
+            }
+            above += c4[j];
+        }
+    }
+}
+
+// Order-preserving keys of two bf16 scores in one word (low half first),
+// the sign-magnitude flip of key16 on both halves at once.  The indexer
+// stores no -0, so no zero fix-up is needed.
+CSA_DEV uint32_t key16x2(uint32_t w)
+{
+    return w ^ 0x80008000u ^ (((w >> 15) & 0x00010001u) * 0x7FFFu);
+}
+
+// The 16 keys of thread t in the round starting at position p0 (positions
+// p0 + 16 t .. p0 + 16 t + 15) as two 16-byte vectors of packed bf16 pairs;
+// vectors past the row are clamped to its last one (masked by position).
+CSA_DEV void sel_load(const uint16_t* sr, int nvec_row, int p0, uint4 (&q)[2])
+{
+    const int v0 = (p0 + (int)threadIdx.x * SEL_KPT) / 8;
+    q[0] = ld16(sr + 8 * (size_t)min(v0, nvec_row - 1));
+    q[1] = ld16(sr + 8 * (size_t)min(v0 + 1, nvec_row - 1));
+}
+
+// Coarse digit of the k-th largest key of a row from the per-chunk counts
+// (all 256 threads): bin b* into pick[0], the rank of the k-th key inside it
+// into pick[1].  Thread t adds bins 8 (t mod 32) .. +7 of chunks t/32,
+// t/32 + 8, .. (16-byte loads, four chunks in flight), the 8 chunk groups
+// meet in LDS.
+CSA_DEV void coarse_pick(const uint16_t* hr, int nch, uint32_t k, uint32_t (&part)[8][256], uint32_t (&tot)[256],
+                         uint32_t* pick)
+{
+    const int tid = threadIdx.x, sub = tid & 31, cgrp = tid >> 5;
+    uint32_t acc[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    for (int c0 = cgrp; c0 < nch; c0 += 4 * 8) {
+        uint4 h[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c = c0 + 8 * u;
+            h[u] = c < nch ? ld16(hr + (size_t)c * 256 + 8 * sub) : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t w4[4] = {h[u].x, h[u].y, h[u].z, h[u].w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] += (w4[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+        }
+    }
+    *(uint4*)&part[cgrp][8 * sub] = make_uint4(acc[0], acc[1], acc[2], acc[3]);
+    *(uint4*)&part[cgrp][8 * sub + 4] = make_uint4(acc[4], acc[5], acc[6], acc[7]);
+    if (tid == 0) {                                          // defined even if no bin qualifies
+        pick[0] = 0u;
+        pick[1] = 1u;
+    }
+    __syncthreads();
+    uint32_t t = 0;
+#pragma unroll
+    for (int g2 = 0; g2 < 8; ++g2) t += part[g2][tid];
+    tot[tid] = t;
+    __syncthreads();
+    if (tid < 64) wave_pick_bin([&](int b) { return tot[b]; }, k, &pick[0], &pick[1]);
+    __syncthreads();
+    if (tid == 0) pick[0] = min(pick[0], 255u);
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(SEL_NT) void topk_seg_count_kernel(const uint16_t* scores, int ld,
+                                                                const int32_t* n_valid, const uint16_t* hist,
+                                                                int hist_chunks, int chunk, int k, int rounds,
+                                                                int seg_stride, uint32_t* rec)
+{
+    const int row = blockIdx.y, sgi = blockIdx.x, tid = threadIdx.x;
+    const int V = min(n_valid[row], ld);
+    const int s0 = sgi * rounds * SEL_ROUND;
+    if (V <= k || s0 >= V) return;                           // uniform: nothing of this segment is needed
+    __shared__ uint32_t part[8][256];
+    __shared__ uint32_t tot[256];
+    __shared__ uint32_t fine[256];
+    __shared__ uint32_t pick[2];
+    const uint16_t* sr = scores + (size_t)row * ld;
+    const int nvec_row = ld / 8;
+    uint4 q[2];
+    sel_load(sr, nvec_row, s0, q);                           // in flight during the coarse sums
+    fine[tid] = 0u;
+    coarse_pick(hist + (size_t)row * hist_chunks * 256, (V + chunk - 1) / chunk, (uint32_t)k, part, tot, pick);
+    const uint32_t bstar = pick[0];
+    uint32_t gt = 0;
+    for (int rnd = 0; rnd < rounds; ++rnd) {
+        const int p0 = s0 + rnd * SEL_ROUND;
+        if (p0 >= V) break;                                  // uniform
+        if (rnd > 0) sel_load(sr, nvec_row, p0, q);
+        const int base = p0 + tid * SEL_KPT;
+        const uint32_t w8[8] = {q[0].x, q[0].y, q[0].z, q[0].w, q[1].x, q[1].y, q[1].z, q[1].w};
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+            const uint32_t kp = key16x2(w8[h]);
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const uint32_t kv = (kp >> (16 * half)) & 0xFFFFu;
+                const bool in = base + 2 * h + half < V;
+                gt += in && (kv >> 8) > bstar;
+                if (in && (kv >> 8) == bstar) atomicAdd(&fine[kv & 0xFFu], 1u);
+            }
+        }
+    }
+    __syncthreads();
+    // suffix sums of the fine counts (thread t holds bin 255 - t: an
+    // inclusive scan in thread order) and the segment's keys above b*
+    BlockScan bs;
+    uint32_t gt_tot;
+    const uint32_t gt_before = bs.exscan(gt, &gt_tot);
+    (void)gt_before;
+    uint32_t fin_tot;
+    const uint32_t f = fine[255 - tid];
+    const uint32_t suffix = bs.exscan(f, &fin_tot) + f;     // cum[255 - t]
+    uint32_t* r = rec + ((size_t)row * seg_stride + sgi) * SEL_REC;
+    r[1 + (255 - tid)] = suffix;
+    if (tid == 0) {
+        r[0] = gt_tot;
+        r[1 + 256] = 0u;
+        r[258] = bstar;                                      // the row's coarse digit and the rank in it
+        r[259] = pick[1];                                    // (the same in every segment's record)
+    }
+}
+
+__global__ __launch_bounds__(SEL_NT) void topk_seg_emit_kernel(const uint16_t* scores, int ld, const int32_t* n_valid,
+                                                               int k, int rounds, int seg_stride,
+                                                               const uint32_t* rec, int32_t* out)
+{
+    const int row = blockIdx.y, sgi = blockIdx.x, tid = threadIdx.x;
+    const int V = min(n_valid[row], ld);
+    int32_t* o = out + (size_t)row * k;
+    if (V <= k) {                                            // every visible entry, then -1
+        if (sgi == 0)
+            for (int r = tid; r < k; r += SEL_NT) o[r] = r < V ? r : -1;
+        return;
+    }
+    const int seg = rounds * SEL_ROUND;
+    const int s0 = sgi * seg;
+    if (s0 >= V) return;
+    const int nseg = (V + seg - 1) / seg;
+    __shared__ uint32_t ctot[257];
+    __shared__ uint32_t pick[2];
+    const uint16_t* sr = scores + (size_t)row * ld;
+    const int nvec_row = ld / 8;
+    uint4 q[2];
+    sel_load(sr, nvec_row, s0, q);
+    // the coarse digit and the rank in it, from the count kernel's records;
+    // suffix sums over every segment of the row: thread t adds cum[t] of
+    // segments 0, 1, .. (sixteen loads in flight)
+    const uint32_t* rr = rec + (size_t)row * seg_stride * SEL_REC;
+    const uint32_t bstar = min(rr[258], 255u), r1 = rr[259];
+    {
+        uint32_t c = 0;
+        for (int i0 = 0; i0 < nseg; i0 += 16) {
+            uint32_t v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = i0 + u < nseg ? rr[(size_t)(i0 + u) * SEL_REC + 1 + tid] : 0u;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) c += v[u];
+        }
+        ctot[tid] = c;
+        if (tid == 0) ctot[256] = 0u;
+    }
+    if (tid == 0) {                                          // defined even if no bin qualifies
+        pick[0] = 0u;
+        pick[1] = 0u;
+    }
+    __syncthreads();
+    // the low 8 bits f* of the k-th key: the largest f with ctot[f] >= r1
+    if (ctot[tid] >= r1 && ctot[tid + 1] < r1) {
+        pick[0] = (uint32_t)tid;
+        pick[1] = r1 - ctot[tid + 1];                        // keys equal to T taken
+    }
+    __syncthreads();
+    const uint32_t fstar = min(pick[0], 255u), rem = pick[1];   // fstar indexes cum[0..256]
+    const uint32_t T = (bstar << 8) | fstar;
+    // outputs of the segments before this one: their keys above T and their
+    // keys equal to T
+    uint32_t gtp = 0, eqp = 0;
+    for (int i = tid; i < sgi; i += SEL_NT) {
+        const uint32_t* ri = rr + (size_t)i * SEL_REC;
+        gtp += ri[0] + ri[1 + fstar + 1];
+        eqp += ri[1 + fstar] - ri[1 + fstar + 1];
+    }
+    int parity = 0;
+    uint32_t a0, b0, gt_before, eq_before;
+    block_exscan2(gtp, eqp, a0, b0, gt_before, eq_before, parity);
+    uint32_t out_base = gt_before + min(eq_before, rem);
+    uint32_t rem_left = rem - min(eq_before, rem);
+    for (int rnd = 0; rnd < rounds; ++rnd) {
+        const int p0 = s0 + rnd * SEL_ROUND;
+        if (p0 >= V) break;                                  // uniform
+        if (rnd > 0) sel_load(sr, nvec_row, p0, q);
+        const int base = p0 + tid * SEL_KPT;
+        const uint32_t w8[8] = {q[0].x, q[0].y, q[0].z, q[0].w, q[1].x, q[1].y, q[1].z, q[1].w};
+        uint32_t kp[8];
+        uint32_t gt = 0, eq = 0;
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+            kp[h] = key16x2(w8[h]);
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const uint32_t kv = (kp[h] >> (16 * half)) & 0xFFFFu;
+                const bool in = base + 2 * h + half < V;
+                gt += in && kv > T;
+                eq += in && kv == T;
+            }
+        }
+        uint32_t gtb, eqb, gtt, eqt;
+        block_exscan2(gt, eq, gtb, eqb, gtt, eqt, parity);
+        int oi = (int)(out_base + gtb + min(eqb, rem_left));
+        int take_eq = (int)min(eq, rem_left > eqb ? rem_left - eqb : 0u);
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int pos = base + 2 * h + half;
+                const uint32_t kv = (kp[h] >> (16 * half)) & 0xFFFFu;
+                if (pos < V && (kv > T || (kv == T && take_eq > 0)) && (unsigned)oi < (unsigned)k) {   // ranks below k
+                    take_eq -= kv == T;
+                    o[oi++] = pos;
+                }
+            }
+        }
+        out_base += gtt + min(eqt, rem_left);
+        rem_left -= min(eqt, rem_left);
+    }
+}
+
+// Rounds of SEL_ROUND keys per segment: doubled while a launch would have
+// more than 4096 segment workgroups, at most 8 (decode rows: one round).
+static int sel_rounds(int n_rows, int ld)
+{
+    const long keys = (long)n_rows * ld;
+    int r = 1;
+    while (r < 8 && keys / ((long)SEL_ROUND * r) > 4096) r *= 2;
+    return r;
+}
+
+size_t topk_hist_workspace(int n_rows, int ld)
+{
+    const int seg = sel_rounds(n_rows, ld) * SEL_ROUND;
+    return (size_t)n_rows * ((ld + seg - 1) / seg) * SEL_REC * 4;
+}
+
+hipError_t launch_topk_hist(hipStream_t st, int n_rows, const void* scores, int ld, const int32_t* n_valid,
+                            const uint16_t* hist, int hist_chunks, int chunk, int k, int32_t* out, void* ws)
+{
+    if (n_rows <= 0) return hipSuccess;
+    const int rounds = sel_rounds(n_rows, ld);
+    const int seg = rounds * SEL_ROUND;
+    const int nseg = (ld + seg - 1) / seg;
+    const dim3 grid(nseg, n_rows);
+    uint32_t* rec = (uint32_t*)ws;
+    topk_seg_count_kernel<<<grid, SEL_NT, 0, st>>>((const uint16_t*)scores, ld, n_valid, hist, hist_chunks, chunk, k,
+                                                   rounds, nseg, rec);
+    topk_seg_emit_kernel<<<grid, SEL_NT, 0, st>>>((const uint16_t*)scores, ld, n_valid, k, rounds, nseg, rec, out);
+    return hipGetLastError();
 }
 
 // Chunk length per first-stage workgroup.  A row that fits one workgroup is

@@ -111,6 +111,11 @@ class LayerState:
     def index(self, bi: BatchInfo, n_tokens: int, q_idx, w, scores, ld, n_valid, stream=None):
         abi.index_scores(self.desc, bi.batch, n_tokens, q_idx, w, self.idx, scores, ld, n_valid, stream=stream)
 
+    def index_topk(self, bi: BatchInfo, n_tokens: int, q_idx, w, scores, ld, n_valid, out_idx, stream=None):
+        ws = self.workspace("index_topk", abi.workspace_size(self.desc, abi.OP_INDEX_TOPK, n_tokens, ld))
+        abi.index_topk(self.desc, bi.batch, n_tokens, q_idx, w, self.idx, scores, ld, n_valid, out_idx, ws,
+                       stream=stream)
+
     def topk(self, n_rows: int, scores, ld: int, n_valid, out_idx, stream=None):
         d = self.desc
         ws = self.workspace("topk", abi.workspace_size(d, abi.OP_TOPK, n_rows, ld, d.top_k))

@@ -33,9 +33,11 @@ def torch_rows(seed: int):
 
 class DecodeWorkload:
     def __init__(self, descs, d_model: int, n_req: int, ctx: int, max_steps: int, rows, seed: int = 0,
-                 weight_std: float | None = None, fill_chunk: int = 1 << 16, fused_append: bool = True):
+                 weight_std: float | None = None, fill_chunk: int = 1 << 16, fused_append: bool = True,
+                 fused_topk: bool = True):
         self.descs = list(descs)
         self.fused_append = fused_append
+        self.fused_topk = fused_topk
         self.d = d_model
         self.n_req = n_req
         self.ctx = ctx
@@ -145,6 +147,7 @@ class DecodeWorkload:
                 b["n_valid"] = torch.empty(n, dtype=torch.int32, device=dev)
                 b["sel"] = torch.empty((n, desc.top_k), dtype=torch.int32, device=dev)
                 b["ws_t"] = st.workspace("topk", abi.workspace_size(desc, abi.OP_TOPK, n, self.ld, desc.top_k))
+                b["ws_it"] = st.workspace("index_topk", abi.workspace_size(desc, abi.OP_INDEX_TOPK, n, self.ld))
                 b["ld"] = self.ld
             self.bufs.append(b)
 
@@ -172,11 +175,16 @@ class DecodeWorkload:
         if st.is_csa:
             if hooks:
                 hooks[0]()
-            abi.index_scores(desc, bi.batch, n, b["qI"], b["w"], st.idx, b["scores"], b["ld"], b["n_valid"], stream=s)
-            if hooks:
-                hooks[1]()
-            abi.topk_select(desc.score_fmt, n, b["scores"], b["ld"], b["n_valid"], desc.top_k, b["sel"], b["ws_t"],
-                            stream=s)
+            if self.fused_topk:
+                abi.index_topk(desc, bi.batch, n, b["qI"], b["w"], st.idx, b["scores"], b["ld"], b["n_valid"],
+                               b["sel"], b["ws_it"], stream=s)
+            else:
+                abi.index_scores(desc, bi.batch, n, b["qI"], b["w"], st.idx, b["scores"], b["ld"], b["n_valid"],
+                                 stream=s)
+                if hooks:
+                    hooks[1]()
+                abi.topk_select(desc.score_fmt, n, b["scores"], b["ld"], b["n_valid"], desc.top_k, b["sel"],
+                                b["ws_t"], stream=s)
             abi.sparse_mqa(desc, bi.batch, n, b["q"], P["q_gamma"], b["sel"], st.kv, st.state, P["sinks"], b["out"],
                            b["ws_a"], stream=s)
         else:

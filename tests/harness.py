@@ -135,3 +135,83 @@ def ring_rows(st, desc, req, positions):
         rows = ring.view(torch.float32).view(desc.win_cap, desc.c)
     sl = torch.as_tensor(np.asarray(positions, np.int64) % desc.win_cap, device="cuda")
     return rows[sl].cpu().numpy()
+
+
+def _e4m3_table():
+    import oracle as O
+    return O.e4m3_decode(np.arange(256, dtype=np.uint8))
+
+
+def _bf16_value(bits):
+    return (np.asarray(bits, np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _grid_gap(grid, v):
+    """Spacing of the sorted value grid around |v| (the step a rounding at v can take)."""
+    a = abs(v)
+    i = int(np.searchsorted(grid, a))
+    lo = grid[max(0, min(i, len(grid) - 1) - 1)]
+    hi = grid[min(i, len(grid) - 1)]
+    return max(hi - lo, 0.0)
+
+
+def reconcile_fp8_blocks(spec, o_blocks, g_blocks, E32, rel=1e-4, slack=1e-5):
+    """The oracle's FP8 block bytes (o_blocks) made to agree with the GPU's
+    (g_blocks) where both are valid roundings of the same entry: the two
+    sides compute an entry in different summation orders (and the RoPE
+    angles in fp32 vs fp64), so a value near a rounding midpoint can get the
+    neighbouring code.  Accepted: a block scale within `rel` relative; a GPU
+    value (E4M3 code times the GPU's scale, or bf16 RoPE value) within half a
+    step of its format's grid plus `slack` times the larger of the value and
+    the entry's RMS of the oracle's unrounded value, i.e. a rounding of a
+    value at most that far from the oracle's.  Any other difference fails.  Entries are appended in
+    whole fresh blocks or fresh slots here (no scale raise re-encodes an
+    earlier slot), so the oracle's entry over the scale is the value each
+    code rounds.  Returns (blocks, number of values taken from the GPU)."""
+    tab = _e4m3_table()
+    fin = np.sort(np.unique(np.abs(tab[np.isfinite(tab)])))
+    bgrid = np.sort(np.unique(np.abs(_bf16_value(np.arange(0x7F80, dtype=np.uint32)))))
+    c, r, epb = spec.c, spec.r, spec.epb
+    nf, rec = c - r, (c - r) + 2 * r
+    out = np.array(o_blocks, copy=True)
+    E32 = np.asarray(E32, np.float32)
+    taken = 0
+    for b in range(o_blocks.shape[0]):
+        ob, gb = o_blocks[b], g_blocks[b]
+        if np.array_equal(ob, gb):
+            continue
+        so, sg = ob[:4].copy().view(np.float32)[0], gb[:4].copy().view(np.float32)[0]
+        assert abs(float(sg) - float(so)) <= rel * abs(float(so)), f"block {b}: scales {so} vs {sg}"
+        for slot in range(min(epb, E32.shape[0] - b * epb)):
+            i = b * epb + slot
+            o0 = 64 + slot * rec
+            tol_abs = slack * float(np.sqrt(np.mean(E32[i].astype(np.float64) ** 2)))
+            co, cg = ob[o0:o0 + nf], gb[o0:o0 + nf]
+            for ch in np.nonzero(co != cg)[0]:
+                x = float(np.float32(E32[i, ch]) / np.float32(sg))
+                vg = float(tab[cg[ch]])
+                t = max(tol_abs, slack * abs(float(E32[i, ch])))
+                assert abs(vg - x) <= 0.5 * _grid_gap(fin, x) + t / float(sg), \
+                    f"entry {i} ch {ch}: GPU code {cg[ch]} ({vg}) is no rounding of {x} (oracle code {co[ch]})"
+                out[b, o0 + ch] = cg[ch]
+                taken += 1
+            bo = ob[o0 + nf:o0 + rec].copy().view(np.uint16)
+            bg = gb[o0 + nf:o0 + rec].copy().view(np.uint16)
+            for k in np.nonzero(bo != bg)[0]:
+                x = float(E32[i, nf + k])
+                vg = float(_bf16_value(bg[k]))
+                assert abs(vg - x) <= 0.5 * _grid_gap(bgrid, x) + max(tol_abs, slack * abs(x)), \
+                    f"entry {i} rope ch {k}: GPU bf16 {bg[k]:#x} ({vg}) is no rounding of {x}"
+                out[b, o0 + nf + 2 * k:o0 + nf + 2 * k + 2] = gb[o0 + nf + 2 * k:o0 + nf + 2 * k + 2]
+                taken += 1
+        out[b, :4] = gb[:4]
+    return out, taken
+
+
+def decode_fp8_blocks(spec, blocks, n_entries):
+    """Dequantised entries (fp64) of n_entries entries held in blocks."""
+    import oracle as O
+    deq = np.zeros((n_entries, spec.c), np.float64)
+    for i in range(n_entries):
+        deq[i] = O.fp8_block_decode(blocks[i // spec.epb], spec.c, spec.r, spec.epb, i % spec.epb)
+    return deq

@@ -359,7 +359,8 @@ ATTN_CASES = {
     "fp8_hca_128h": (presets.hca_pro(), [[70000, 1], [20000, 1]]),
     # sinks of -inf (the ordinary softmax) and queries that see no compressed
     # entry yet (V = 0: window rows only; V = 1), 128 heads, FP8 entries
-    "fp8_sparse_128h_sink_neg_inf": (presets.csa_pro(), [[0, 1], [2, 1], [3, 1], [130, 1], [5000, 2]], "-inf"),
+    "fp8_sparse_128h_sink_neg_inf": (presets.csa_pro(win_cap=256), [[0, 1], [2, 1], [3, 1], [130, 1], [5000, 2]],
+                                     "-inf"),
 }
 
 

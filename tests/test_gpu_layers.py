@@ -83,7 +83,19 @@ def gpu_layer_call(st, desc, P, start, n_new, bt, H, q, qI=None, w=None, max_ctx
         st.index(bi, T, to_dev(qI, adt), to_dev(w), scores, ld, nv)
         sel = torch.empty((T, desc.top_k), dtype=torch.int32, device="cuda")
         st.topk(T, scores, ld, nv, sel)
+        # the fused index + top-k on the same inputs: identical scores, counts
+        # and selection, bit for bit
+        sc2 = torch.zeros_like(scores)
+        nv2 = torch.empty_like(nv)
+        sel2 = torch.full_like(sel, -7)
+        st.index_topk(bi, T, to_dev(qI, adt), to_dev(w), sc2, ld, nv2, sel2)
         st.attend(bi, T, to_dev(q, adt), dv["q_gamma"], dv["sinks"], o, sel=sel)
+        torch.cuda.synchronize()
+        assert torch.equal(nv2, nv), "fused index_topk: n_valid differs"
+        assert torch.equal(sc2.view(torch.int16 if sc2.dtype == torch.bfloat16 else torch.int32),
+                           scores.view(torch.int16 if scores.dtype == torch.bfloat16 else torch.int32)), \
+            "fused index_topk: scores differ"
+        assert torch.equal(sel2, sel), "fused index_topk: selection differs from topk_select"
         out.update(scores=scores, n_valid=nv, sel=sel)
     else:
         st.attend(bi, T, to_dev(q, adt), dv["q_gamma"], dv["sinks"], o)

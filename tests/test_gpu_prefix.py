@@ -69,4 +69,5 @@ def test_prefix_save_and_restore(kind, flags):
     assert blocks.numel() == abi.prefix_bytes(desc, P_len // desc.block_tokens)
     print(f"  restored run bit-identical over {steps} steps", flush=True)
     # and the (identical) outputs against the oracle
-    oracle_check_request(desc, P, x, [(0, P_len)] + [(P_len + i, 1) for i in range(steps)], [None] + got)
+    oracle_check_request(desc, P, x, [(0, P_len)] + [(P_len + i, 1) for i in range(steps)], [None] + got, st=st2,
+                         bt_row=bt2[0])
