@@ -378,7 +378,11 @@ def time_decode(name, steps, warmup, replicas=0, graph=True, fused_append=True, 
 
 def time_prefill(steps, warmup):
     """One 4096-token chunk on top of 1,048,576 cached tokens (Pro shape):
-    compress_kv, cache_append, index_scores, topk_select, sparse_mqa."""
+    compress_kv, cache_append, the fused index_topk, sparse_mqa.  The
+    roofline times the index scan alone (csa_index_scores, the same kernel
+    without the fused selection's per-chunk counts) right after the steps;
+    the standalone selector (csa_topk_select) on the same scores is timed
+    too, for comparison."""
     import torch
     from long_context_sparse_03_amd import abi, presets
     from long_context_sparse_03_amd import abi
@@ -412,6 +416,7 @@ def time_prefill(steps, warmup):
     out = torch.empty((T, desc.n_heads, desc.c), dtype=torch.bfloat16, device=dev)
     ws_a = torch.empty(max(1, abi.workspace_size(desc, abi.OP_ATTENTION, T, desc.top_k + desc.n_win)),
                        dtype=torch.uint8, device=dev)
+    ws_it = torch.empty(max(1, abi.workspace_size(desc, abi.OP_INDEX_TOPK, T, ld)), dtype=torch.uint8, device=dev)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
 
     def step():
@@ -420,43 +425,55 @@ def time_prefill(steps, warmup):
                         P["gamma"], st.state, ent, keys, meta, cnt, n_e, win, ws_c)
         abi.cache_append(desc, bi.batch, T, ent, keys, meta, cnt, n_e, win, st.kv, st.idx, st.state)
         ev[1].record()
-        abi.index_scores(desc, bi.batch, T, qI, w, st.idx, scores, ld, nv)
+        abi.index_topk(desc, bi.batch, T, qI, w, st.idx, scores, ld, nv, sel, ws_it)
         ev[2].record()
-        abi.topk_select(desc.score_fmt, T, scores, ld, nv, desc.top_k, sel, ws_t)
-        ev[3].record()
         abi.sparse_mqa(desc, bi.batch, T, q, P["q_gamma"], sel, st.kv, st.state, P["sinks"], out, ws_a)
-        ev[4].record()
+        ev[3].record()
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    parts = np.zeros(4)
+    parts = np.zeros(3)
     tot = 0.0
     for _ in range(steps):
         step()
         torch.cuda.synchronize()
-        e = [ev[i].elapsed_time(ev[i + 1]) for i in range(4)]
-        parts += e
-        tot += ev[0].elapsed_time(ev[4])
+        parts += [ev[i].elapsed_time(ev[i + 1]) for i in range(3)]
+        tot += ev[0].elapsed_time(ev[3])
     parts /= steps
     ms = tot / steps
+    # the index scan alone (roofline) and the standalone selector, each
+    # timed over `steps` launches on the scores the last step left
+    ev[4].record()
+    for _ in range(steps):
+        abi.index_scores(desc, bi.batch, T, qI, w, st.idx, scores, ld, nv)
+    ev[5].record()
+    torch.cuda.synchronize()
+    ms_index = ev[4].elapsed_time(ev[5]) / steps
+    ev[4].record()
+    for _ in range(steps):
+        abi.topk_select(desc.score_fmt, T, scores, ld, nv, desc.top_k, sel, ws_t)
+    ev[5].record()
+    torch.cuda.synchronize()
+    ms_topk_standalone = ev[4].elapsed_time(ev[5]) / steps
     E = ctx // desc.m
     sumV = sum((ctx + t + 1) // desc.m for t in range(T))
     idx_flop = 2.0 * desc.n_idx_heads * desc.c_idx * sumV
     attn_flop = 4.0 * desc.n_heads * desc.c * T * (desc.top_k + desc.n_win)
     proj_flop = 2.0 * T * d * (4 * desc.c + 4 * desc.c_idx)
-    idx_tfs = idx_flop / (parts[1] * 1e-3) / 1e12
+    idx_tfs = idx_flop / (ms_index * 1e-3) / 1e12
     del wl
     torch.cuda.empty_cache()
     return {"workload": "csa_prefill_1m", "tokens_per_s": round(T / (ms * 1e-3), 1), "ms_per_chunk": round(ms, 3),
             "chunk": T, "ctx": ctx, "d": d,
-            "ms_compress_append": round(parts[0], 3), "ms_index": round(parts[1], 3), "ms_topk": round(parts[2], 3),
-            "ms_attention": round(parts[3], 3),
+            "ms_compress_append": round(parts[0], 3), "ms_index_topk": round(parts[1], 3),
+            "ms_attention": round(parts[2], 3), "ms_index": round(ms_index, 3),
+            "ms_topk_standalone": round(ms_topk_standalone, 3),
             "tflops_total": round((idx_flop + attn_flop + proj_flop) / (ms * 1e-3) / 1e12, 1),
             "roofline": {"bound": "mfma", "kernel": "index_prefill_kernel", "achieved": round(idx_tfs, 1),
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(idx_tfs / BF16_PEAK_TFLOPS, 4),
                          "traffic": None, "algorithmic_flop_per_launch": idx_flop},
-            "attention_tflops": round(attn_flop / (parts[3] * 1e-3) / 1e12, 1)}
+            "attention_tflops": round(attn_flop / (parts[2] * 1e-3) / 1e12, 1)}
 
 
 def time_small(name: str, reps: int = 5):

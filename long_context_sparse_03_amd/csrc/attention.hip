@@ -978,14 +978,15 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
 // normalise, rotate back at -t and store.  The weights and the denominator
 // come from fixed-order reductions, so the result does not depend on
 // scheduling.
-constexpr int CB = 8;                                          // splits whose channels load in one batch
-// One wave per (query, head), four per workgroup, no LDS and no barrier: lane
-// l holds split l's (max, sum) (64 splits at a time) and output channels
-// 8l .. 8l+7.  The reference max M (with the sink) and the denominator are
-// wave reductions (butterfly; further chunks of 64 splits added in order);
-// every lane then adds its channels of each split in split order, weighted
-// 2^(m_s - M), and rotates its channel pairs of the RoPE part back by the
-// query position.
+constexpr int CB = 16;                                         // splits whose loads are issued together
+// One wave per (query, head), four per workgroup, no LDS, no barrier and no
+// exchange between lanes: lane l holds output channels 8l .. 8l+7 and reads
+// every split's (max, sum) itself (the same addresses in every lane, one
+// memory request per wave), so the reference max M (with the sink), the
+// denominator and the weighted sum of the partial outputs are formed in
+// split order, alike in every lane.  The loads of a batch of CB splits (their
+// (max, sum) and the lane's channels) are all issued before any is used, so
+// up to CB splits cost one round trip to memory.
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a)
 {
     const int lane = threadIdx.x & 63;
@@ -997,53 +998,47 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a)
     const char* pp = (const char*)a.ws + ((size_t)gq * a.nh + head) * S * pstride;
     const int d0 = 8 * lane;
     const bool dv = d0 < C;
-    // loads first: (max, sum) of split `lane`, the lane's channels of the
-    // first CB splits, the position
-    const float2 ml0 = lane < S ? *(const float2*)(pp + (size_t)lane * pstride) : make_float2(-INFINITY, 0.f);
+    // a batch of CB splits from split s0: (max, sum) and this lane's channels
+    float2 ml[CB];
     uint4 ov[CB][2];
+    auto load_batch = [&](int s0) {
 #pragma unroll
-    for (int sb = 0; sb < CB; ++sb) {
-        const char* src = pp + (size_t)min(sb, S - 1) * pstride + 16;
-        ov[sb][0] = ov[sb][1] = make_uint4(0u, 0u, 0u, 0u);
-        if (dv && sb < S) {
-            if (bf) {
-                ov[sb][0] = *(const uint4*)(src + 2 * (size_t)d0);
-            } else {
-                ov[sb][0] = *(const uint4*)(src + 4 * (size_t)d0);
-                ov[sb][1] = *(const uint4*)(src + 4 * (size_t)d0 + 16);
+        for (int sb = 0; sb < CB; ++sb) {
+            const char* src = pp + (size_t)min(s0 + sb, S - 1) * pstride;
+            ml[sb] = *(const float2*)src;
+            ov[sb][0] = ov[sb][1] = make_uint4(0u, 0u, 0u, 0u);
+            if (dv) {
+                if (bf) {
+                    ov[sb][0] = *(const uint4*)(src + 16 + 2 * (size_t)d0);
+                } else {
+                    ov[sb][0] = *(const uint4*)(src + 16 + 4 * (size_t)d0);
+                    ov[sb][1] = *(const uint4*)(src + 16 + 4 * (size_t)d0 + 16);
+                }
             }
         }
-    }
-    int req, tok;
-    if (a.one_per_req) {
-        req = gq;
-        tok = 0;
-    } else {
-        req = find_request(a.cu_new, a.n_req, gq);
-        tok = gq - a.cu_new[req];
-    }
-    const int t = a.start_pos[req] + tok;
+    };
+    load_batch(0);
     const float zs = a.sinks[head] * LOG2E;
-    // the common reference max (with the sink)
-    float M = ml0.x;
-    for (int s0 = 64; s0 < S; s0 += 64)
-        M = fmaxf(M, s0 + lane < S ? *(const float*)(pp + (size_t)(s0 + lane) * pstride) : -INFINITY);
-    M = fmaxf(wave_max(M), zs);
-    // the denominator: sum of l_s * 2^(m_s - M)
-    float L = wave_sum(ml0.y * (ml0.x == -INFINITY ? 0.f : exp2f(ml0.x - M)));
-    for (int s0 = 64; s0 < S; s0 += 64) {
-        const float2 v = s0 + lane < S ? *(const float2*)(pp + (size_t)(s0 + lane) * pstride)
-                                       : make_float2(-INFINITY, 0.f);
-        L += wave_sum(v.y * (v.x == -INFINITY ? 0.f : exp2f(v.x - M)));
+    // the common reference max (with the sink): the first batch's maxima,
+    // then those of any further splits
+    float M = zs;
+#pragma unroll
+    for (int sb = 0; sb < CB; ++sb)
+        if (sb < S) M = fmaxf(M, ml[sb].x);
+    for (int s0 = CB; s0 < S; s0 += CB) {                       // further maxima, CB loads at a time
+        float mb[CB];
+#pragma unroll
+        for (int sb = 0; sb < CB; ++sb) mb[sb] = *(const float*)(pp + (size_t)min(s0 + sb, S - 1) * pstride);
+#pragma unroll
+        for (int sb = 0; sb < CB; ++sb) M = fmaxf(M, mb[sb]);
     }
-    const float inv = 1.0f / (exp2f(zs - M) + L);
-    // weighted sum of the partial outputs in split order
+    // the denominator and the weighted sum of the partial outputs, in split order
+    float L = 0.f;
     float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    auto accum = [&](int sidx, const uint4& u0, const uint4& u1) {
-        const float ms = sidx < 64 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ml0.x), sidx))
-                                   : *(const float*)(pp + (size_t)sidx * pstride);
-        const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
+    auto accum = [&](float2 msl, const uint4& u0, const uint4& u1) {
+        const float w = msl.x == -INFINITY ? 0.f : exp2f(msl.x - M);
         if (w == 0.f) return;                                  // empty splits add nothing, not even +0
+        L += msl.y * w;
         float v[8];
         if (bf) {
             const uint32_t h[4] = {u0.x, u0.y, u0.z, u0.w};
@@ -1062,41 +1057,39 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a)
     };
 #pragma unroll
     for (int sb = 0; sb < CB; ++sb)
-        if (sb < S) accum(sb, ov[sb][0], ov[sb][1]);
-    // further splits in batches of CB, each batch's loads issued before its
-    // accumulation (same order of additions)
+        if (sb < S) accum(ml[sb], ov[sb][0], ov[sb][1]);
     for (int s0 = CB; s0 < S; s0 += CB) {
-#pragma unroll
-        for (int sb = 0; sb < CB; ++sb) {
-            const char* src = pp + (size_t)min(s0 + sb, S - 1) * pstride + 16;
-            ov[sb][0] = ov[sb][1] = make_uint4(0u, 0u, 0u, 0u);
-            if (dv) {
-                if (bf) {
-                    ov[sb][0] = *(const uint4*)(src + 2 * (size_t)d0);
-                } else {
-                    ov[sb][0] = *(const uint4*)(src + 4 * (size_t)d0);
-                    ov[sb][1] = *(const uint4*)(src + 4 * (size_t)d0 + 16);
-                }
-            }
-        }
+        load_batch(s0);
 #pragma unroll
         for (int sb = 0; sb < CB; ++sb)
-            if (s0 + sb < S) accum(s0 + sb, ov[sb][0], ov[sb][1]);
+            if (s0 + sb < S) accum(ml[sb], ov[sb][0], ov[sb][1]);
     }
     if (!dv) return;
+    const float inv = 1.0f / (exp2f(zs - M) + L);
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] *= inv;
     // channel pairs (d, d+1) of the RoPE part: nf is even, so pairs never
     // straddle a lane's eight channels or the RoPE boundary
+    if (d0 + 8 > nf) {
+        int req, tok;
+        if (a.one_per_req) {
+            req = gq;
+            tok = 0;
+        } else {
+            req = find_request(a.cu_new, a.n_req, gq);
+            tok = gq - a.cu_new[req];
+        }
+        const int t = a.start_pos[req] + tok;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int d = d0 + 2 * q;
-        if (d >= nf) {
-            float cs, sn;
-            rope_cs_f((double)t, a.inv_freq[(d - nf) >> 1], &cs, &sn);
-            const float u0 = o[2 * q], u1 = o[2 * q + 1];
-            o[2 * q] = u0 * cs + u1 * sn;
-            o[2 * q + 1] = -u0 * sn + u1 * cs;
+        for (int q = 0; q < 4; ++q) {
+            const int d = d0 + 2 * q;
+            if (d >= nf) {
+                float cs, sn;
+                rope_cs_f((double)t, a.inv_freq[(d - nf) >> 1], &cs, &sn);
+                const float u0 = o[2 * q], u1 = o[2 * q + 1];
+                o[2 * q] = u0 * cs + u1 * sn;
+                o[2 * q + 1] = -u0 * sn + u1 * cs;
+            }
         }
     }
     const size_t ob = ((size_t)gq * a.nh + head) * C + d0;
