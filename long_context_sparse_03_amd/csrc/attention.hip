@@ -559,15 +559,17 @@ __global__ __launch_bounds__((AttnCfg<KVF, C, R, HT>::NT)) void attn_kernel(Attn
 
 // FP8 entry records with bf16 queries (the serving shapes): two waves per
 // head tile.  Waves w and w + HT own heads 16w .. 16w+15 of the group and one
-// half of the channels each: each contracts its half of the tile for those
-// heads (S^T = K . Q^T), the two partial logits meet in LDS and are summed
-// in the same order by both waves, both run the same online softmax in
-// registers, and each accumulates the output of its half of the channels
-// (O^T = V^T . P^T).  Tiles are double-buffered in LDS: the rows of the next
-// two tiles are loaded into registers while one computes, and two barriers
-// per tile publish a stored tile and the partial logits.  Each lane keeps
-// the output of its head for 4 channels of every 16-channel group of its
-// half (C/8 fp32 accumulators).
+// half of the channels each (alternate 32-channel MFMA steps for the logits,
+// alternate 16-channel tiles for the output, so that both halves have the
+// same mix of FP8 and rotary channels at the same positions): each contracts
+// its half of the tile for those heads (S^T = K . Q^T), the two partial
+// logits meet in LDS and are summed in the same order by both waves, both
+// run the same online softmax in registers, and each accumulates the output
+// of its half of the channels (O^T = V^T . P^T).  Tiles are double-buffered
+// in LDS: the rows of the next two tiles are loaded into registers while one
+// computes, and two barriers per tile publish a stored tile and the partial
+// logits.  Each lane keeps the output of its head for 4 channels of every
+// 16-channel tile of its half (C/8 fp32 accumulators).
 template <int C, int R, int HT>
 __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
 {
@@ -583,8 +585,12 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
     constexpr int EB = NF + 2 * R;                             // bytes of an FP8 entry record
     constexpr int NCH = NF / 16;                               // 16-byte chunks of FP8 codes
     constexpr int DESC = NT;                                   // rows described at a time
-    static_assert(NF % 32 == 0 && R % 32 == 0 && WB <= 1024 && 32 % NWV == 0 && DESC % NT == 0 && DT % 2 == 0,
-                  "shape");
+    static_assert(NF % 32 == 0 && R % 32 == 0 && WB <= 1024 && 32 % NWV == 0 && DESC % NT == 0 && DT % 2 == 0 &&
+                  KSN % 2 == 0 && DTN % 2 == 0, "shape");
+    // The two waves of a head tile take alternate 32-channel MFMA steps
+    // (step 2j + half) and alternate 16-channel output tiles (tile 2j + half):
+    // both then meet the FP8 / rotary boundary at the same j, so which
+    // accumulator or which P a step uses is known at compile time.
 
     __shared__ __attribute__((aligned(16))) uint16_t Kt[2][32 * KP];
     __shared__ float tscl[2][32];                              // per buffer: row scales ...
@@ -609,11 +615,11 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
 
     // query fragments (B operand of S^T): channels 32s + 8g .. +7 of `head`,
     // loaded first so that their latency overlaps the lookups below
-    uint4 QB[KSH];                                             // this wave's half: steps KSH*half + j
+    uint4 QB[KSH];                                             // this wave's steps 2j + half
     {
         const char* qp = (const char*)a.q + ((size_t)gq * a.nh + (hvalid ? head : 0)) * C * 2;
 #pragma unroll
-        for (int j = 0; j < KSH; ++j) QB[j] = ld16(qp + (size_t)(32 * (KSH * half + j) + 8 * g) * 2);
+        for (int j = 0; j < KSH; ++j) QB[j] = ld16(qp + (size_t)(32 * (2 * j + half) + 8 * g) * 2);
     }
     // selected entries of this workgroup's first rows (independent of the
     // position, so these loads overlap its lookup)
@@ -730,8 +736,7 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
                 ss += x0 * x0 + x1 * x1;
             }
         }
-        ss += __shfl_xor(ss, 16, 64);
-        ss += __shfl_xor(ss, 32, 64);
+        ss = xsum32(xsum16(ss));
         if (g == 0) ssx[ht][half][li] = ss;
     }
     __syncthreads();
@@ -752,7 +757,7 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
         const float inv = hvalid ? 1.0f / sqrtf(ss / (float)C + a.eps) : 0.f;
 #pragma unroll
         for (int j = 0; j < KSH; ++j) {
-            const int s = KSH * half + j;
+            const int s = 2 * j + half;
             const int d0 = 32 * s + 8 * g;
             const float4 ga = *(const float4*)(gam + d0), gb = *(const float4*)(gam + d0 + 4);
             const float gm[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
@@ -763,7 +768,7 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
                 x[2 * h] = gm[2 * h] * (bf16_to_f32(w4[h] & 0xFFFF) * inv);
                 x[2 * h + 1] = gm[2 * h + 1] * (bf16_to_f32(w4[h] >> 16) * inv);
             }
-            if (s >= KSN) {
+            if (j >= KSN / 2) {                                // the rotary steps (compile-time)
 #pragma unroll
                 for (int j = 0; j < 8; j += 2) {
                     const int pr = (d0 + j - NF) >> 1;
@@ -779,7 +784,7 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
         }
     }
 
-    // lane (g, li): O^T[16 (DTH half + j) + 4g + i][head li]
+    // lane (g, li): O^T[16 (2j + half) + 4g + i][head li]
     f32x4_t O[DTH];
 #pragma unroll
     for (int j = 0; j < DTH; ++j) O[j] = zero4();
@@ -810,7 +815,7 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
         auto read_k = [&](int c, uint4 (&f)[QC][2]) {
 #pragma unroll
             for (int u = 0; u < QC; ++u) {
-                const int s = KSH * half + QC * c + u;
+                const int s = 2 * (QC * c + u) + half;
                 f[u][0] = *(const uint4*)(kt + li * KP + 32 * s + 8 * g);
                 f[u][1] = *(const uint4*)(kt + (16 + li) * KP + 32 * s + 8 * g);
             }
@@ -823,7 +828,7 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
 #pragma unroll
             for (int u = 0; u < QC; ++u) {
                 const int j = QC * c + u;
-                if (KSH * half + j < KSN) {                     // wave-uniform
+                if (j < KSN / 2) {                             // compile-time
                     an[0] = MmaBF16::step(kf[c & 1][u][0], QF[j], an[0]);
                     an[1] = MmaBF16::step(kf[c & 1][u][1], QF[j], an[1]);
                 } else {
@@ -861,8 +866,7 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
         float mx = sv[0];
 #pragma unroll
         for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx = xmax32(xmax16(mx));
         // the reference max moves only when a logit exceeds it by more than
         // 2^8 (base 2), so weights stay <= 256 and rescales are rare
         const bool raise = mx > m_run + 8.0f;
@@ -876,8 +880,7 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
             p[i] = __builtin_amdgcn_exp2f(sv[i] - m_use);
             ps += p[i];
         }
-        ps += __shfl_xor(ps, 16, 64);
-        ps += __shfl_xor(ps, 32, 64);
+        ps = xsum32(xsum16(ps));
         l_run = l_run * alpha + ps;
         m_run = m_new;
         if (__any(rescale)) {
@@ -901,7 +904,7 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
         auto read_v = [&](int c, uint4 (&f)[VC]) {
 #pragma unroll
             for (int u = 0; u < VC; ++u) {
-                const int dt = DTH * half + VC * c + u;
+                const int dt = 2 * (VC * c + u) + half;
                 const uint16_t* base = kt + (4 * g + (li >> 2)) * KP + 16 * dt + 4 * (li & 3);
                 const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS s16x4_t*)base);
                 const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS s16x4_t*)(base + 16 * KP));
@@ -917,8 +920,7 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
 #pragma unroll
             for (int u = 0; u < VC; ++u) {
                 const int j = VC * c + u;
-                const int dt = DTH * half + j;
-                O[j] = MmaBF16::step(vf[c & 1][u], dt < DTN ? psc : pp, O[j]);
+                O[j] = MmaBF16::step(vf[c & 1][u], j < DTN / 2 ? psc : pp, O[j]);   // compile-time choice
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -938,9 +940,9 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
         const float inv = sc / (l_run * sc + exp2f(zs - M));
 #pragma unroll
         for (int j = 0; j < DTH; ++j) {
-            const int d = 16 * (DTH * half + j) + 4 * g;
+            const int d = 16 * (2 * j + half) + 4 * g;
             float o[4] = {O[j][0] * inv, O[j][1] * inv, O[j][2] * inv, O[j][3] * inv};
-            if (d >= NF) {
+            if (j >= DTN / 2) {                                // the rotary channels (compile-time)
 #pragma unroll
                 for (int j = 0; j < 4; j += 2) {               // rotate back at -t
                     const int pj = (d + j - NF) >> 1;
@@ -964,7 +966,7 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
         }
 #pragma unroll
         for (int j = 0; j < DTH; ++j) {
-            const int d = 16 * (DTH * half + j) + 4 * g;
+            const int d = 16 * (2 * j + half) + 4 * g;
             if (a.out_bf16)
                 *(uint2*)(pp + 16 + 2 * (size_t)d) = make_uint2(pack_bf16x2(O[j][0], O[j][1]),
                                                                 pack_bf16x2(O[j][2], O[j][3]));

@@ -193,6 +193,30 @@ CSA_DEV int find_request(const int32_t* cu_new, int n_req, int g)
 // reductions (fixed order: butterfly over the wave, then waves in index order)
 // ---------------------------------------------------------------------------
 
+// Max / sum of v over lanes l and l ^ 16 (l ^ 32): gfx950's permlane swaps
+// hand every lane both values, lower lane first, so both lanes of a pair
+// get the same result.
+CSA_DEV float xmax16(float v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+CSA_DEV float xsum16(float v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+CSA_DEV float xmax32(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+CSA_DEV float xsum32(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 CSA_DEV float wave_sum(float v)
 {
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
