@@ -980,7 +980,6 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
 // normalise, rotate back at -t and store.  The weights and the denominator
 // come from fixed-order reductions, so the result does not depend on
 // scheduling.
-constexpr int CB = 16;                                         // splits whose loads are issued together
 // One wave per (query, head), four per workgroup, no LDS, no barrier and no
 // exchange between lanes: lane l holds output channels 8l .. 8l+7 and reads
 // every split's (max, sum) itself (the same addresses in every lane, one
@@ -988,35 +987,31 @@ constexpr int CB = 16;                                         // splits whose l
 // denominator and the weighted sum of the partial outputs are formed in
 // split order, alike in every lane.  The loads of a batch of CB splits (their
 // (max, sum) and the lane's channels) are all issued before any is used, so
-// up to CB splits cost one round trip to memory.
+// up to CB splits cost one round trip to memory (CB = 32 for more than 16
+// bf16 partials, else 16; fp32 channels take twice the registers).
+template <bool BF, int CB>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a)
 {
     const int lane = threadIdx.x & 63;
     const int gq = blockIdx.x, head = blockIdx.y * 4 + (int)(threadIdx.x >> 6);
     if (head >= a.nh) return;                                  // wave-uniform
     const int C = a.c, S = a.n_splits, nf = C - a.r;
-    const bool bf = a.out_bf16;
+    constexpr bool bf = BF;
     const size_t pstride = bf ? 2 * (size_t)C + 16 : 4 * (size_t)C + 16;
     const char* pp = (const char*)a.ws + ((size_t)gq * a.nh + head) * S * pstride;
     const int d0 = 8 * lane;
     const bool dv = d0 < C;
     // a batch of CB splits from split s0: (max, sum) and this lane's channels
     float2 ml[CB];
-    uint4 ov[CB][2];
+    uint4 ov[CB][BF ? 1 : 2];
     auto load_batch = [&](int s0) {
 #pragma unroll
         for (int sb = 0; sb < CB; ++sb) {
             const char* src = pp + (size_t)min(s0 + sb, S - 1) * pstride;
             ml[sb] = *(const float2*)src;
-            ov[sb][0] = ov[sb][1] = make_uint4(0u, 0u, 0u, 0u);
-            if (dv) {
-                if (bf) {
-                    ov[sb][0] = *(const uint4*)(src + 16 + 2 * (size_t)d0);
-                } else {
-                    ov[sb][0] = *(const uint4*)(src + 16 + 4 * (size_t)d0);
-                    ov[sb][1] = *(const uint4*)(src + 16 + 4 * (size_t)d0 + 16);
-                }
-            }
+#pragma unroll
+            for (int h = 0; h < (BF ? 1 : 2); ++h)
+                ov[sb][h] = dv ? *(const uint4*)(src + 16 + (BF ? 2 : 4) * (size_t)d0 + 16 * h) : make_uint4(0u, 0u, 0u, 0u);
         }
     };
     load_batch(0);
@@ -1037,20 +1032,20 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a)
     // the denominator and the weighted sum of the partial outputs, in split order
     float L = 0.f;
     float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    auto accum = [&](float2 msl, const uint4& u0, const uint4& u1) {
+    auto accum = [&](float2 msl, const uint4 (&u)[BF ? 1 : 2]) {
         const float w = msl.x == -INFINITY ? 0.f : exp2f(msl.x - M);
         if (w == 0.f) return;                                  // empty splits add nothing, not even +0
         L += msl.y * w;
         float v[8];
-        if (bf) {
-            const uint32_t h[4] = {u0.x, u0.y, u0.z, u0.w};
+        if constexpr (BF) {
+            const uint32_t h[4] = {u[0].x, u[0].y, u[0].z, u[0].w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 v[2 * i] = bf16_to_f32(h[i] & 0xFFFF);
                 v[2 * i + 1] = bf16_to_f32(h[i] >> 16);
             }
         } else {
-            const uint32_t h[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+            const uint32_t h[8] = {u[0].x, u[0].y, u[0].z, u[0].w, u[1].x, u[1].y, u[1].z, u[1].w};
 #pragma unroll
             for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(h[i]);
         }
@@ -1059,12 +1054,12 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a)
     };
 #pragma unroll
     for (int sb = 0; sb < CB; ++sb)
-        if (sb < S) accum(ml[sb], ov[sb][0], ov[sb][1]);
+        if (sb < S) accum(ml[sb], ov[sb]);
     for (int s0 = CB; s0 < S; s0 += CB) {
         load_batch(s0);
 #pragma unroll
         for (int sb = 0; sb < CB; ++sb)
-            if (s0 + sb < S) accum(ml[sb], ov[sb][0], ov[sb][1]);
+            if (s0 + sb < S) accum(ml[sb], ov[sb]);
     }
     if (!dv) return;
     const float inv = 1.0f / (exp2f(zs - M) + L);
@@ -1183,7 +1178,12 @@ hipError_t launch_attention(hipStream_t st, AttnArgs a)
         attn_ht_kernel<512, 64, 4><<<grid, 512, 0, st>>>(a);     // FP8 serving shapes: two waves per head tile
     else if (ht == 4) launch_ht<4>(st, a, grid);
     else launch_ht<1>(st, a, grid);
-    if (a.n_splits > 1 || a.invariant) attn_combine_kernel<<<dim3(a.n_tokens, (a.nh + 3) / 4), 256, 0, st>>>(a);
+    if (a.n_splits > 1 || a.invariant) {
+        const dim3 cg(a.n_tokens, (a.nh + 3) / 4);
+        if (a.out_bf16 && a.n_splits > 16) attn_combine_kernel<true, 32><<<cg, 256, 0, st>>>(a);
+        else if (a.out_bf16) attn_combine_kernel<true, 16><<<cg, 256, 0, st>>>(a);
+        else attn_combine_kernel<false, 16><<<cg, 256, 0, st>>>(a);
+    }
     return hipGetLastError();
 }
 
