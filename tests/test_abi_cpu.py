@@ -115,6 +115,8 @@ def test_workspace_sizes():
     assert P.workspace_size(d, abi.OP_TOPK, 16, 40961, 512) == 16 * 3 * 512 * 8    # 3 chunks of 13696
     assert P.workspace_size(d, abi.OP_TOPK, 4, 262144, 1024) == 4 * 16 * 1024 * 8  # 16 chunks of 16384
     assert P.workspace_size(d, abi.OP_TOPK, 4096, 262144, 1024) == 4096 * 7 * 1024 * 8   # many rows: 40960
+    # the 1M decode rows (ld 262,208): 17 equal chunks of 15,424 keys
+    assert P.workspace_size(presets.csa_pro(), abi.OP_TOPK, 4, 262208, 1024) == 4 * 17 * 1024 * 8
     assert P.workspace_size(d, abi.OP_ATTENTION, 16, 640) > 0               # few queries: split-KV partials
     assert P.workspace_size(d, abi.OP_ATTENTION, 4096, 640) == 0
     # batch-invariant layer: partials of splits every 128 rows, whatever the

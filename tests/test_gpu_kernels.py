@@ -175,6 +175,30 @@ def test_topk_exact(fmt, V, k):
         assert np.array_equal(got[t], want[t]), f"row {t} (V={V[t]}) differs"
 
 
+def test_topk_exact_rows_past_2_18():
+    """The 1M decode shape: rows of up to 262,208 bf16 scores (ld 262,208,
+    k 1024), which the standalone selector splits into 17 chunks merged by
+    its 24-keys-per-thread instance; selections equal the oracle's."""
+    V = [262208, 262145, 200000, 262207]
+    ld, k = 262208, 1024
+    _flush(f"topk bf16 k={k} ld={ld} V={V}")
+    g = synth.rng(103)
+    sc = O.bf16_round(synth.normal(g, (len(V), ld)))
+    sc[1, ::5] = sc[1, 3]                            # ties
+    nv = np.array(V, np.int32)
+    want = O.topk(sc, nv, k)
+    desc = presets.csa_pro()
+    nbytes = abi.workspace_size(desc, abi.OP_TOPK, len(V), ld, k)
+    assert nbytes == len(V) * 17 * k * 8
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.full((len(V), k), -7, dtype=torch.int32, device="cuda")
+    abi.topk_select(abi.ACT_BF16, len(V), to_dev(sc, torch.bfloat16), ld, i32(nv), k, out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for t in range(len(V)):
+        assert np.array_equal(got[t], want[t]), f"row {t} (V={V[t]}) differs"
+
+
 # ---------------------------------------------------------------------------
 # a3: index scores
 # ---------------------------------------------------------------------------
