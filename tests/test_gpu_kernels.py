@@ -375,6 +375,11 @@ def test_index_prefill_matches_decode():
 # a5 / a6: attention with window and sink, on shared inputs
 # ---------------------------------------------------------------------------
 
+def _invariant(d):
+    d.flags = abi.FLAG_BATCH_INVARIANT
+    return d
+
+
 ATTN_CASES = {
     "f32_sparse": (presets.tiny_csa_fp32(win_cap=512), [[600, 2], [130, 1], [2050, 40]]),
     "bf16_hca": (presets.hca_bf16(win_cap=1024), [[8192, 3], [700, 2], [127, 1]]),
@@ -385,6 +390,9 @@ ATTN_CASES = {
     # entry yet (V = 0: window rows only; V = 1), 128 heads, FP8 entries
     "fp8_sparse_128h_sink_neg_inf": (presets.csa_pro(win_cap=256), [[0, 1], [2, 1], [3, 1], [130, 1], [5000, 2]],
                                      "-inf"),
+    # batch-invariant HCA over 5,120 entries: 41 fixed 128-row splits (two
+    # load batches in the combine), the shorter request's later splits empty
+    "fp8_hca_128h_invariant_41_splits": (_invariant(presets.hca_pro()), [[655360, 1], [40000, 1]]),
 }
 
 
