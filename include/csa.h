@@ -159,7 +159,10 @@ const char* csa_last_error(void);
 int csa_layer_sizes(const csa_layer_desc* layer, csa_sizes* out);
 
 /* Workspace bytes an op needs for n_rows rows (tokens or queries):
- *   CSA_OP_COMPRESS  projection rows [n_rows x ncols] fp32
+ *   CSA_OP_COMPRESS  projection rows [n_rows x ncols] fp32; bf16 activations:
+ *                    4 partial products of n_rows rows each (n_rows <= 64, or
+ *                    a batch-invariant layer), else max(n_rows, 256) rows, so
+ *                    the size never falls as n_rows grows
  *   CSA_OP_TOPK      candidate lists for n_rows score rows of up to max_cols
  *   CSA_OP_ATTENTION split-KV partial results for n_rows queries, max_cols =
  *                    the largest number of rows (entries + window) a query reads

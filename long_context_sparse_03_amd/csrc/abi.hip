@@ -188,7 +188,9 @@ int csa_workspace_size(const csa_layer_desc* layer, int op, int n_rows, int max_
     REQUIRE(bytes != nullptr, CSA_EINVAL, "bytes is NULL");
     REQUIRE(n_rows >= 0 && max_cols >= 0, CSA_EINVAL, "n_rows=%d max_cols=%d", n_rows, max_cols);
     switch (op) {
-    case CSA_OP_COMPRESS: *bytes = (size_t)n_rows * proj_cols(layer) * 4; return CSA_OK;
+    case CSA_OP_COMPRESS:
+        *bytes = csa::compress_workspace(layer->act_fmt == CSA_FMT_BF16, invariant(layer), n_rows, proj_cols(layer));
+        return CSA_OK;
     case CSA_OP_TOPK:
         REQUIRE(top_k >= 1, CSA_EINVAL, "top_k=%d", top_k);
         *bytes = csa::topk_workspace(n_rows, max_cols, top_k, layer->score_fmt == CSA_FMT_BF16);
@@ -232,7 +234,8 @@ int compress_args(const csa_layer_desc* layer, const csa_batch* batch, int n_tok
         REQUIRE(n_tokens == 0 || W_idx != nullptr, CSA_EINVAL, "W_idx is NULL");
         REQUIRE(max_entries == 0 || out_keys != nullptr, CSA_EINVAL, "out_keys is NULL");
     }
-    const size_t need = (size_t)n_tokens * proj_cols(layer) * 4;
+    const size_t need = n_tokens > 0 ? csa::compress_workspace(layer->act_fmt == CSA_FMT_BF16, invariant(layer),
+                                                                n_tokens, proj_cols(layer)) : 0;
     REQUIRE(ws_bytes >= need && (need == 0 || ws != nullptr), CSA_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes,
             need);
     csa::CompressArgs& a = *out;

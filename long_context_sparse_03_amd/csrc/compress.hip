@@ -234,14 +234,93 @@ __global__ __launch_bounds__(64 * PL_NW) void proj_small_lds(const uint16_t* __r
     }
 }
 
+// Few-row compressor projection as PROJ_PARTS partial products over equal
+// chunks of the contraction: chunk s (grid z) of K / PROJ_PARTS channels
+// writes P_s [M x N] fp32 at P + s * M * N, and the kernels that read the
+// projection add the partials in chunk order.  Splitting the contraction
+// gives more workgroups than 16-column blocks (a 1024-column projection has
+// only 64), and each wave takes at most PK_KB channels per batch (one batch
+// up to K = 4096 with 4 waves, 8192 with 8), so all of a wave's weight bytes
+// are in flight at once.  Weight rows go through LDS as coalesced 512-byte
+// row pieces (as in proj_small_lds); the few activation rows are read
+// straight into MFMA fragments (they stay in the L2 cache).
+constexpr int PK_KB = 256;                    // channels per wave and batch
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void proj_ksplit(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
+                                                       const uint16_t* __restrict__ Wi, int n_main, int N, int M,
+                                                       int K, float* __restrict__ P)
+{
+    constexpr int RB = 2 * PK_KB;                              // elements of two rows' batches
+    __shared__ __attribute__((aligned(16))) uint16_t Ws[NW][16 * PK_KB];
+    __shared__ float red[NW][64][4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
+    const int kc = K / PROJ_PARTS;                             // channels of a chunk (a multiple of 32)
+    const int steps = kc / MmaBF16::K, spw = (steps + NW - 1) / NW;
+    const int st0 = min(steps, wave * spw), nst = min(steps, st0 + spw) - st0;   // this wave's 32-channel steps
+    const int k0 = blockIdx.z * kc + MmaBF16::K * st0;        // and its first channel
+    const int m = blockIdx.y * 16 + li;
+    // rows past M or N read row 0 (their outputs are not stored)
+    const uint16_t* xr = X + (size_t)(m < M ? m : 0) * K + k0 + 8 * g;
+    const char* wr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int n = blockIdx.x * 16 + 2 * i + (lane >> 5), nn = n < N ? n : 0;
+        wr[i] = (const char*)(nn < n_main ? W + (size_t)nn * K : Wi + (size_t)(nn - n_main) * K) + 2 * (size_t)k0;
+    }
+    f32x4_t acc[4] = {zero4(), zero4(), zero4(), zero4()};
+    for (int b0 = 0; b0 < nst; b0 += 8) {
+        const int nb = min(8, nst - b0);                       // steps in this batch
+        // this wave's fragment reads of the previous batch are done before
+        // its region is refilled
+        __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0)
+        uint4 xf[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (u < nb) xf[u] = *(const uint4*)(xr + MmaBF16::K * (b0 + u));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 2 * i + (lane >> 5);
+            // chunks past the batch (a short batch) repeat its last chunk
+            const int c = min((lane & 31) ^ r, 4 * nb - 1);
+            __builtin_amdgcn_global_load_lds((const CSA_GLOBAL void*)(wr[i] + 64 * (size_t)b0 + 16 * c),
+                                             (CSA_LDS void*)&Ws[wave][i * RB], 16, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);                    // vmcnt(0): fragments and the region filled
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (u < nb) {
+                const int slot = (4 * u + g) ^ li;
+                const uint4 bv = *(const uint4*)&Ws[wave][li * PK_KB + 8 * slot];
+                acc[u & 3] = MmaBF16::step(xf[u], bv, acc[u & 3]);
+            }
+        }
+    }
+    const f32x4_t acc0 = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) red[wave][lane][q] = acc0[q];
+    __syncthreads();
+    // the waves' sums in wave order, one output row per wave
+    float* Ps = P + (size_t)blockIdx.z * M * N;
+    for (int q = wave; q < 4; q += NW) {
+        const int col = blockIdx.x * 16 + li, row = blockIdx.y * 16 + 4 * g + q;
+        float v = red[0][lane][q];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) v += red[w][lane][q];
+        if (row < M && col < N) Ps[(size_t)row * N + col] = v;
+    }
+}
+
 // Copy n floats from src to dst (and the first n2 of them also to dst2) with
 // the threads of the block: 16-byte pieces when every pointer is 16-byte
 // aligned and n, n2 are multiples of 4, each thread's pieces of a batch all
-// loaded before any is stored (one memory latency per batch).
-CSA_DEV void copy_row(float* __restrict__ dst, const float* __restrict__ src, int n, float* dst2 = nullptr, int n2 = 0)
+// loaded before any is stored (one memory latency per batch).  With ns > 1
+// the source is ns partial rows sst floats apart, added in order.
+CSA_DEV void copy_row(float* __restrict__ dst, const float* __restrict__ src, int n, float* dst2 = nullptr,
+                      int n2 = 0, int ns = 1, size_t sst = 0)
 {
     constexpr int U = 4;
-    if (((n | n2) & 3) == 0 && (((uintptr_t)dst | (uintptr_t)src | (uintptr_t)dst2) & 15) == 0) {
+    if (((n | n2) & 3) == 0 && (sst & 3) == 0 && (((uintptr_t)dst | (uintptr_t)src | (uintptr_t)dst2) & 15) == 0) {
         const int n4 = n >> 2;
         for (int b = threadIdx.x; b < n4; b += U * blockDim.x) {
             float4 v[U];
@@ -249,6 +328,13 @@ CSA_DEV void copy_row(float* __restrict__ dst, const float* __restrict__ src, in
             for (int u = 0; u < U; ++u) {
                 const int i = b + u * blockDim.x;
                 if (i < n4) v[u] = ((const float4*)src)[i];
+            }
+            for (int s = 1; s < ns; ++s) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int i = b + u * blockDim.x;
+                    if (i < n4) v[u] += ((const float4*)(src + s * sst))[i];
+                }
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -264,6 +350,13 @@ CSA_DEV void copy_row(float* __restrict__ dst, const float* __restrict__ src, in
             for (int u = 0; u < U; ++u) {
                 const int i = b + u * blockDim.x;
                 if (i < n) v[u] = src[i];
+            }
+            for (int s = 1; s < ns; ++s) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int i = b + u * blockDim.x;
+                    if (i < n) v[u] += src[s * sst + i];
+                }
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -385,9 +478,18 @@ CSA_DEV void merge_located(const CompressArgs& a, int e, int req, int ent, float
                 const bool second = rr >= m;                    // a row of the previous entry (overlap)
                 const int r = second ? rr - m : rr;
                 const int p = m * (second ? ent - 1 : ent) + r;
-                const float* row = (p >= s0) ? a.P + (size_t)(cu + p - s0) * a.ncols : tail + (size_t)(p % a.R) * a.ncols;
-                z[u] = row[second ? colZb : colZa] + (second ? Bb : Ba)[r * w + cc];
-                cv[u] = row[second ? colCb : colCa];
+                const bool new_row = p >= s0;                   // projected in this call (partials)
+                const float* row = new_row ? a.P + (size_t)(cu + p - s0) * a.ncols : tail + (size_t)(p % a.R) * a.ncols;
+                const int cz = second ? colZb : colZa, cC = second ? colCb : colCa;
+                float zv = row[cz], cvv = row[cC];
+                if (new_row) {
+                    for (int s = 1; s < a.n_psplit; ++s) {
+                        zv += row[s * a.psplit_stride + cz];
+                        cvv += row[s * a.psplit_stride + cC];
+                    }
+                }
+                z[u] = zv + (second ? Bb : Ba)[r * w + cc];
+                cv[u] = cvv;
             }
             float cm = -INFINITY;
 #pragma unroll
@@ -450,7 +552,7 @@ __global__ __launch_bounds__(256) void merge_kernel(CompressArgs a)
 // rotated at its position
 CSA_DEV void window_row(const CompressArgs& a, int gtok, int pos, float* xs, float* red)
 {
-    copy_row(xs, a.P + (size_t)gtok * a.ncols, a.c);       // C^a (CSA) or C (HCA) at column 0
+    copy_row(xs, a.P + (size_t)gtok * a.ncols, a.c, nullptr, 0, a.n_psplit, a.psplit_stride);   // C^a (CSA) or C (HCA)
     __syncthreads();
     norm_rope_store(xs, red, a.c, a.r, a.gamma, a.eps, (double)pos, a.theta, a.out_win + (size_t)gtok * a.c);
 }
@@ -472,7 +574,8 @@ __global__ __launch_bounds__(256) void tail_update_kernel(CompressArgs a)
     if (j >= keep) return;
     const int p = s0 + n - keep + j;
     float* tail = (float*)((char*)a.state + (size_t)req * a.state_stride + a.tail_off);
-    copy_row(tail + (size_t)(p % a.R) * a.ncols, a.P + (size_t)(cu + n - keep + j) * a.ncols, a.ncols);
+    copy_row(tail + (size_t)(p % a.R) * a.ncols, a.P + (size_t)(cu + n - keep + j) * a.ncols, a.ncols, nullptr, 0,
+             a.n_psplit, a.psplit_stride);
 }
 
 // At most one new token per request: the merges, the window rows and the
@@ -495,7 +598,8 @@ __global__ __launch_bounds__(256) void post_decode_kernel(CompressArgs a, int nm
     // one pass over the projected row: into the tail ring, and its first c
     // channels (C^a, HCA: C) into LDS for the window row
     float* tail = (float*)((char*)a.state + (size_t)req * a.state_stride + a.tail_off);
-    copy_row(tail + (size_t)(pos % a.R) * a.ncols, a.P + (size_t)gtok * a.ncols, a.ncols, xs, a.c);
+    copy_row(tail + (size_t)(pos % a.R) * a.ncols, a.P + (size_t)gtok * a.ncols, a.ncols, xs, a.c, a.n_psplit,
+             a.psplit_stride);
     __syncthreads();
     norm_rope_store(xs, red, a.c, a.r, a.gamma, a.eps, (double)pos, a.theta, a.out_win + (size_t)gtok * a.c);
 }
@@ -533,7 +637,8 @@ __global__ __launch_bounds__(256) void post_decode_append_kernel(CompressArgs a,
     const int req = a.one_per_req ? gtok : find_request(a.cu_new, a.n_req, gtok);
     const int pos = a.start_pos[req] + (a.one_per_req ? 0 : gtok - a.cu_new[req]);
     float* tail = (float*)((char*)a.state + (size_t)req * a.state_stride + a.tail_off);
-    copy_row(tail + (size_t)(pos % a.R) * a.ncols, a.P + (size_t)gtok * a.ncols, a.ncols, xs, a.c);
+    copy_row(tail + (size_t)(pos % a.R) * a.ncols, a.P + (size_t)gtok * a.ncols, a.ncols, xs, a.c, a.n_psplit,
+             a.psplit_stride);
     __syncthreads();
     norm_rope_store(xs, red, a.c, a.r, a.gamma, a.eps, (double)pos, a.theta, a.out_win + (size_t)gtok * a.c);
     store_window_row(b, req, pos, xs);
@@ -543,15 +648,42 @@ __global__ __launch_bounds__(256) void post_decode_append_kernel(CompressArgs a,
 // host launcher
 // ---------------------------------------------------------------------------
 
-hipError_t launch_compress(hipStream_t st, const CompressArgs& a, const void* H, const void* W, const void* Wi,
+int proj_parts(bool bf16, bool invariant, int n_rows)
+{
+    return bf16 && (n_rows <= 64 || invariant) ? PROJ_PARTS : 1;
+}
+
+size_t compress_workspace(bool bf16, bool invariant, int n_rows, int ncols)
+{
+    // a call with fewer rows may take more partials: at least 64 rows' worth
+    // of partials whenever a call of up to n_rows rows can split
+    const size_t rows = proj_parts(bf16, invariant, n_rows) > 1 ? (size_t)n_rows * PROJ_PARTS
+                        : bf16 ? (size_t)max(n_rows, 64 * PROJ_PARTS) : (size_t)n_rows;
+    return rows * (size_t)ncols * 4;
+}
+
+hipError_t launch_compress(hipStream_t st, const CompressArgs& args, const void* H, const void* W, const void* Wi,
                            int n_main, int d, bool bf16, int n_tokens, const AppendArgs* app)
 {
-    const int N = a.ncols, M = n_tokens;
+    const int N = args.ncols, M = n_tokens;
     const GemmShape sh{d, N, 0, 0, 0, 0};
+    CompressArgs a = args;
+    a.n_psplit = 1;
+    a.psplit_stride = 0;
     if (M > 0) {
         // batch-invariant layers: one kernel whatever the row count (its sums
         // for a row do not depend on the other rows)
-        if (M <= 64 || a.invariant) {
+        if (proj_parts(bf16, a.invariant, M) > 1 && d % (PROJ_PARTS * MmaBF16::K) == 0) {
+            a.n_psplit = PROJ_PARTS;
+            a.psplit_stride = (size_t)M * N;
+            const dim3 grid((N + 15) / 16, (M + 15) / 16, PROJ_PARTS);
+            if (d <= 4 * PROJ_PARTS * PK_KB)
+                proj_ksplit<4><<<grid, 256, 0, st>>>((const uint16_t*)H, (const uint16_t*)W, (const uint16_t*)Wi, n_main,
+                                                     N, M, d, a.P);
+            else
+                proj_ksplit<8><<<grid, 512, 0, st>>>((const uint16_t*)H, (const uint16_t*)W, (const uint16_t*)Wi, n_main,
+                                                     N, M, d, a.P);
+        } else if (M <= 64 || a.invariant) {
             dim3 grid((N + 15) / 16, (M + 15) / 16);
             if (bf16 && d % (PL_NW * MmaBF16::K) == 0 && d >= PL_NW * PL_KB)   // whole steps, full batches
                 proj_small_lds<<<grid, 64 * PL_NW, 0, st>>>((const uint16_t*)H, (const uint16_t*)W, (const uint16_t*)Wi,

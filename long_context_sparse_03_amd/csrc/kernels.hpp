@@ -30,7 +30,16 @@ struct CompressArgs {
     int one_per_req;           // set by launch_compress: every request has exactly one new token
     int invariant;             // batch-invariant layer: the projection kernel does not depend on the row count
     int32_t* next_pos;         // [n_req] or null: start_pos + new tokens, written by the post-projection kernel
+    int n_psplit;              // set by launch_compress: P holds this many partial products ...
+    size_t psplit_stride;      // ... this many floats apart, which readers add in order
 };
+
+// Few-row bf16 projections (and every projection of a batch-invariant layer)
+// are PROJ_PARTS partial products over equal chunks of the contraction.
+constexpr int PROJ_PARTS = 4;
+int proj_parts(bool bf16, bool invariant, int n_rows);
+// compress_kv's workspace for calls of up to n_rows rows (never less for more rows)
+size_t compress_workspace(bool bf16, bool invariant, int n_rows, int ncols);
 
 // Y[M x groups*N] = per group g: X[:, g*K .. g*K+K) . W[g]^T, W [groups x N x K];
 // X, W bf16 (bf16) or fp32, Y fp32 or (out_bf16) bf16.

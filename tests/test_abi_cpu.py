@@ -108,7 +108,21 @@ def test_calls_reject_bad_arguments_before_launch():
 
 def test_workspace_sizes():
     d = presets.csa_flash_decode()
-    assert P.workspace_size(d, abi.OP_COMPRESS, 16) == 16 * (4 * 512 + 4 * 128) * 4
+    cols = 4 * 512 + 4 * 128
+    # few bf16 rows: the projection as four partial products over the contraction
+    assert P.workspace_size(d, abi.OP_COMPRESS, 16) == 4 * 16 * cols * 4
+    # one product from 65 rows on, but never less workspace for more rows
+    sizes = [P.workspace_size(d, abi.OP_COMPRESS, n) for n in (0, 1, 63, 64, 65, 255, 256, 257, 4096)]
+    assert sizes == sorted(sizes) and sizes[0] == 0
+    assert P.workspace_size(d, abi.OP_COMPRESS, 65) == 256 * cols * 4
+    assert P.workspace_size(d, abi.OP_COMPRESS, 4096) == 4096 * cols * 4
+    # a batch-invariant layer splits at any row count; fp32 activations never
+    inv = presets.layer(abi.KIND_CSA, 4, 512, 64, 64, 64, 128, 512, kv_fmt=abi.KV_FP8, idx_fmt=abi.IDX_BF16,
+                        score_fmt=abi.ACT_BF16, act_fmt=abi.ACT_BF16, out_fmt=abi.ACT_BF16,
+                        flags=abi.FLAG_BATCH_INVARIANT)
+    assert P.workspace_size(inv, abi.OP_COMPRESS, 4096) == 4 * 4096 * cols * 4
+    t = presets.tiny_csa_fp32()
+    assert P.workspace_size(t, abi.OP_COMPRESS, 16) == 16 * (4 * t.c + 4 * t.c_idx) * 4
     assert P.workspace_size(d, abi.OP_TOPK, 4096, 32768, 512) == 0        # rows that fit a workgroup: one stage
     assert P.workspace_size(d, abi.OP_TOPK, 16, 32768, 512) == 0
     # few long bf16 rows: equal chunks of at most 16384 keys (multiples of 64)
