@@ -355,11 +355,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void i
     // u < 4, i.e. rows 16w + 4u .. +3; lane l brings chunk (l mod 16) ^ (row
     // mod 16) of row 16w + 4u + l/16 (rows past the range repeat the last key)
     auto issue_tile = [&](int t0, uint16_t* buf) {
+        // the lane's row and chunk are recomputed here rather than kept
+        // across the loop (kept, they were spilled to scratch)
+        int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+        asm volatile("" : "+v"(ln));
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int row = 16 * wave + 4 * u + (lane >> 4);
+            const int row = 16 * wave + 4 * u + (ln >> 4);
             const int e = min(t0 + row, e1 - 1);
-            const int c = (lane & 15) ^ (row & 15);
+            const int c = (ln & 15) ^ (row & 15);
             const uint32_t in_blk = (uint32_t)(e & (a.epb - 1)) * (PF_CI * 2) + 16u * (uint32_t)c;
             const char* src = (const char*)a.keys + (size_t)bt[(e >> a.epb_log2) - blk0] * a.key_block_bytes + in_blk;
             __builtin_amdgcn_global_load_lds((const CSA_GLOBAL void*)src,
@@ -370,18 +374,38 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void i
     // store issued right before the end-of-tile wait would hold it up)
     float xs[PF_TILE / 64];
     int es = -1;                                                    // first key of those scores (-1: none)
+    // fused top-k: the count bins of the stored scores (~0: none), added to
+    // the counts at the top of the next pass, where no tile load is in
+    // flight (an LDS atomic issued while the direct-to-LDS loads of the next
+    // tile are pending is made to wait for them)
+    uint32_t hb[PF_TILE / 64];
+#pragma unroll
+    for (int eb = 0; eb < PF_TILE / 64; ++eb) hb[eb] = ~0u;
+    auto hist_flush = [&]() {
+        if constexpr (HIST) {
+#pragma unroll
+            for (int eb = 0; eb < PF_TILE / 64; ++eb) {
+                if (hb[eb] != ~0u) atomicAdd(&hcnt[wave][hb[eb]], 1u);
+                hb[eb] = ~0u;
+            }
+        }
+    };
     auto store_scores = [&]() {
         if (es < 0) return;
+        // the key offsets are recomputed (a spilled copy's reload would wait
+        // for the next tile's loads, issued just before)
+        int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+        asm volatile("" : "+v"(ln));
 #pragma unroll
         for (int eb = 0; eb < PF_TILE / 64; ++eb) {
-            const int e = es + eb * 64 + 16 * (2 * (g & 1) + (g >> 1)) + li;
+            const int e = es + eb * 64 + 16 * (2 * ((ln >> 4) & 1) + (ln >> 5)) + (ln & 15);
             if (e < V) {
                 float x = xs[eb];
                 if (x == 0.0f) x = 0.0f;                            // -0 is stored as +0
                 if constexpr (BF16OUT) {
                     const uint16_t b = canon_bf16(f32_to_bf16(x));   // a value rounding to -0 is stored as +0
                     ((uint16_t*)a.scores)[(size_t)gq * a.ld + e] = b;
-                    if (HIST) atomicAdd(&hcnt[wave][key16(b) >> 8], 1u);
+                    if (HIST) hb[eb] = key16(b) >> 8;
                 } else {
                     ((float*)a.scores)[(size_t)gq * a.ld + e] = x;
                 }
@@ -440,18 +464,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void i
     tile_done();
     for (int it = 0; it < n_tiles; it += 2) {
         const int t0 = e0 + it * PF_TILE;
+        hist_flush();
         // Ks1 was last read in the previous pass, finished before its barrier
         if (it + 1 < n_tiles) issue_tile(t0 + PF_TILE, Ks1);
         store_scores();
         compute(t0, Ks0);
         tile_done();
         if (it + 1 >= n_tiles) break;
+        hist_flush();
         if (it + 2 < n_tiles) issue_tile(t0 + 2 * PF_TILE, Ks0);
         store_scores();
         compute(t0 + PF_TILE, Ks1);
         tile_done();
     }
+    hist_flush();                                                   // the counts of the last stored scores
     store_scores();
+    hist_flush();
     // fused top-k: each valid query's counts of this chunk, lane l bins 4l..4l+3
     if (HIST) {
         __syncthreads();
