@@ -199,6 +199,47 @@ def test_topk_exact_rows_past_2_18():
         assert np.array_equal(got[t], want[t]), f"row {t} (V={V[t]}) differs"
 
 
+def test_topk_f32_keys_at_the_top_of_the_key_range():
+    """fp32 scores whose order-preserving keys crowd the top of the 32-bit
+    range (+NaN bit patterns with payloads up to 0x7FFFFFFF, keys up to
+    0xFFFFFFFF), so the threshold's range narrowing works at the very top,
+    where a bin's upper end would pass 2^32 without the clamp.  The oracle
+    compares floats and does not order NaNs, so the expected sets come from
+    the selector's documented total order: the sign-magnitude key of the bit
+    pattern descending (-0 and +0 alike, keys 0 and 1 alike), then the lower
+    position."""
+    _flush("topk f32 keys near 0xFFFFFFFF")
+    g = synth.rng(107)
+    ld, k = 4096, 1500
+    bits = np.empty((4, ld), np.uint32)
+    bits[0] = synth.normal(g, (ld,)).astype(np.float32).view(np.uint32)
+    bits[0, :3000] = 0x7FFFF000 + g.integers(0, 4096, size=3000).astype(np.uint32)
+    bits[1] = 0x7FFFFF00 + g.integers(0, 256, size=ld).astype(np.uint32)   # 256 keys, long tie runs
+    bits[1, ::97] = 0x7FFFFFFF                                              # the largest key
+    bits[2] = synth.normal(g, (ld,)).astype(np.float32).view(np.uint32)
+    bits[2, ::3] = 0xFFFFFFFF                                               # the smallest key
+    bits[2, 1::3] = 0x7FFFFFFF
+    bits[3] = 0x7FFFFFF0 + g.integers(0, 16, size=ld).astype(np.uint32)
+    nv = np.array([ld, ld, ld - 5, 1000], np.int32)
+    key = np.where(bits >> 31 == 1, ~bits, bits | np.uint32(0x80000000)).astype(np.uint64)
+    key[(bits & 0x7FFFFFFF) == 0] = 0x80000000
+    key = np.maximum(key, 1)      # keys 0 and 1 (two negative NaNs) share a rank, as the selector documents
+    want = np.full((4, k), -1, np.int32)
+    for t in range(4):
+        V = int(nv[t])
+        order = sorted(range(V), key=lambda s: (-int(key[t, s]), s))[:min(k, V)]
+        want[t, :len(order)] = np.sort(order)
+    scores = torch.from_numpy(bits.view(np.float32).copy()).cuda()
+    out = torch.full((4, k), -7, dtype=torch.int32, device="cuda")
+    desc = presets.tiny_csa_fp32()
+    ws = torch.empty(max(abi.workspace_size(desc, abi.OP_TOPK, 4, ld, k), 1), dtype=torch.uint8, device="cuda")
+    abi.topk_select(abi.ACT_F32, 4, scores, ld, i32(nv), k, out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for t in range(4):
+        assert np.array_equal(got[t], want[t]), f"row {t} (V={nv[t]}) differs"
+
+
 # ---------------------------------------------------------------------------
 # a3: index scores
 # ---------------------------------------------------------------------------
