@@ -383,9 +383,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void i
     for (int eb = 0; eb < PF_TILE / 64; ++eb) hb[eb] = ~0u;
     auto hist_flush = [&]() {
         if constexpr (HIST) {
+            // a quad of lanes holds four consecutive keys, which mostly fall
+            // into one bin: the first lane of the quad with a given bin adds
+            // the quad's count of it (fewer same-address atomics)
+            const int qd = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) & 3;
 #pragma unroll
             for (int eb = 0; eb < PF_TILE / 64; ++eb) {
-                if (hb[eb] != ~0u) atomicAdd(&hcnt[wave][hb[eb]], 1u);
+                const uint32_t b = hb[eb];
+                const uint32_t b1 = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)b, 0xB1, 0xF, 0xF, false);  // lane ^ 1
+                const uint32_t b2 = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)b, 0x4E, 0xF, 0xF, false);  // lane ^ 2
+                const uint32_t b3 = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)b, 0x1B, 0xF, 0xF, false);  // lane ^ 3
+                const bool m1 = b1 == b, m2 = b2 == b, m3 = b3 == b;
+                const bool later = (qd == 1 && m1) || (qd == 2 && (m2 || m3)) || (qd == 3 && (m1 || m2 || m3));
+                if (b != ~0u && !later) atomicAdd(&hcnt[wave][b], 1u + m1 + m2 + m3);
                 hb[eb] = ~0u;
             }
         }
