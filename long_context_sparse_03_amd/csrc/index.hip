@@ -125,6 +125,21 @@ CSA_DEV void load_keys(const IndexArgs& a, const int* bt, int blk0, int e0, int 
 // the scores are stored and counted
 CSA_DEV uint16_t canon_bf16(uint16_t b) { return (b & 0x7FFFu) == 0u ? (uint16_t)0u : b; }
 
+// Fused top-k counts: lanes 4j .. 4j+3 (a quad) hold four consecutive keys,
+// which mostly fall into one bin, so the first lane of a quad with a given
+// bin adds the quad's count of it; bin ~0 counts nothing.  Every lane of the
+// wave calls it (the quad permutes read the other lanes' bins).
+CSA_DEV void count_bins_quad(uint32_t* h, uint32_t b)
+{
+    const int qd = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) & 3;
+    const uint32_t b1 = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)b, 0xB1, 0xF, 0xF, false);   // lane ^ 1
+    const uint32_t b2 = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)b, 0x4E, 0xF, 0xF, false);   // lane ^ 2
+    const uint32_t b3 = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)b, 0x1B, 0xF, 0xF, false);   // lane ^ 3
+    const bool m1 = b1 == b, m2 = b2 == b, m3 = b3 == b;
+    const bool later = (qd == 1 && m1) || (qd == 2 && (m2 || m3)) || (qd == 3 && (m1 || m2 || m3));
+    if (b != ~0u && !later) atomicAdd(&h[b], 1u + m1 + m2 + m3);
+}
+
 // Fused top-k: the chunk's 256 counts of query row gq (threads 0..255, one
 // coalesced 512-byte store), after every wave has counted its scores.  Every
 // wave of the workgroup must call it (it holds a barrier when HIST).
@@ -262,16 +277,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S <= 4 ? 2 
         float x = o2 ? k1 : k0;
         x += __shfl_xor(o2 ? k0 : k1, 32, 64);
         const int e = e_base + 16 * (2 * (g & 1) + (g >> 1)) + li;
+        uint32_t hbin = ~0u;
         if (e < V) {
             if (x == 0.0f) x = 0.0f;                    // -0 is stored as +0
             if (a.score_bf16) {
                 const uint16_t b = canon_bf16(f32_to_bf16(x));   // a value rounding to -0 is stored as +0
                 ((uint16_t*)a.scores)[(size_t)gq * a.ld + e] = b;
-                if (HIST) atomicAdd(&hcnt[key16(b) >> 8], 1u);
+                hbin = key16(b) >> 8;
             } else {
                 ((float*)a.scores)[(size_t)gq * a.ld + e] = x;
             }
         }
+        if (HIST) count_bins_quad(hcnt, hbin);
     }
     store_hist<HIST>(a, gq, blockIdx.y, hcnt);
 }
@@ -383,19 +400,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void i
     for (int eb = 0; eb < PF_TILE / 64; ++eb) hb[eb] = ~0u;
     auto hist_flush = [&]() {
         if constexpr (HIST) {
-            // a quad of lanes holds four consecutive keys, which mostly fall
-            // into one bin: the first lane of the quad with a given bin adds
-            // the quad's count of it (fewer same-address atomics)
-            const int qd = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) & 3;
 #pragma unroll
             for (int eb = 0; eb < PF_TILE / 64; ++eb) {
-                const uint32_t b = hb[eb];
-                const uint32_t b1 = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)b, 0xB1, 0xF, 0xF, false);  // lane ^ 1
-                const uint32_t b2 = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)b, 0x4E, 0xF, 0xF, false);  // lane ^ 2
-                const uint32_t b3 = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)b, 0x1B, 0xF, 0xF, false);  // lane ^ 3
-                const bool m1 = b1 == b, m2 = b2 == b, m3 = b3 == b;
-                const bool later = (qd == 1 && m1) || (qd == 2 && (m2 || m3)) || (qd == 3 && (m1 || m2 || m3));
-                if (b != ~0u && !later) atomicAdd(&hcnt[wave][b], 1u + m1 + m2 + m3);
+                count_bins_quad(hcnt[wave], hb[eb]);
                 hb[eb] = ~0u;
             }
         }
@@ -623,16 +630,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
         float x = o2 ? k1 : k0;
         x += __shfl_xor(o2 ? k0 : k1, 32, 64);
         const int e = e_base + 16 * (2 * (g & 1) + (g >> 1)) + li;
+        uint32_t hbin = ~0u;
         if (e < V) {
             if (x == 0.0f) x = 0.0f;                    // -0 is stored as +0
             if (a.score_bf16) {
                 const uint16_t b = canon_bf16(f32_to_bf16(x));   // a value rounding to -0 is stored as +0
                 ((uint16_t*)a.scores)[(size_t)gq * a.ld + e] = b;
-                if (HIST) atomicAdd(&hcnt[key16(b) >> 8], 1u);
+                hbin = key16(b) >> 8;
             } else {
                 ((float*)a.scores)[(size_t)gq * a.ld + e] = x;
             }
         }
+        if (HIST) count_bins_quad(hcnt, hbin);
     }
     store_hist<HIST>(a, gq, blockIdx.y, hcnt);
 }
