@@ -559,7 +559,11 @@ def test_compress_kv_chunked_and_decode(name):
     else:
         desc, d = presets.hca_bf16(win_cap=4224), presets.D_HCA
         ctx = [8192, 5000]
-        sched = [[3000, 4000], [4000, 1000], [1192, 0]]
+        # a 60-row call (four 16-row blocks, the last ragged) and one-token
+        # calls take the projection in four partial products, which the
+        # merge, window and tail kernels (several new tokens) and the fused
+        # decode kernel (at most one) add; the long calls take the 128 x 128 tiles
+        sched = [[3000, 4000], [40, 20], [1, 1], [1, 0], [4000, 979], [1150, 0]]
         w_ = synth.hca_weights(g, d, desc.c, desc.m)
         W, Wi, Ba, Bb, BaI, BbI = w_["W"], None, w_["Ba"], None, None, None
         W = synth.to_bf16_values(W)
