@@ -152,7 +152,7 @@ class DecodeWorkload:
             self.bufs.append(b)
 
     # ------------------------------------------------------------------
-    def layer_calls(self, li: int, hooks=None, parity: int = 0):
+    def layer_calls(self, li: int, parity: int = 0):
         """The library calls of layer li for one decode token per request, at
         the positions of buffer `parity` (layer 0 also advances them into the
         other buffer)."""
@@ -173,16 +173,12 @@ class DecodeWorkload:
             abi.cache_append(desc, bi.batch, n, b["entries"], keys, b["meta"], b["count"], n, b["win"], st.kv,
                              st.idx, st.state, stream=s)
         if st.is_csa:
-            if hooks:
-                hooks[0]()
             if self.fused_topk:
                 abi.index_topk(desc, bi.batch, n, b["qI"], b["w"], st.idx, b["scores"], b["ld"], b["n_valid"],
                                b["sel"], b["ws_it"], stream=s)
             else:
                 abi.index_scores(desc, bi.batch, n, b["qI"], b["w"], st.idx, b["scores"], b["ld"], b["n_valid"],
                                  stream=s)
-                if hooks:
-                    hooks[1]()
                 abi.topk_select(desc.score_fmt, n, b["scores"], b["ld"], b["n_valid"], desc.top_k, b["sel"],
                                 b["ws_t"], stream=s)
             abi.sparse_mqa(desc, bi.batch, n, b["q"], P["q_gamma"], b["sel"], st.kv, st.state, P["sinks"], b["out"],
@@ -198,12 +194,12 @@ class DecodeWorkload:
         abi.index_scores(st.desc, self.bis[self.parity].batch, self.n_req, b["qI"], b["w"], st.idx, b["scores"],
                          b["ld"], b["n_valid"])
 
-    def step(self, hooks=None, parity: int | None = None):
+    def step(self, parity: int | None = None):
         """One decode step through every layer at the positions of buffer
         `parity` (default: the workload's current one, which then flips); the
         first layer writes the next positions into the other buffer."""
         p = self.parity if parity is None else parity
         for li in range(len(self.layers)):
-            self.layer_calls(li, hooks[li] if hooks else None, parity=p)
+            self.layer_calls(li, parity=p)
         if parity is None:
             self.parity ^= 1
