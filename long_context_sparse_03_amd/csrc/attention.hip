@@ -557,6 +557,14 @@ __global__ __launch_bounds__((AttnCfg<KVF, C, R, HT>::NT)) void attn_kernel(Attn
     }
 }
 
+// What a slot of attn_ht_kernel reads when it has no row (past the query's
+// entries or window, an entry that is not visible): 1 KB of zeros, and a
+// scale word of -1, which marks the slot as masked.  bf16 window rows take
+// the scale 1.
+static __device__ __attribute__((aligned(16))) uint32_t attn_zero_row[256];
+static __device__ float attn_masked_scale = -1.0f;
+static __device__ float attn_unit_scale = 1.0f;
+
 // FP8 entry records with bf16 queries (the serving shapes): two waves per
 // head tile.  Waves w and w + HT own heads 16w .. 16w+15 of the group and one
 // half of the channels each (alternate 32-channel MFMA steps for the logits,
@@ -593,10 +601,9 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
     // accumulator or which P a step uses is known at compile time.
 
     __shared__ __attribute__((aligned(16))) uint16_t Kt[2][32 * KP];
-    __shared__ float tscl[2][32];                              // per buffer: row scales ...
-    __shared__ int tval[2][32];                                // ... and valid rows
-    __shared__ const char* rptr[DESC];                         // row start (null: masked row)
-    __shared__ const char* rblk[DESC];                         // FP8 entry rows: their block (scale at byte 0)
+    __shared__ float tscl[2][32];                              // per buffer: row scales (-1: masked row)
+    __shared__ const char* rptr[DESC];                         // row start (the zero row when masked)
+    __shared__ const char* rblk[DESC];                         // the row's scale (FP8 entries: block byte 0)
     __shared__ float rcs[R / 2], rsn[R / 2];
     __shared__ int cu_sh[257];
     __shared__ __attribute__((aligned(16))) float gam[C];      // query norm gains
@@ -638,7 +645,9 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
         req = find_request_block(a.cu_new, a.n_req, gq, cu_sh, 256);
         tok = gq - (a.n_req < 256 ? cu_sh[req] : a.cu_new[req]);
     }
-    const int t = a.start_pos[req] + tok;
+    // the position and what follows from it are the same for the whole
+    // workgroup (scalar registers, so the row-kind tests below are scalar)
+    const int t = __builtin_amdgcn_readfirstlane(a.start_pos[req] + tok);
     const int V = (t + 1) / a.m;
     const int K0 = dense ? V : a.k;                            // entry slots before the window
     const int nwr = min(a.n_win, t + 1);
@@ -649,14 +658,19 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
     const char* ring = (const char*)a.state + (size_t)req * a.state_stride;
 
     // ---- row descriptors of DESC consecutive slots (e: the entry of a
-    //      slot < K0, already loaded for the first window of a sparse query)
+    //      slot < K0, already loaded for the first window of a sparse query):
+    //      where the row starts and where its scale is; a masked slot gets the
+    //      zero row and the scale -1
+    const char* const zrow = (const char*)attn_zero_row;
+    const char* const mscl = (const char*)&attn_masked_scale;
+    const char* const uscl = (const char*)&attn_unit_scale;
     auto describe = [&](int first_slot, bool have_e) {
 #pragma unroll
         for (int u = 0; u < DESC / NT; ++u) {
             const int j = (int)threadIdx.x + u * NT;
             const int slot = first_slot + j;
-            const char* p = nullptr;
-            const char* blk = nullptr;
+            const char* p = zrow;
+            const char* blk = mscl;
             if (slot < K0) {
                 const int e = dense ? slot : (have_e ? esel[u] : a.sel[(size_t)gq * a.k + slot]);
                 if (e >= 0 && e < V) {
@@ -667,6 +681,7 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
                 }
             } else if (slot < n_slots && slot - K0 < nwr) {
                 p = ring + (size_t)((w0 + slot - K0) % a.win_cap) * WB;
+                blk = uscl;
             }
             rptr[j] = p;
             rblk[j] = blk;
@@ -674,37 +689,27 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
     };
     // ---- one tile into registers: wave w loads rows w, w+NWV, .., one row
     //      per instruction, lane l the row's bytes 16l..16l+15 (clamped to
-    //      the row; masked rows read a valid dummy row), the block scale of
-    //      each entry row and (bit j of rok) whether row j is valid
-    const char* dummy = (const char*)a.kv;
-    auto load_tile = [&](int tile, int drow0, uint4 (&raw)[RPW], float (&rsr)[RPW], int& rok) {
+    //      the row), and each row's scale
+    auto load_tile = [&](int tile, int drow0, uint4 (&raw)[RPW], float (&rsr)[RPW]) {
         const int slot0 = tile * 32;
-        rok = 0;
 #pragma unroll
         for (int j = 0; j < RPW; ++j) {
             const int row = wave + NWV * j;
-            const char* p = rptr[drow0 + row];
             const int bytes = (slot0 + row < K0) ? EB : WB;
-            raw[j] = ld16((p != nullptr ? p : dummy) + min(lane * 16, bytes - 16));
-            const char* b = rblk[drow0 + row];
-            rsr[j] = *(const CSA_GLOBAL float*)(b != nullptr ? b : dummy);
-            rok |= (p != nullptr) << j;
+            raw[j] = ld16(rptr[drow0 + row] + min(lane * 16, bytes - 16));
+            rsr[j] = *(const CSA_GLOBAL float*)rblk[drow0 + row];
         }
     };
-    // ---- expand a loaded tile into Kt[buf] (masked rows become zeros) with
-    //      its row flags and scales
-    auto store_tile = [&](int tile, int buf, const uint4 (&raw)[RPW], const float (&rsr)[RPW], int rok) {
+    // ---- expand a loaded tile into Kt[buf] (masked rows are zeros already)
+    //      with its row scales
+    auto store_tile = [&](int tile, int buf, const uint4 (&raw)[RPW], const float (&rsr)[RPW]) {
         const int slot0 = tile * 32;
 #pragma unroll
         for (int j = 0; j < RPW; ++j) {
             const int row = wave + NWV * j;
-            const bool ok = (rok >> j) & 1;
             const bool entry = slot0 + row < K0;
-            if (lane == 0) {
-                tval[buf][row] = ok;
-                tscl[buf][row] = (ok && entry) ? rsr[j] : 1.0f;
-            }
-            const uint4 v = sel16(ok, raw[j]);
+            if (lane == 0) tscl[buf][row] = rsr[j];
+            const uint4 v = raw[j];
             uint16_t* kr = &Kt[buf][row * KP];
             if (entry) {
                 if (lane < NCH) {                              // 16 FP8 codes per lane
@@ -741,14 +746,13 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
     }
     __syncthreads();
     // two tiles in flight: the rows of tiles n+1 and n+2 load while tile n
-    // computes (slot k of raw / rsr / rok and LDS buffer k serve tiles
+    // computes (slot k of raw / rsr and LDS buffer k serve tiles
     // tile0 + k, tile0 + k + 2, ..)
     static_assert(DESC >= 64, "two tiles per descriptor window");
     uint4 raw[2][RPW];
     float rsr[2][RPW];
-    int rok[2];
-    if (tile0 < tile1) load_tile(tile0, 0, raw[0], rsr[0], rok[0]);
-    if (tile0 + 1 < tile1) load_tile(tile0 + 1, 32, raw[1], rsr[1], rok[1]);
+    if (tile0 < tile1) load_tile(tile0, 0, raw[0], rsr[0]);
+    if (tile0 + 1 < tile1) load_tile(tile0 + 1, 32, raw[1], rsr[1]);
 
     // normalised, rotated, scaled query fragments of this lane's head
     uint4 QF[KSH];
@@ -794,7 +798,7 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
         constexpr int buf = decltype(slot)::value;
         // Kt[buf] was last read by tile-2, which every wave finished before
         // the barrier of tile-1
-        store_tile(tile, buf, raw[buf], rsr[buf], rok[buf]);
+        store_tile(tile, buf, raw[buf], rsr[buf]);
         __syncthreads();                                       // tile in Kt[buf]
         if (tile + 2 < tile1) {
             const int drow = ((tile + 2 - tile0) * 32) % DESC;
@@ -802,7 +806,7 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
                 describe((tile + 2) * 32, false);              // are issued, stores read no descriptors)
                 __syncthreads();
             }
-            load_tile(tile + 2, drow, raw[buf], rsr[buf], rok[buf]);
+            load_tile(tile + 2, drow, raw[buf], rsr[buf]);
         }
         const uint16_t* kt = Kt[buf];
 
@@ -840,6 +844,7 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
         }
         // ---- the two halves' partial logits (FP8 channels scaled by the
         //      row's block scale) meet in LDS; both waves add them in half order
+        //      (a masked row's zeros give 0 whatever its scale)
         float rsc[8];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
@@ -859,8 +864,7 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
             const f32x4_t s0 = Sx[buf][ht][0][rt][lane], s1 = Sx[buf][ht][1][rt][lane];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int row = 16 * rt + 4 * g + i;
-                sv[4 * rt + i] = tval[buf][row] != 0 ? s0[i] + s1[i] : -INFINITY;
+                sv[4 * rt + i] = rsc[4 * rt + i] >= 0.f ? s0[i] + s1[i] : -INFINITY;   // -1: masked
             }
         }
         float mx = sv[0];
