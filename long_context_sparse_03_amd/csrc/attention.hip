@@ -571,8 +571,9 @@ static __device__ float attn_unit_scale = 1.0f;
 // alternate 16-channel tiles for the output, so that both halves have the
 // same mix of FP8 and rotary channels at the same positions): each contracts
 // its half of the tile for those heads (S^T = K . Q^T), the two partial
-// logits meet in LDS and are summed in the same order by both waves, both
-// run the same online softmax in registers, and each accumulates the output
+// logits meet in LDS and each wave adds the other's to its own (a two-term
+// sum, equal in both waves), both run the same online softmax in
+// registers, and each accumulates the output
 // of its half of the channels (O^T = V^T . P^T).  Tiles are double-buffered
 // in LDS: the rows of the next two tiles are loaded into registers while one
 // computes, and two barriers per tile publish a stored tile and the partial
@@ -843,28 +844,30 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
             __builtin_amdgcn_sched_barrier(0);
         }
         // ---- the two halves' partial logits (FP8 channels scaled by the
-        //      row's block scale) meet in LDS; both waves add them in half order
-        //      (a masked row's zeros give 0 whatever its scale)
+        //      row's block scale) meet in LDS (a masked row's zeros give 0
+        //      whatever its scale)
         float rsc[8];
+        f32x4_t part[2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-            f32x4_t part;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 rsc[4 * rt + i] = tscl[buf][16 * rt + 4 * g + i];
-                part[i] = rsc[4 * rt + i] * an[rt][i] + ar[rt][i];
+                part[rt][i] = rsc[4 * rt + i] * an[rt][i] + ar[rt][i];
             }
-            Sx[buf][ht][half][rt][lane] = part;
+            Sx[buf][ht][half][rt][lane] = part[rt];
         }
         __syncthreads();                                       // partial logits of both halves in LDS
-        // ---- online softmax of head li over the 32 rows, in base 2
+        // ---- online softmax of head li over the 32 rows, in base 2; each
+        //      wave reads the other half's partials only (a sum of two terms
+        //      is the same in either order, so both waves get equal logits)
         float sv[8];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-            const f32x4_t s0 = Sx[buf][ht][0][rt][lane], s1 = Sx[buf][ht][1][rt][lane];
+            const f32x4_t so = Sx[buf][ht][half ^ 1][rt][lane];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                sv[4 * rt + i] = rsc[4 * rt + i] >= 0.f ? s0[i] + s1[i] : -INFINITY;   // -1: masked
+                sv[4 * rt + i] = rsc[4 * rt + i] >= 0.f ? part[rt][i] + so[i] : -INFINITY;   // -1: masked
             }
         }
         float mx = sv[0];
