@@ -781,27 +781,42 @@ __global__ __launch_bounds__(SEL_NT) void topk_seg_emit_kernel(const uint16_t* s
     if (s0 >= V) return;
     const int nseg = (V + seg - 1) / seg;
     __shared__ uint32_t ctot[257];
+    __shared__ uint32_t cpre[257];
+    __shared__ uint32_t gsum[SEL_NT / 64];
     __shared__ uint32_t pick[2];
     const uint16_t* sr = scores + (size_t)row * ld;
     const int nvec_row = ld / 8;
     uint4 q[2];
     sel_load(sr, nvec_row, s0, q);
     // the coarse digit and the rank in it, from the count kernel's records;
-    // suffix sums over every segment of the row: thread t adds cum[t] of
-    // segments 0, 1, .. (sixteen loads in flight)
+    // suffix sums over every segment of the row and over the segments before
+    // this one: thread t adds cum[t] of segments 0, 1, .. (sixteen loads in
+    // flight), and the keys above b* of the segments before this one are
+    // added up at the same time, so nothing waits for the fine digit below
     const uint32_t* rr = rec + (size_t)row * seg_stride * SEL_REC;
     const uint32_t bstar = min(rr[258], 255u), r1 = rr[259];
     {
-        uint32_t c = 0;
+        uint32_t g0 = 0;
+        for (int i = tid; i < sgi; i += SEL_NT) g0 += rr[(size_t)i * SEL_REC];
+        uint32_t c = 0, cp = 0;
         for (int i0 = 0; i0 < nseg; i0 += 16) {
             uint32_t v[16];
 #pragma unroll
             for (int u = 0; u < 16; ++u) v[u] = i0 + u < nseg ? rr[(size_t)(i0 + u) * SEL_REC + 1 + tid] : 0u;
 #pragma unroll
-            for (int u = 0; u < 16; ++u) c += v[u];
+            for (int u = 0; u < 16; ++u) {
+                c += v[u];
+                cp += i0 + u < sgi ? v[u] : 0u;
+            }
         }
         ctot[tid] = c;
-        if (tid == 0) ctot[256] = 0u;
+        cpre[tid] = cp;
+        if (tid == 0) {
+            ctot[256] = 0u;
+            cpre[256] = 0u;
+        }
+        g0 = wave_incl_scan(g0);
+        if ((tid & 63) == 63) gsum[tid >> 6] = g0;
     }
     if (tid == 0) {                                          // defined even if no bin qualifies
         pick[0] = 0u;
@@ -816,17 +831,13 @@ __global__ __launch_bounds__(SEL_NT) void topk_seg_emit_kernel(const uint16_t* s
     __syncthreads();
     const uint32_t fstar = min(pick[0], 255u), rem = pick[1];   // fstar indexes cum[0..256]
     const uint32_t T = (bstar << 8) | fstar;
-    // outputs of the segments before this one: their keys above T and their
-    // keys equal to T
-    uint32_t gtp = 0, eqp = 0;
-    for (int i = tid; i < sgi; i += SEL_NT) {
-        const uint32_t* ri = rr + (size_t)i * SEL_REC;
-        gtp += ri[0] + ri[1 + fstar + 1];
-        eqp += ri[1 + fstar] - ri[1 + fstar + 1];
-    }
+    // outputs of the segments before this one: their keys above T (those
+    // above b*, and those of bin b* above f*) and their keys equal to T
+    uint32_t gt_before = cpre[fstar + 1];
+#pragma unroll
+    for (int w = 0; w < SEL_NT / 64; ++w) gt_before += gsum[w];
+    const uint32_t eq_before = cpre[fstar] - cpre[fstar + 1];
     int parity = 0;
-    uint32_t a0, b0, gt_before, eq_before;
-    block_exscan2(gtp, eqp, a0, b0, gt_before, eq_before, parity);
     uint32_t out_base = gt_before + min(eq_before, rem);
     uint32_t rem_left = rem - min(eq_before, rem);
     for (int rnd = 0; rnd < rounds; ++rnd) {
