@@ -95,6 +95,127 @@ __global__ __launch_bounds__(256) void proj_large(const T* __restrict__ X, const
         }
 }
 
+// Many rows, bf16 (prefill chunks): 256 x 160 output tiles (the 4096-row
+// compressor projection of 2560 columns is 16 x 16 tiles, one per compute
+// unit), four waves of 128 x 80, the contraction in stages of 64 channels
+// that go from memory straight into LDS (direct-to-LDS loads), two stages in
+// flight: the next stage's loads are issued right after the barrier that
+// publishes the current one.  A stage row is the row's 8 chunks of 16 bytes,
+// chunk c at slot c ^ ((row / 2) mod 8), so the 16 lanes that read one chunk
+// of 16 consecutive rows cover all 64 banks.  Rows past M / N are clamped
+// (their outputs dropped); K is a multiple of the stage.
+constexpr int PG_BM = 256, PG_BN = 160, PG_BK = 64;
+
+__global__ __launch_bounds__(256) void proj_lds(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
+                                                const uint16_t* __restrict__ Wi, int n_main, int N, int M, int K,
+                                                void* __restrict__ P, GemmShape sh)
+{
+    static_assert(PG_BK == 64 && PG_BM == 256 && PG_BN == 160, "8 chunks per stage row; 32 + 20 row blocks of 8");
+    // the two stages as separate objects, so that reads of one need not wait
+    // for the loads in flight into the other
+    __shared__ __attribute__((aligned(16))) uint8_t As0[PG_BM * 128];
+    __shared__ __attribute__((aligned(16))) uint8_t As1[PG_BM * 128];
+    __shared__ __attribute__((aligned(16))) uint8_t Bs0[PG_BN * 128];
+    __shared__ __attribute__((aligned(16))) uint8_t Bs1[PG_BN * 128];
+    X += blockIdx.z * sh.gx;
+    W += blockIdx.z * sh.gw;
+    Wi += blockIdx.z * sh.gw;
+    const size_t p0 = blockIdx.z * sh.gp;
+    const int lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int bm0 = blockIdx.y * PG_BM, bn0 = blockIdx.x * PG_BN;
+    const int wm = wave >> 1, wn = wave & 1;                   // this wave's 128 x 80 sub-tile
+
+    // direct-to-LDS sources: the u-th load of wave w fills row block 4u + w
+    // (rows 8 (4u + w) .. +7, 1 KB), lane l the slot l mod 8 of row l / 8,
+    // i.e. chunk (l mod 8) ^ ((row / 2) mod 8), the same chunk for every u
+    const int rr = lane >> 3;
+    const int ch = (lane & 7) ^ ((4 * wave + (rr >> 1)) & 7);
+    const uint16_t* asrc[8];
+    const uint16_t* bsrc[5];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int m = min(bm0 + 8 * (4 * u + wave) + rr, M - 1);
+        asrc[u] = X + (size_t)m * sh.ldx + 8 * ch;
+    }
+#pragma unroll
+    for (int u = 0; u < 5; ++u) {
+        const int n = min(bn0 + 8 * (4 * u + wave) + rr, N - 1);
+        bsrc[u] = (n < n_main ? W + (size_t)n * K : Wi + (size_t)(n - n_main) * K) + 8 * ch;
+    }
+    auto issue = [&](int k0, uint8_t* as, uint8_t* bs) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            __builtin_amdgcn_global_load_lds((const CSA_GLOBAL void*)(asrc[u] + k0),
+                                             (CSA_LDS void*)(as + (4 * u + wave) * 1024), 16, 0, 0);
+#pragma unroll
+        for (int u = 0; u < 5; ++u)
+            __builtin_amdgcn_global_load_lds((const CSA_GLOBAL void*)(bsrc[u] + k0),
+                                             (CSA_LDS void*)(bs + (4 * u + wave) * 1024), 16, 0, 0);
+    };
+
+    f32x4_t acc[8][5];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 5; ++j) acc[i][j] = zero4();
+    // stage kb in buffer kb mod 2: wait for this wave's loads of it, a
+    // barrier (everyone's have landed, and stage kb-1 is no longer read), the
+    // fragments of both steps into registers, then the loads of stage kb+1
+    // into the other buffer (issued after this stage's reads, so nothing
+    // makes the reads wait for them), then the MFMAs.  Fragment of row li (of
+    // a 16-row tile), channels 8 (4s + g) .. +7 of the stage: slot
+    // (4s + g) ^ (li / 2) of the row (tile rows start at multiples of 16, so
+    // the row's (row / 2) mod 8 is li / 2)
+    const int nk = K / PG_BK;
+    issue(0, As0, Bs0);
+    for (int kb = 0; kb < nk; ++kb) {
+        const bool odd = kb & 1;
+        const uint8_t* A = (odd ? As1 : As0) + (size_t)(128 * wm) * 128;
+        const uint8_t* B = (odd ? Bs1 : Bs0) + (size_t)(80 * wn) * 128;
+        __builtin_amdgcn_s_waitcnt(0x0F70);                     // vmcnt(0)
+        __syncthreads();
+        uint4 af[2][8], bf[2][5];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int off = li * 128 + 16 * ((4 * s + g) ^ (li >> 1));
+#pragma unroll
+            for (int i = 0; i < 8; ++i) af[s][i] = *(const uint4*)(A + 16 * i * 128 + off);
+#pragma unroll
+            for (int j = 0; j < 5; ++j) bf[s][j] = *(const uint4*)(B + 16 * j * 128 + off);
+        }
+        if (kb + 1 < nk) issue((kb + 1) * PG_BK, odd ? As0 : As1, odd ? Bs0 : Bs1);
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 5; ++j) acc[i][j] = MmaBF16::step(af[s][i], bf[s][j], acc[i][j]);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 5; ++j) {
+            const int n = bn0 + 80 * wn + 16 * j + li;
+            if (n >= N) continue;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int m = bm0 + 128 * wm + 16 * i + 4 * g + q;
+                if (m < M) store_out(P, p0 + (size_t)m * sh.ldp + n, sh.out_bf16, acc[i][j][q]);
+            }
+        }
+}
+
+// The LDS-staged kernel when the shape suits it: bf16, whole stages, rows
+// 16-byte aligned, and enough tiles to fill the compute units.
+static bool use_proj_lds(bool bf16, int M, int N, int K, int groups, const void* X, const void* W, const void* Wi,
+                         int ldx)
+{
+    const long tiles = (long)((M + PG_BM - 1) / PG_BM) * ((N + PG_BN - 1) / PG_BN) * groups;
+    const uintptr_t al = (uintptr_t)X | (uintptr_t)W | (uintptr_t)Wi;
+    return bf16 && K % PG_BK == 0 && ldx % 8 == 0 && al % 16 == 0 && tiles >= 128;
+}
+
 // Few rows (decode): a 16 x 16 output tile per workgroup; the NW waves
 // split K into contiguous parts (K / NW a multiple of the MMA step), summed
 // in wave order.  Sixteen waves keep a whole 16-column slice of the weights
@@ -694,6 +815,10 @@ hipError_t launch_compress(hipStream_t st, const CompressArgs& args, const void*
             else
                 proj_small<float, MmaF32, 4><<<grid, 256, 0, st>>>((const float*)H, (const float*)W, (const float*)Wi,
                                                                    n_main, N, M, d, a.P, sh);
+        } else if (use_proj_lds(bf16, M, N, d, 1, H, W, Wi, d)) {
+            dim3 grid((N + PG_BN - 1) / PG_BN, (M + PG_BM - 1) / PG_BM);
+            proj_lds<<<grid, 256, 0, st>>>((const uint16_t*)H, (const uint16_t*)W, (const uint16_t*)Wi, n_main, N, M, d,
+                                           a.P, sh);
         } else {
             dim3 grid((N + 127) / 128, (M + 127) / 128);
             if (bf16)
@@ -750,6 +875,9 @@ hipError_t launch_linear(hipStream_t st, bool bf16, int M, int K, int N, int gro
         else
             proj_small<float, MmaF32, 4><<<grid, 256, 0, st>>>((const float*)X, (const float*)W, (const float*)W, N,
                                                                N, M, K, Y, sh);
+    } else if (use_proj_lds(bf16, M, N, K, groups, X, W, W, K * groups)) {
+        dim3 grid((N + PG_BN - 1) / PG_BN, (M + PG_BM - 1) / PG_BM, groups);
+        proj_lds<<<grid, 256, 0, st>>>((const uint16_t*)X, (const uint16_t*)W, (const uint16_t*)W, N, N, M, K, Y, sh);
     } else {
         dim3 grid((N + 127) / 128, (M + 127) / 128, groups);
         if (bf16)

@@ -62,3 +62,26 @@ def test_linear_fp32(rows):
     want = np.concatenate([X[:, j * K:(j + 1) * K].astype(np.float64) @ W[j].T.astype(np.float64) for j in range(G)], 1)
     assert_close(Y.cpu().numpy(), want, 1e-4, "grouped fp32")
     assert_close(Y1.float().cpu().numpy(), want[:, :N], 2e-2, "linear bf16 out")
+
+
+@pytest.mark.parametrize("groups", [1, 2])
+def test_linear_bf16_many_rows(groups):
+    """bf16 operands, many rows (the LDS-staged 256 x 160 tiles): rows and
+    columns that end inside a tile, against the fp64 product of the same bf16
+    values; fp32 out at 1e-4, bf16 out at 2e-2."""
+    print(f"linear bf16 many rows, {groups} group(s)", flush=True)
+    g = synth.rng(402)
+    M, K, N = 2333, 1024, 1999
+    X = synth.to_bf16_values(synth.normal(g, (M, groups * K)))
+    W = np.stack([_w(g, N, K) for _ in range(groups)])
+    bf = torch.bfloat16
+    Y = torch.empty((M, groups * N), device="cuda")
+    abi.grouped_linear(abi.ACT_BF16, abi.ACT_F32, groups, to_dev(X, bf), to_dev(W, bf), Y)
+    Yb = torch.empty((M, groups * N), dtype=bf, device="cuda")
+    abi.grouped_linear(abi.ACT_BF16, abi.ACT_BF16, groups, to_dev(X, bf), to_dev(W, bf), Yb)
+    torch.cuda.synchronize()
+    want = np.concatenate([X[:, j * K:(j + 1) * K].astype(np.float64) @ W[j].T.astype(np.float64)
+                           for j in range(groups)], 1)
+    e = assert_close(Y.cpu().numpy(), want, 1e-4, "fp32 out")
+    eb = assert_close(Yb.float().cpu().numpy(), want, 2e-2, "bf16 out")
+    print(f"  errors fp32 {e:.2e} bf16 {eb:.2e}", flush=True)
