@@ -315,12 +315,15 @@ int csa_index_scores(void* stream, const csa_layer_desc* layer, const csa_batch*
  * arguments, scores and n_valid as csa_index_scores, plus out_idx
  * [n_tokens x top_k] int32 with exactly the selection csa_topk_select would
  * make from those scores (k = layer->top_k: the k largest, ties to the lower
- * index, ascending, -1 padded).  With bf16 scores the indexer's workgroups
- * also count their chunk's scores by the top 8 bits of the order-preserving
- * score key while they stream the keys (the selection's first radix digit,
- * into ws), so the selection needs only a counting and an emitting pass over
- * segments of each row (many workgroups per row), instead of a histogram
- * pipeline of its own.
+ * index, ascending, -1 padded).  With bf16 scores the selection's first
+ * radix digit comes from per-chunk counts of the scores by the top 8 bits of
+ * the order-preserving score key (into ws): for decode-shaped calls the
+ * indexer's workgroups count their chunk while they stream the keys; for
+ * prefill-shaped calls (many new tokens per request; the scan is bound by
+ * its MFMAs) a pass over the stored scores counts them per segment.  The
+ * selection then needs only a counting and an emitting pass over segments
+ * of each row (many workgroups per row), instead of a histogram pipeline of
+ * its own.
  * Requires ld % 8 == 0 and 16-byte aligned scores and ws (bf16 scores).
  * fp32 scores run the two calls' kernels in order.
  *   ws >= csa_workspace_size(CSA_OP_INDEX_TOPK, n_tokens, ld): per (query,

@@ -459,6 +459,8 @@ int csa_index_topk(void* stream, const csa_layer_desc* layer, const csa_batch* b
     a.hist = (uint16_t*)ws;
     int chunk = 0;
     hipError_t e = csa::launch_index(st, a, max_vis, batch->max_new, &chunk);
+    if (e == hipSuccess && chunk == 0)                       // scores stored without their counts
+        e = csa::launch_seg_hist(st, n_tokens, scores, ld, n_valid, (uint16_t*)ws, &chunk);
     if (e == hipSuccess)
         e = csa::launch_topk_hist(st, n_tokens, scores, ld, n_valid, (const uint16_t*)ws, (ld + chunk - 1) / chunk,
                                   chunk, layer->top_k, out_idx,

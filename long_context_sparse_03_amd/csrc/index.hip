@@ -306,7 +306,7 @@ constexpr int PF_TILE = 128;                  // keys per LDS tile
 constexpr int PF_ECH = 8192;                  // keys per workgroup
 constexpr int PF_CI = 128;                    // key channels (16 chunks of 16 bytes)
 
-template <int HT, int S, bool BF16OUT, bool HIST>
+template <int HT, int S, bool BF16OUT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void index_prefill_kernel(IndexArgs a, int groups_per_req)
 {
     static_assert(S * 8 * 4 == PF_CI, "S steps of eight channels in each of four lane groups cover a key");
@@ -317,12 +317,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void i
     __shared__ __attribute__((aligned(16))) uint16_t Ks1[PF_TILE * PF_CI];
     __shared__ int bt[PF_ECH / 32 + 2];
     __shared__ int cu_sh[1025];
-    __shared__ uint32_t hcnt[PF_QPW][256];                          // fused top-k: per wave (query) counts
     const int lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int req = blockIdx.y / groups_per_req, grp = blockIdx.y % groups_per_req;
     if (a.n_req >= 1024) return;                                    // host dispatch keeps n_req small here
-    for (int i = threadIdx.x; i < PF_QPW * 256; i += blockDim.x) (&hcnt[0][0])[i] = 0u;
     for (int i = threadIdx.x; i <= a.n_req; i += blockDim.x) cu_sh[i] = a.cu_new[i];
     __syncthreads();
     const int cu = cu_sh[req], n_tok = cu_sh[req + 1] - cu;
@@ -391,22 +389,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void i
     // store issued right before the end-of-tile wait would hold it up)
     float xs[PF_TILE / 64];
     int es = -1;                                                    // first key of those scores (-1: none)
-    // fused top-k: the count bins of the stored scores (~0: none), added to
-    // the counts at the top of the next pass, where no tile load is in
-    // flight (an LDS atomic issued while the direct-to-LDS loads of the next
-    // tile are pending is made to wait for them)
-    uint32_t hb[PF_TILE / 64];
-#pragma unroll
-    for (int eb = 0; eb < PF_TILE / 64; ++eb) hb[eb] = ~0u;
-    auto hist_flush = [&]() {
-        if constexpr (HIST) {
-#pragma unroll
-            for (int eb = 0; eb < PF_TILE / 64; ++eb) {
-                count_bins_quad(hcnt[wave], hb[eb]);
-                hb[eb] = ~0u;
-            }
-        }
-    };
     auto store_scores = [&]() {
         if (es < 0) return;
         // the key offsets are recomputed (a spilled copy's reload would wait
@@ -422,7 +404,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void i
                 if constexpr (BF16OUT) {
                     const uint16_t b = canon_bf16(f32_to_bf16(x));   // a value rounding to -0 is stored as +0
                     ((uint16_t*)a.scores)[(size_t)gq * a.ld + e] = b;
-                    if (HIST) hb[eb] = key16(b) >> 8;
                 } else {
                     ((float*)a.scores)[(size_t)gq * a.ld + e] = x;
                 }
@@ -481,31 +462,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void i
     tile_done();
     for (int it = 0; it < n_tiles; it += 2) {
         const int t0 = e0 + it * PF_TILE;
-        hist_flush();
         // Ks1 was last read in the previous pass, finished before its barrier
         if (it + 1 < n_tiles) issue_tile(t0 + PF_TILE, Ks1);
         store_scores();
         compute(t0, Ks0);
         tile_done();
         if (it + 1 >= n_tiles) break;
-        hist_flush();
         if (it + 2 < n_tiles) issue_tile(t0 + 2 * PF_TILE, Ks0);
         store_scores();
         compute(t0 + PF_TILE, Ks1);
         tile_done();
     }
-    hist_flush();                                                   // the counts of the last stored scores
     store_scores();
-    hist_flush();
-    // fused top-k: each valid query's counts of this chunk, lane l bins 4l..4l+3
-    if (HIST) {
-        __syncthreads();
-        if (qvalid) {
-            uint16_t* h = a.hist + ((size_t)gq * a.hist_chunks + blockIdx.x) * 256 + 4 * lane;
-            const uint32_t* c = &hcnt[wave][4 * lane];
-            *(uint2*)h = make_uint2(c[0] | (c[1] << 16), c[2] | (c[3] << 16));
-        }
-    }
 }
 
 // MXFP4 decode launch: as the bf16 decode kernel, with the stored key bytes
@@ -674,14 +642,14 @@ static void launch_fmt(hipStream_t st, const IndexArgs& a, dim3 grid)
     }
 }
 
-template <bool BF16OUT, bool HIST>
+template <bool BF16OUT>
 static void launch_prefill(hipStream_t st, const IndexArgs& a, dim3 grid, int groups)
 {
     const int HT = (a.nh + 15) / 16;
-    if (HT == 4) index_prefill_kernel<4, 4, BF16OUT, HIST><<<grid, 512, 0, st>>>(a, groups);
-    else if (HT == 3) index_prefill_kernel<3, 4, BF16OUT, HIST><<<grid, 512, 0, st>>>(a, groups);
-    else if (HT == 2) index_prefill_kernel<2, 4, BF16OUT, HIST><<<grid, 512, 0, st>>>(a, groups);
-    else index_prefill_kernel<1, 4, BF16OUT, HIST><<<grid, 512, 0, st>>>(a, groups);
+    if (HT == 4) index_prefill_kernel<4, 4, BF16OUT><<<grid, 512, 0, st>>>(a, groups);
+    else if (HT == 3) index_prefill_kernel<3, 4, BF16OUT><<<grid, 512, 0, st>>>(a, groups);
+    else if (HT == 2) index_prefill_kernel<2, 4, BF16OUT><<<grid, 512, 0, st>>>(a, groups);
+    else index_prefill_kernel<1, 4, BF16OUT><<<grid, 512, 0, st>>>(a, groups);
 }
 
 template <bool HIST>
@@ -705,13 +673,13 @@ hipError_t launch_index(hipStream_t st, const IndexArgs& args, int max_visible, 
     // the per-chunk counts of the fused top-k (bf16 scores only)
     const bool hist = a.hist != nullptr && a.score_bf16;
     if (a.idx_fmt == 1 && a.cI == 128 && a.nh <= 64 && max_new >= 2 * PF_QPW && a.n_req < 1024) {
-        if (chunk) *chunk = PF_ECH;
-        a.hist_chunks = (a.ld + PF_ECH - 1) / PF_ECH;
+        // MFMA-bound: the counts are left to a pass over the stored scores
+        // (*chunk = 0), which costs less than counting here
+        if (chunk) *chunk = 0;
         const int groups = (max_new + PF_QPW - 1) / PF_QPW;
         dim3 grid(max_visible > 0 ? (max_visible + PF_ECH - 1) / PF_ECH : 1, a.n_req * groups);
-        if (!a.score_bf16) launch_prefill<false, false>(st, a, grid, groups);
-        else if (hist) launch_prefill<true, true>(st, a, grid, groups);
-        else launch_prefill<true, false>(st, a, grid, groups);
+        if (!a.score_bf16) launch_prefill<false>(st, a, grid, groups);
+        else launch_prefill<true>(st, a, grid, groups);
         return hipGetLastError();
     }
     const int epw = a.idx_fmt == 2 ? IDX_EPW : IDXD_EPW;

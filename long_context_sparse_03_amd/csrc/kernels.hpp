@@ -109,6 +109,8 @@ int index_min_chunk(int idx_fmt);
 // bits from the indexer's per-chunk counts, then a counting and an emitting
 // pass over segments of each row (many workgroups per row); ws holds the
 // per-segment counts (topk_hist_workspace bytes, 16-byte aligned).
+hipError_t launch_seg_hist(hipStream_t st, int n_rows, const void* scores, int ld, const int32_t* n_valid,
+                           uint16_t* hist, int* chunk);
 hipError_t launch_topk_hist(hipStream_t st, int n_rows, const void* scores, int ld, const int32_t* n_valid,
                             const uint16_t* hist, int hist_chunks, int chunk, int k, int32_t* out, void* ws);
 size_t topk_hist_workspace(int n_rows, int ld);

@@ -880,6 +880,55 @@ __global__ __launch_bounds__(SEL_NT) void topk_seg_emit_kernel(const uint16_t* s
     }
 }
 
+// Coarse counts of one segment of a row whose scores were stored without
+// them: the 256 bins of the keys' top 8 bits, in the layout of the index
+// launches' per-chunk counts (the segment is the chunk).  Each lane counts
+// into its own copy of a bin (32 copies, lane mod 32), so the lanes of a
+// wave, whose keys mostly fall into a few bins, do not queue on one LDS
+// address; the copies are added at the end.
+__global__ __launch_bounds__(SEL_NT) void topk_seg_hist_kernel(const uint16_t* scores, int ld, const int32_t* n_valid,
+                                                               int rounds, int nseg, uint16_t* hist)
+{
+    __shared__ uint32_t hc[256 * 32];
+    const int row = blockIdx.y, sgi = blockIdx.x, tid = threadIdx.x;
+    for (int i = tid; i < 256 * 32; i += SEL_NT) hc[i] = 0u;
+    const int V = min(n_valid[row], ld);
+    const int s0 = sgi * rounds * SEL_ROUND;
+    const uint16_t* sr = scores + (size_t)row * ld;
+    const int nvec_row = ld / 8;
+    const uint32_t cp = tid & 31;
+    __syncthreads();
+    if (s0 < V) {                                            // uniform
+        uint4 q[2];
+        sel_load(sr, nvec_row, s0, q);
+        for (int rnd = 0; rnd < rounds; ++rnd) {
+            const int p0 = s0 + rnd * SEL_ROUND;
+            if (p0 >= V) break;                              // uniform
+            uint4 qn[2];                                     // the next round's keys load meanwhile
+            if (rnd + 1 < rounds && p0 + SEL_ROUND < V) sel_load(sr, nvec_row, p0 + SEL_ROUND, qn);
+            const int base = p0 + tid * SEL_KPT;
+            const uint32_t w8[8] = {q[0].x, q[0].y, q[0].z, q[0].w, q[1].x, q[1].y, q[1].z, q[1].w};
+#pragma unroll
+            for (int h = 0; h < 8; ++h) {
+                const uint32_t kp = key16x2(w8[h]);
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const uint32_t kv = (kp >> (16 * half)) & 0xFFFFu;
+                    if (base + 2 * h + half < V) atomicAdd(&hc[(kv >> 8) * 32 + cp], 1u);
+                }
+            }
+            q[0] = qn[0];
+            q[1] = qn[1];
+        }
+    }
+    __syncthreads();
+    // thread t adds the 32 copies of bin t (rotated start: fewer bank conflicts)
+    uint32_t c = 0;
+#pragma unroll 8
+    for (int j = 0; j < 32; ++j) c += hc[tid * 32 + ((j + tid) & 31)];
+    hist[((size_t)row * nseg + sgi) * 256 + tid] = (uint16_t)c;
+}
+
 // Rounds of SEL_ROUND keys per segment: doubled while a launch would have
 // more than 4096 segment workgroups, at most 8 (decode rows: one round).
 static int sel_rounds(int n_rows, int ld)
@@ -894,6 +943,21 @@ size_t topk_hist_workspace(int n_rows, int ld)
 {
     const int seg = sel_rounds(n_rows, ld) * SEL_ROUND;
     return (size_t)n_rows * ((ld + seg - 1) / seg) * SEL_REC * 4;
+}
+
+// The per-segment coarse counts of rows stored without them, in the segments
+// launch_topk_hist will use (*chunk: the segment length).
+hipError_t launch_seg_hist(hipStream_t st, int n_rows, const void* scores, int ld, const int32_t* n_valid,
+                           uint16_t* hist, int* chunk)
+{
+    const int rounds = sel_rounds(n_rows, ld);
+    const int seg = rounds * SEL_ROUND;
+    *chunk = seg;
+    if (n_rows <= 0) return hipSuccess;
+    const int nseg = (ld + seg - 1) / seg;
+    topk_seg_hist_kernel<<<dim3(nseg, n_rows), SEL_NT, 0, st>>>((const uint16_t*)scores, ld, n_valid, rounds, nseg,
+                                                                hist);
+    return hipGetLastError();
 }
 
 hipError_t launch_topk_hist(hipStream_t st, int n_rows, const void* scores, int ld, const int32_t* n_valid,
