@@ -64,15 +64,14 @@ def test_linear_fp32(rows):
     assert_close(Y1.float().cpu().numpy(), want[:, :N], 2e-2, "linear bf16 out")
 
 
-@pytest.mark.parametrize("groups,K", [(1, 1024), (2, 1024), (2, 992)])
-def test_linear_bf16_many_rows(groups, K):
-    """bf16 operands, many rows (the LDS-staged 256 x 160 tiles when K is a
-    multiple of their 64-channel stage, else the 128 x 128 tiles): rows and
+@pytest.mark.parametrize("groups,M,K,N", [(1, 2333, 1024, 1999), (2, 2333, 1024, 1999), (1, 600, 1152, 700)])
+def test_linear_bf16_many_rows(groups, M, K, N):
+    """bf16 operands, more than 64 rows: the LDS-staged 256 x 160 tiles when
+    the output has at least 128 of them, else the 128 x 128 tiles; rows and
     columns that end inside a tile, against the fp64 product of the same bf16
     values; fp32 out at 1e-4, bf16 out at 2e-2."""
-    print(f"linear bf16 many rows, {groups} group(s), K {K}", flush=True)
+    print(f"linear bf16 many rows, {groups} group(s), {M} x {K} x {N}", flush=True)
     g = synth.rng(402)
-    M, N = 2333, 1999
     X = synth.to_bf16_values(synth.normal(g, (M, groups * K)))
     W = np.stack([_w(g, N, K) for _ in range(groups)])
     bf = torch.bfloat16
