@@ -437,26 +437,56 @@ __global__ __launch_bounds__(64 * NW) void proj_ksplit(const uint16_t* __restric
 // aligned and n, n2 are multiples of 4, each thread's pieces of a batch all
 // loaded before any is stored (one memory latency per batch).  With ns > 1
 // the source is ns partial rows sst floats apart, added in order.
+// Loads of a projected row for copy_row / token_row: pieces b, b + blockDim,
+// .. (U of them) of T (float4 or float), of ns partial planes sst floats
+// apart, summed in plane order.  Every load is issued before any is used:
+// pieces past the row (n pieces) read the row's last piece instead (never
+// stored), so no load sits behind a per-lane branch, which would make each
+// of them wait for its data before the next is issued.
+template <class T, int U>
+CSA_DEV void row_planes(const float* __restrict__ src, int n, int b, int ns, size_t sst, T (&v)[U])
+{
+    // pieces u whose slot starts past the row in every thread are skipped
+    // (a uniform test: b - threadIdx.x is the workgroup's first piece)
+    const int b0 = b - (int)threadIdx.x;
+    int ic[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) ic[u] = min(b + u * (int)blockDim.x, n - 1);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        if (u == 0 || b0 + u * (int)blockDim.x < n) v[u] = ((const T*)src)[ic[u]];
+    if (ns <= 1) return;
+    T x[PROJ_PARTS - 1][U];
+#pragma unroll
+    for (int s = 1; s < PROJ_PARTS; ++s)
+        if (s < ns)
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (u == 0 || b0 + u * (int)blockDim.x < n) x[s - 1][u] = ((const T*)(src + s * sst))[ic[u]];
+#pragma unroll
+    for (int s = 1; s < PROJ_PARTS; ++s)
+        if (s < ns)
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (u == 0 || b0 + u * (int)blockDim.x < n) v[u] += x[s - 1][u];
+    for (int s = PROJ_PARTS; s < ns; ++s)                      // (more planes than the projection makes)
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (u == 0 || b0 + u * (int)blockDim.x < n) v[u] += ((const T*)(src + s * sst))[ic[u]];
+}
+
+// dst[0..n) (and dst2[0..n2), n2 <= n) = the sum of the ns partial planes of
+// the row at src.
 CSA_DEV void copy_row(float* __restrict__ dst, const float* __restrict__ src, int n, float* dst2 = nullptr,
                       int n2 = 0, int ns = 1, size_t sst = 0)
 {
     constexpr int U = 4;
+    if (n <= 0) return;
     if (((n | n2) & 3) == 0 && (sst & 3) == 0 && (((uintptr_t)dst | (uintptr_t)src | (uintptr_t)dst2) & 15) == 0) {
         const int n4 = n >> 2;
         for (int b = threadIdx.x; b < n4; b += U * blockDim.x) {
             float4 v[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int i = b + u * blockDim.x;
-                if (i < n4) v[u] = ((const float4*)src)[i];
-            }
-            for (int s = 1; s < ns; ++s) {
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int i = b + u * blockDim.x;
-                    if (i < n4) v[u] += ((const float4*)(src + s * sst))[i];
-                }
-            }
+            row_planes<float4, U>(src, n4, b, ns, sst, v);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int i = b + u * blockDim.x;
@@ -467,18 +497,7 @@ CSA_DEV void copy_row(float* __restrict__ dst, const float* __restrict__ src, in
     } else {
         for (int b = threadIdx.x; b < n; b += U * blockDim.x) {
             float v[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int i = b + u * blockDim.x;
-                if (i < n) v[u] = src[i];
-            }
-            for (int s = 1; s < ns; ++s) {
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int i = b + u * blockDim.x;
-                    if (i < n) v[u] += src[s * sst + i];
-                }
-            }
+            row_planes<float, U>(src, n, b, ns, sst, v);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int i = b + u * blockDim.x;
@@ -593,6 +612,11 @@ CSA_DEV void merge_located(const CompressArgs& a, int e, int req, int ent, float
         float mx = -INFINITY, den = 0.f, acc = 0.f;
         for (int r0 = 0; r0 < nrows; r0 += MB) {
             float z[MB], cv[MB];
+            // every load of the batch (a row's Z and C values, the partial
+            // planes of rows projected in this call, the bias) is issued
+            // before any is used; the planes are then added in plane order
+            float zl[MB], cl[MB], bl[MB], zx[MB][PROJ_PARTS - 1], cx[MB][PROJ_PARTS - 1];
+            bool nw[MB];
 #pragma unroll
             for (int u = 0; u < MB; ++u) {
                 const int rr = min(r0 + u, nrows - 1);
@@ -602,14 +626,33 @@ CSA_DEV void merge_located(const CompressArgs& a, int e, int req, int ent, float
                 const bool new_row = p >= s0;                   // projected in this call (partials)
                 const float* row = new_row ? a.P + (size_t)(cu + p - s0) * a.ncols : tail + (size_t)(p % a.R) * a.ncols;
                 const int cz = second ? colZb : colZa, cC = second ? colCb : colCa;
-                float zv = row[cz], cvv = row[cC];
+                nw[u] = new_row;
+                zl[u] = row[cz];
+                cl[u] = row[cC];
+                bl[u] = (second ? Bb : Ba)[r * w + cc];
                 if (new_row) {
-                    for (int s = 1; s < a.n_psplit; ++s) {
-                        zv += row[s * a.psplit_stride + cz];
-                        cvv += row[s * a.psplit_stride + cC];
+#pragma unroll
+                    for (int s = 1; s < PROJ_PARTS; ++s) {
+                        if (s < a.n_psplit) {
+                            zx[u][s - 1] = row[s * a.psplit_stride + cz];
+                            cx[u][s - 1] = row[s * a.psplit_stride + cC];
+                        }
                     }
                 }
-                z[u] = zv + (second ? Bb : Ba)[r * w + cc];
+            }
+#pragma unroll
+            for (int u = 0; u < MB; ++u) {
+                float zv = zl[u], cvv = cl[u];
+                if (nw[u]) {                                    // (n_psplit <= PROJ_PARTS)
+#pragma unroll
+                    for (int s = 1; s < PROJ_PARTS; ++s) {
+                        if (s < a.n_psplit) {
+                            zv += zx[u][s - 1];
+                            cvv += cx[u][s - 1];
+                        }
+                    }
+                }
+                z[u] = zv + bl[u];
                 cv[u] = cvv;
             }
             float cm = -INFINITY;
@@ -699,6 +742,41 @@ __global__ __launch_bounds__(256) void tail_update_kernel(CompressArgs a)
              a.n_psplit, a.psplit_stride);
 }
 
+// New token gtok of a call with at most one new token per request: the sum
+// of its projected row's partial planes goes into the request's tail ring
+// (slot pos mod R) and its first c channels (C^a, HCA: C) into xs; returns
+// the token's position.  The row's loads do not depend on the position, so
+// they are issued before the wait for it (one round trip to memory for both,
+// not two in a row).  Threads take 16-byte pieces when the row allows.
+CSA_DEV int token_row(const CompressArgs& a, int gtok, float* xs)
+{
+    const int req = a.one_per_req ? gtok : find_request(a.cu_new, a.n_req, gtok);
+    const int pos_raw = a.start_pos[req];
+    const float* src = a.P + (size_t)gtok * a.ncols;
+    const int n = a.ncols, nc = a.c;
+    constexpr int U = 4;
+    const bool vec = ((n | nc) & 3) == 0 && (a.psplit_stride & 3) == 0 && (((uintptr_t)src | (uintptr_t)xs) & 15) == 0 &&
+                     (((uintptr_t)a.state | a.tail_off | a.state_stride) & 15) == 0;
+    if (vec && n > 0 && (n >> 2) <= U * (int)blockDim.x) {      // the whole row in one batch
+        const int n4 = n >> 2;
+        float4 v[U];
+        row_planes<float4, U>(src, n4, (int)threadIdx.x, a.n_psplit, a.psplit_stride, v);
+        const int pos = pos_raw + (a.one_per_req ? 0 : gtok - a.cu_new[req]);
+        float* tail = (float*)((char*)a.state + (size_t)req * a.state_stride + a.tail_off) + (size_t)(pos % a.R) * n;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = (int)threadIdx.x + u * (int)blockDim.x;
+            if (i < n4) ((float4*)tail)[i] = v[u];
+            if (4 * i < nc) ((float4*)xs)[i] = v[u];
+        }
+        return pos;
+    }
+    const int pos = pos_raw + (a.one_per_req ? 0 : gtok - a.cu_new[req]);
+    float* tail = (float*)((char*)a.state + (size_t)req * a.state_stride + a.tail_off);
+    copy_row(tail + (size_t)(pos % a.R) * n, src, n, xs, nc, a.n_psplit, a.psplit_stride);
+    return pos;
+}
+
 // At most one new token per request: the merges, the window rows and the
 // tail update in one launch.  Blocks [0, nm) merge entries; block nm + g
 // handles token g: its window row, and its projected row into the tail ring.
@@ -714,13 +792,7 @@ __global__ __launch_bounds__(256) void post_decode_kernel(CompressArgs a, int nm
         return;
     }
     const int gtok = blockIdx.x - nm;
-    const int req = a.one_per_req ? gtok : find_request(a.cu_new, a.n_req, gtok);
-    const int pos = a.start_pos[req] + (a.one_per_req ? 0 : gtok - a.cu_new[req]);
-    // one pass over the projected row: into the tail ring, and its first c
-    // channels (C^a, HCA: C) into LDS for the window row
-    float* tail = (float*)((char*)a.state + (size_t)req * a.state_stride + a.tail_off);
-    copy_row(tail + (size_t)(pos % a.R) * a.ncols, a.P + (size_t)gtok * a.ncols, a.ncols, xs, a.c, a.n_psplit,
-             a.psplit_stride);
+    const int pos = token_row(a, gtok, xs);
     __syncthreads();
     norm_rope_store(xs, red, a.c, a.r, a.gamma, a.eps, (double)pos, a.theta, a.out_win + (size_t)gtok * a.c);
 }
@@ -756,10 +828,7 @@ __global__ __launch_bounds__(256) void post_decode_append_kernel(CompressArgs a,
     }
     const int gtok = blockIdx.x - nm;
     const int req = a.one_per_req ? gtok : find_request(a.cu_new, a.n_req, gtok);
-    const int pos = a.start_pos[req] + (a.one_per_req ? 0 : gtok - a.cu_new[req]);
-    float* tail = (float*)((char*)a.state + (size_t)req * a.state_stride + a.tail_off);
-    copy_row(tail + (size_t)(pos % a.R) * a.ncols, a.P + (size_t)gtok * a.ncols, a.ncols, xs, a.c, a.n_psplit,
-             a.psplit_stride);
+    const int pos = token_row(a, gtok, xs);
     __syncthreads();
     norm_rope_store(xs, red, a.c, a.r, a.gamma, a.eps, (double)pos, a.theta, a.out_win + (size_t)gtok * a.c);
     store_window_row(b, req, pos, xs);
