@@ -39,6 +39,7 @@
 
 namespace csa {
 
+
 constexpr float LOG2E = 1.4426950408889634f;
 
 template <int KVF, int C, int R, int HT>
@@ -607,14 +608,14 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
     __shared__ const char* rblk[DESC];                         // the row's scale (FP8 entries: block byte 0)
     __shared__ float rcs[R / 2], rsn[R / 2];
     __shared__ int cu_sh[257];
-    __shared__ __attribute__((aligned(16))) float gam[C];      // query norm gains
+    __shared__ __attribute__((aligned(16))) float gam[C];      // query norm gains times the softmax scale
     __shared__ __attribute__((aligned(16))) f32x4_t Sx[2][HT][2][2][64];  // partial logits per half
     __shared__ float ssx[HT][2][16];                           // partial sums of squares of the query
 
     const int lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int ht = wave % HT, half = wave / HT;               // head tile, channel half
-    for (int j = threadIdx.x; j < C; j += NT) gam[j] = a.q_gamma[j];
+    for (int j = threadIdx.x; j < C; j += NT) gam[j] = a.q_gamma[j] * a.scale_log2;
     const int gq = blockIdx.x;
     const int head = blockIdx.y * 16 * HT + 16 * ht + li;     // this lane's head
     const bool hvalid = head < a.nh;
@@ -732,14 +733,16 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
     for (int j = threadIdx.x; j < R / 2; j += NT) rope_cs_f((double)t, a.inv_freq[j], &rcs[j], &rsn[j]);
     if (tile0 < tile1) describe(tile0 * 32, true);
     {
+        // sum of squares of this lane's channels: one bf16 dot product per
+        // pair of channels
         float ss = 0.f;
 #pragma unroll
         for (int j = 0; j < KSH; ++j) {
             const uint32_t w4[4] = {QB[j].x, QB[j].y, QB[j].z, QB[j].w};
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
-                const float x0 = bf16_to_f32(w4[h] & 0xFFFF), x1 = bf16_to_f32(w4[h] >> 16);
-                ss += x0 * x0 + x1 * x1;
+                const bf16x2_t v = __builtin_bit_cast(bf16x2_t, w4[h]);
+                ss = __builtin_amdgcn_fdot2_f32_bf16(v, v, ss, false);
             }
         }
         ss = xsum32(xsum16(ss));
@@ -755,7 +758,8 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
     if (tile0 < tile1) load_tile(tile0, 0, raw[0], rsr[0]);
     if (tile0 + 1 < tile1) load_tile(tile0 + 1, 32, raw[1], rsr[1]);
 
-    // normalised, rotated, scaled query fragments of this lane's head
+    // normalised, rotated, scaled query fragments of this lane's head (the
+    // softmax scale is in gam; the rotation is linear, so it commutes)
     uint4 QF[KSH];
     {
         const float ss = ssx[ht][0][li] + ssx[ht][1][li];     // the same order in both waves
@@ -782,10 +786,8 @@ __global__ __launch_bounds__(128 * HT) void attn_ht_kernel(AttnArgs a)
                     x[j + 1] = u0 * rsn[pr] + u1 * rcs[pr];
                 }
             }
-            QF[j] = make_uint4(pack_bf16x2(x[0] * a.scale_log2, x[1] * a.scale_log2),
-                               pack_bf16x2(x[2] * a.scale_log2, x[3] * a.scale_log2),
-                               pack_bf16x2(x[4] * a.scale_log2, x[5] * a.scale_log2),
-                               pack_bf16x2(x[6] * a.scale_log2, x[7] * a.scale_log2));
+            QF[j] = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                               pack_bf16x2(x[6], x[7]));
         }
     }
 

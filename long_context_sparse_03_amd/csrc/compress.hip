@@ -432,11 +432,6 @@ __global__ __launch_bounds__(64 * NW) void proj_ksplit(const uint16_t* __restric
     }
 }
 
-// Copy n floats from src to dst (and the first n2 of them also to dst2) with
-// the threads of the block: 16-byte pieces when every pointer is 16-byte
-// aligned and n, n2 are multiples of 4, each thread's pieces of a batch all
-// loaded before any is stored (one memory latency per batch).  With ns > 1
-// the source is ns partial rows sst floats apart, added in order.
 // Loads of a projected row for copy_row / token_row: pieces b, b + blockDim,
 // .. (U of them) of T (float4 or float), of ns partial planes sst floats
 // apart, summed in plane order.  Every load is issued before any is used:
@@ -476,7 +471,9 @@ CSA_DEV void row_planes(const float* __restrict__ src, int n, int b, int ns, siz
 }
 
 // dst[0..n) (and dst2[0..n2), n2 <= n) = the sum of the ns partial planes of
-// the row at src.
+// the row at src, with the threads of the block: 16-byte pieces when every
+// pointer is 16-byte aligned and n, n2 are multiples of 4, a batch of pieces
+// loaded before any is stored (one memory latency per batch).
 CSA_DEV void copy_row(float* __restrict__ dst, const float* __restrict__ src, int n, float* dst2 = nullptr,
                       int n2 = 0, int ns = 1, size_t sst = 0)
 {
