@@ -1005,7 +1005,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a)
     constexpr int CPL = 8 / NSUB;                              // channels per lane
     constexpr int W = BF ? CPL / 2 : CPL;                      // 32-bit words per lane and split
     static_assert(W == 2 || W % 4 == 0, "8- or 16-byte pieces");
-    const int lane = threadIdx.x & 63, wv = (int)(threadIdx.x >> 6);
+    // the wave index (so the head, the split rows' addresses and every
+    // split's (max, sum)) is uniform in the wave: in scalar registers a
+    // split's address is one scalar add, not a 64-bit multiply per lane
+    // (batches of up to 16 splits; 32 splits' (max, sum) pairs would not fit
+    // the scalar registers)
+    const int lane = threadIdx.x & 63;
+    const int wv = CB <= 16 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) : (int)(threadIdx.x >> 6);
     const int gq = blockIdx.x, head = blockIdx.y * (4 / NSUB) + wv / NSUB, sub = wv % NSUB;
     if (head >= a.nh) return;                                  // wave-uniform
     const int C = a.c, S = a.n_splits, nf = C - a.r;
@@ -1059,7 +1065,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a)
 #pragma unroll
     for (int i = 0; i < CPL; ++i) o[i] = 0.f;
     auto accum = [&](float2 msl, const uint32_t (&u)[W]) {
-        const float w = msl.x == -INFINITY ? 0.f : exp2f(msl.x - M);
+        // msl.x - M <= 0: the hardware exp2 (a weight below 2^-126 flushes to 0)
+        const float w = msl.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(msl.x - M);
         if (w == 0.f) return;                                  // empty splits add nothing, not even +0
         L += msl.y * w;
         float v[CPL];
