@@ -396,9 +396,19 @@ __global__ __launch_bounds__(64 * NW) void proj_ksplit(const uint16_t* __restric
         // its region is refilled
         __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0)
         uint4 xf[8];
+        // four waves (K up to 4096): a full batch of 8 steps without per-step
+        // branches, which otherwise make each fragment read wait before its
+        // MFMA (measured: 128K compressor projection 8.6 -> 8.2 us; with
+        // eight waves and 7-step batches the same form was slower)
+        const bool full = NW == 4 && nb == 8;
+        if (full) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            if (u < nb) xf[u] = *(const uint4*)(xr + MmaBF16::K * (b0 + u));
+            for (int u = 0; u < 8; ++u) xf[u] = *(const uint4*)(xr + MmaBF16::K * (b0 + u));
+        } else {
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (u < nb) xf[u] = *(const uint4*)(xr + MmaBF16::K * (b0 + u));
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int r = 2 * i + (lane >> 5);
@@ -408,12 +418,22 @@ __global__ __launch_bounds__(64 * NW) void proj_ksplit(const uint16_t* __restric
                                              (CSA_LDS void*)&Ws[wave][i * RB], 16, 0, 0);
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);                    // vmcnt(0): fragments and the region filled
+        if (full) {
+            // every fragment read issued before the first MFMA (steps in the
+            // same order per accumulator as below)
+            uint4 bv[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            if (u < nb) {
-                const int slot = (4 * u + g) ^ li;
-                const uint4 bv = *(const uint4*)&Ws[wave][li * PK_KB + 8 * slot];
-                acc[u & 3] = MmaBF16::step(xf[u], bv, acc[u & 3]);
+            for (int u = 0; u < 8; ++u) bv[u] = *(const uint4*)&Ws[wave][li * PK_KB + 8 * ((4 * u + g) ^ li)];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc[u & 3] = MmaBF16::step(xf[u], bv[u], acc[u & 3]);
+        } else {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (u < nb) {
+                    const int slot = (4 * u + g) ^ li;
+                    const uint4 bv = *(const uint4*)&Ws[wave][li * PK_KB + 8 * slot];
+                    acc[u & 3] = MmaBF16::step(xf[u], bv, acc[u & 3]);
+                }
             }
         }
     }
